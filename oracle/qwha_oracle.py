@@ -1,0 +1,353 @@
+"""CPU oracle for the Walsh-Hadamard adapter (WHA) of QWHA -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module. The product path
+(``quantization_aware_sparse_amd``) never does, and this module imports
+nothing from it: the two share only the seeded input generators in ``synth``.
+
+Everything is plain numpy in float64 on the CPU, with the Walsh-Hadamard
+matrix built densely by Sylvester's construction. Where the method has a plain
+definition (materialisation, forward, backward) the oracle is that definition
+written out with dense matrix products; where it is a heuristic (the budget
+allocation and the in-row selection of AdaAlloc) the oracle takes the steps in
+the order the pages describe.
+
+Sources (cited by page title and section):
+  [PN]  QWHA notes, papernotes.org (ICLR 2026 model-compression notes):
+        方法详解 › 整体框架; 关键设计 1 (WHA), 2 (AdaAlloc), 3 (Value Refinement);
+        损失函数 / 训练策略.
+  [GS]  QWHA technical summary, gist.science (arXiv 2509.17428):
+        §2.1 Adapter Design, §2.2 Quantization-Aware Initialization.
+
+Readings of points the pages leave open (all listed in the design notes):
+  * H is the Sylvester (natural-order) +-1 matrix, unnormalised; H^-1 = H/n.
+  * AdaAlloc's budget formula is missing from the notes; it is read as
+    p_i proportional to w_i^(1/t) (t = 1: proportional), floor rounding, a
+    per-row floor m and cap d_in enforced by fix-and-reallocate passes (rows
+    below the floor are fixed first; only when none are, rows above the cap
+    are fixed), then the leftover (< d_out) goes one unit each to the rows
+    with the smallest budget, lower row index first, rows at the cap skipped.
+  * "Activation error magnitude" without calibration data is the row's l2
+    norm of dW_Q (identity Hessian).
+  * In-row selection orders columns by (-|C[i,j]|, j): ties go to the lower
+    column; +0.0 and -0.0 are equal magnitudes. E is listed by (i, j).
+  * Value Refinement with an identity Hessian (R = I) is exactly the identity
+    on the dense solution, so c = fp32_RNE(C[i, E_i]) (see ``refine_ls``).
+
+Parity pins: every public function here is pinned by tests under ``tests/``
+against closed forms, library routines or brute force, except the parts of
+``adaalloc`` that the pages do not print (the floor/cap passes, the leftover
+tie rule and t != 1): those are pinned only to the reading above --
+"parity unpinned" with respect to the pages.
+"""
+
+from __future__ import annotations
+
+import functools
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "sylvester", "transform", "row_norms", "adaalloc", "adaalloc_margins",
+    "select", "values", "refine_ls", "csc", "init_select", "scatter_dense",
+    "materialize", "forward", "backward", "backward_dc_rows", "sign_update",
+    "rel_err",
+]
+
+
+# --------------------------------------------------------------------------
+# O1: the transform kernel H   ([PN] 关键设计 1; [GS] §2.1)
+# --------------------------------------------------------------------------
+
+@functools.lru_cache(maxsize=4)
+def _sylvester_cached(n: int) -> np.ndarray:
+    H = np.ones((1, 1), dtype=np.float64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    H.setflags(write=False)
+    return H
+
+
+def sylvester(n: int) -> np.ndarray:
+    """Dense fp64 Walsh-Hadamard matrix of order n by Sylvester's doubling
+    H_{2m} = [[H_m, H_m], [H_m, -H_m]] from H_1 = [1]. Entries are +-1 (the
+    square-wave basis of [PN] 关键设计 1); H is symmetric and H H = n I, so
+    H^-1 = H / n."""
+    if n < 1 or (n & (n - 1)) != 0:
+        raise ValueError("n must be a power of two")
+    return _sylvester_cached(int(n))
+
+
+# --------------------------------------------------------------------------
+# O2, O3: dense solution and row error norms   ([PN] 关键设计 2, 3)
+# --------------------------------------------------------------------------
+
+def transform(dwq: np.ndarray) -> np.ndarray:
+    """Dense solution C = dW_Q H (fp64 matmul). Row i is x0 = v B^-1 of the
+    refinement sub-problem with R = I ([PN] 关键设计 3), the candidates AdaAlloc
+    picks from ([PN] 关键设计 2)."""
+    d_in = dwq.shape[1]
+    return np.asarray(dwq, dtype=np.float64) @ sylvester(d_in)
+
+
+def row_norms(dwq: np.ndarray) -> np.ndarray:
+    """w_i = ||dW_Q[i, :]||_2 in fp64: the per-output-channel error magnitude
+    AdaAlloc allocates by ([PN] 关键设计 2; [GS] §2.2), identity Hessian."""
+    a = np.asarray(dwq, dtype=np.float64)
+    return np.sqrt(np.sum(a * a, axis=1))
+
+
+# --------------------------------------------------------------------------
+# O4: AdaAlloc budgets   ([PN] 关键设计 2; [GS] §2.2)
+# --------------------------------------------------------------------------
+
+def adaalloc(w: np.ndarray, p: int, d_in: int, m: int = 3,
+             t: float = 1.0) -> np.ndarray:
+    """Per-row budgets p_i with sum p_i = p.
+
+    Proportional pass: p_i = floor(P * s_i / S) over the rows U not yet fixed,
+    with s_i = w_i^(1/t), P = p - (budgets of fixed rows), S = sum_U s_i
+    (floor(P/|U|) when S = 0). Rows below m are fixed at m; if there are none,
+    rows above d_in are fixed at d_in; repeat until a pass fixes nothing.
+    The leftover r = p - sum p_i goes one unit each to the rows with the
+    smallest p_i (lower row index first), skipping rows at d_in; if r exceeds
+    the eligible rows, it is handed out in further such rounds."""
+    w = np.asarray(w, dtype=np.float64)
+    d_out = w.shape[0]
+    if not (m * d_out <= p <= d_in * d_out):
+        raise ValueError("budget out of range")
+    s = w if t == 1.0 else w ** (1.0 / t)
+    budget = np.zeros(d_out, dtype=np.int64)
+    fixed = np.zeros(d_out, dtype=bool)
+    while not fixed.all():
+        U = ~fixed
+        P = int(p - budget[fixed].sum())
+        S = float(np.sum(s[U]))
+        if S > 0.0:
+            budget[U] = np.floor((float(P) * s[U]) / S).astype(np.int64)
+        else:
+            budget[U] = P // int(U.sum())
+        low = U & (budget < m)
+        if low.any():
+            budget[low] = m
+            fixed |= low
+            continue
+        high = U & (budget > d_in)
+        if high.any():
+            budget[high] = d_in
+            fixed |= high
+            continue
+        break
+    r = int(p - budget.sum())
+    while r > 0:
+        elig = np.nonzero(budget < d_in)[0]
+        order = elig[np.lexsort((elig, budget[elig]))]
+        give = order[:r]
+        budget[give] += 1
+        r -= len(give)
+    assert int(budget.sum()) == p
+    return budget
+
+
+def adaalloc_margins(w: np.ndarray, p: int, d_in: int, m: int = 3,
+                     t: float = 1.0) -> np.ndarray:
+    """Distance of P*s_i/S to the nearest integer in the final proportional
+    pass, per row (inf for rows fixed at the floor or the cap). A small
+    margin means fp64 rounding order could change that row's floor."""
+    w = np.asarray(w, dtype=np.float64)
+    d_out = w.shape[0]
+    s = w if t == 1.0 else w ** (1.0 / t)
+    budget = np.zeros(d_out, dtype=np.int64)
+    fixed = np.zeros(d_out, dtype=bool)
+    margin = np.full(d_out, np.inf)
+    while not fixed.all():
+        U = ~fixed
+        P = int(p - budget[fixed].sum())
+        S = float(np.sum(s[U]))
+        if S > 0.0:
+            q = (float(P) * s[U]) / S
+            budget[U] = np.floor(q).astype(np.int64)
+            margin[:] = np.inf
+            margin[U] = np.abs(q - np.rint(q))
+        else:
+            budget[U] = P // int(U.sum())
+        low = U & (budget < m)
+        if low.any():
+            budget[low] = m
+            fixed |= low
+            continue
+        high = U & (budget > d_in)
+        if high.any():
+            budget[high] = d_in
+            fixed |= high
+            continue
+        break
+    margin[fixed] = np.inf
+    return margin
+
+
+# --------------------------------------------------------------------------
+# O5, O6: in-row top-magnitude selection and values   ([PN] 关键设计 2, 3)
+# --------------------------------------------------------------------------
+
+def select(C: np.ndarray, budgets: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """For each row take the p_i columns first in the order (-|C[i,j]|, j)
+    (largest magnitude first, lower column on ties) and list them ascending.
+    Returns (row_ptr int32 [d_out+1], E int32 [p][2] of (i, j))."""
+    d_out, d_in = C.shape
+    budgets = np.asarray(budgets, dtype=np.int64)
+    row_ptr = np.zeros(d_out + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(budgets)
+    E = np.zeros((int(row_ptr[-1]), 2), dtype=np.int64)
+    for i in range(d_out):
+        order = np.argsort(-np.abs(C[i]), kind="stable")
+        cols = np.sort(order[: budgets[i]])
+        E[row_ptr[i]:row_ptr[i + 1], 0] = i
+        E[row_ptr[i]:row_ptr[i + 1], 1] = cols
+    return row_ptr.astype(np.int32), E.astype(np.int32)
+
+
+def values(C: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """c_k = fp32(C[i_k, j_k]), round to nearest even: the dense solution at
+    the chosen positions, which is what refinement returns when R = I."""
+    return C[E[:, 0], E[:, 1]].astype(np.float32)
+
+
+def refine_ls(v: np.ndarray, B: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Value Refinement for one channel ([PN] 关键设计 3): least squares
+    min_x ||v - x B'||^2 over the rows B' = B[cols, :], solved with
+    numpy.linalg.lstsq. With R = I, B = H^-1 = H/n and the solution equals
+    the dense solution at cols (pinned by a test); kept for that pin."""
+    Bp = np.asarray(B, dtype=np.float64)[np.asarray(cols), :]
+    sol, *_ = np.linalg.lstsq(Bp.T, np.asarray(v, dtype=np.float64), rcond=None)
+    return sol
+
+
+def csc(E: np.ndarray, d_in: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Column index of F: csc_perm lists the positions k of E column by
+    column, ascending k within a column (a stable sort by j); col_ptr is its
+    exclusive scan of column counts."""
+    j = np.asarray(E[:, 1], dtype=np.int64)
+    perm = np.argsort(j, kind="stable")
+    counts = np.bincount(j, minlength=d_in)
+    col_ptr = np.zeros(d_in + 1, dtype=np.int64)
+    col_ptr[1:] = np.cumsum(counts)
+    return col_ptr.astype(np.int32), perm.astype(np.int32)
+
+
+def init_select(dwq: np.ndarray, p: int, m: int = 3, t: float = 1.0,
+                with_diagnostics: bool = False) -> Dict[str, np.ndarray]:
+    """Quantization-aware init: w -> budgets -> E, c (+ the column index).
+
+    The pipeline of [PN] 方法详解 › 整体框架 under the identity Hessian:
+    dense solution C = dW_Q H, AdaAlloc budgets from the row norms, in-row
+    top-magnitude positions, values c = C at E (refinement with R = I)."""
+    d_out, d_in = dwq.shape
+    C = transform(dwq)
+    w = row_norms(dwq)
+    budgets = adaalloc(w, p, d_in, m, t)
+    row_ptr, E = select(C, budgets)
+    c = values(C, E)
+    col_ptr, perm = csc(E, d_in)
+    out = dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm,
+               budgets=budgets, w=w)
+    if with_diagnostics:
+        gaps = np.full(d_out, np.inf)
+        for i in range(d_out):
+            a = np.sort(np.abs(C[i]))[::-1]
+            k = int(budgets[i])
+            if 0 < k < d_in and a[k - 1] > 0:
+                gaps[i] = (a[k - 1] - a[k]) / a[k - 1]
+        out["boundary_gap"] = gaps
+        out["budget_margin"] = adaalloc_margins(w, p, d_in, m, t)
+        out["C"] = C
+    return out
+
+
+# --------------------------------------------------------------------------
+# O7-O10: materialisation, forward, backward, update
+#         ([PN] 方法详解 › 整体框架, 损失函数 / 训练策略; [GS] §2.1)
+# --------------------------------------------------------------------------
+
+def scatter_dense(E: np.ndarray, c: np.ndarray, d_out: int,
+                  d_in: int) -> np.ndarray:
+    """F = Scatter(c, E) as a dense fp64 [d_out][d_in] matrix."""
+    F = np.zeros((d_out, d_in), dtype=np.float64)
+    F[E[:, 0], E[:, 1]] = np.asarray(c, dtype=np.float64)
+    return F
+
+
+def _scatter_sparse(E, c, d_out, d_in):
+    import scipy.sparse as sp
+    return sp.csr_matrix(
+        (np.asarray(c, dtype=np.float64), (E[:, 0], E[:, 1])),
+        shape=(d_out, d_in))
+
+
+def materialize(E: np.ndarray, c: np.ndarray, d_out: int, d_in: int,
+                alpha: float = 1.0) -> np.ndarray:
+    """dW = alpha * F H^-1 = alpha * F H / n, F = Scatter(c, E).
+
+    F is held as a scipy sparse matrix so the product skips its zeros; every
+    output entry is the same sum as the dense product F @ H."""
+    H = sylvester(d_in)
+    F = _scatter_sparse(E, c, d_out, d_in)
+    return (alpha / d_in) * np.asarray(F @ H)
+
+
+def forward(x: np.ndarray, dW: np.ndarray) -> np.ndarray:
+    """Adapter branch of the layer output: y = x dW^T (fp64)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(dW, dtype=np.float64).T
+
+
+def backward(x: np.ndarray, dy: np.ndarray, E: np.ndarray, c: np.ndarray,
+             d_out: int, d_in: int, alpha: float = 1.0,
+             dW: Optional[np.ndarray] = None):
+    """Gradients of the adapter branch with W_Q and H frozen and only c
+    trainable ([PN] 损失函数 / 训练策略):
+      dx = dy dW;  G = dy^T x;  dF = alpha * G H / n;  dc = dF[E]."""
+    if dW is None:
+        dW = materialize(E, c, d_out, d_in, alpha)
+    x64 = np.asarray(x, dtype=np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dx = dy64 @ dW
+    G = dy64.T @ x64
+    dF = (alpha / d_in) * (G @ sylvester(d_in))
+    dc = dF[E[:, 0], E[:, 1]]
+    return dx, dc
+
+
+def backward_dc_rows(x: np.ndarray, dy: np.ndarray, E: np.ndarray,
+                     rows: np.ndarray, d_in: int,
+                     alpha: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """dc restricted to the nonzeros of the given rows of F: the same
+    definition as ``backward`` (dF = alpha * (dy^T x) H / n, gathered at E)
+    evaluated on those rows of G only. Returns (k indices, dc values)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    x64 = np.asarray(x, dtype=np.float64)
+    G = np.asarray(dy, dtype=np.float64)[:, rows].T @ x64   # [len(rows)][d_in]
+    dF = (alpha / d_in) * (G @ sylvester(d_in))
+    where = {int(r): a for a, r in enumerate(rows)}
+    ks = np.nonzero(np.isin(E[:, 0], rows))[0]
+    vals = np.array([dF[where[int(E[k, 0])], int(E[k, 1])] for k in ks])
+    return ks, vals
+
+
+def sign_update(c: np.ndarray, dc: np.ndarray, step: float = 1e-3) -> np.ndarray:
+    """c' = c + fp32(step) * sign(dc) in fp32 (sign(0) = 0): the synthetic
+    coefficient update of the attention-block training step."""
+    c32 = np.asarray(c, dtype=np.float32)
+    sg = np.sign(np.asarray(dc, dtype=np.float32)).astype(np.float32)
+    return (c32 + np.float32(step) * sg).astype(np.float32)
+
+
+def rel_err(a: np.ndarray, b: np.ndarray) -> float:
+    """Normwise relative error max|a - b| / max|b| (b is the reference)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = float(np.max(np.abs(b))) if b.size else 0.0
+    num = float(np.max(np.abs(a - b))) if a.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den

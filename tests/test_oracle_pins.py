@@ -1,0 +1,453 @@
+"""Pins of the CPU oracle to things other than itself: closed forms, textbook
+values, library routines (scipy.linalg.hadamard, numpy.linalg.lstsq/inv,
+torch.autograd in fp64) and brute force on tiny inputs. Each test is chosen
+so that a plausible slip in the oracle (a dropped term, a sign, an index, a
+transposed operand) fails it."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.conftest import read_golden
+
+
+# ---------------------------------------------------------------- H (O1)
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64, 256, 1024])
+def test_sylvester_identities(n):
+    H = O.sylvester(n)
+    assert H.shape == (n, n)
+    assert np.array_equal(H @ H.T, n * np.eye(n))          # H H^T = n I
+    assert np.array_equal(H, H.T)                          # symmetric
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    pc = np.vectorize(lambda a: bin(int(a)).count("1"))(i & j)
+    assert np.array_equal(H, (-1.0) ** pc)                 # (-1)^popcount(i&j)
+
+
+@pytest.mark.parametrize("n", [2, 4, 32, 512, 4096])
+def test_sylvester_matches_scipy(n):
+    from scipy.linalg import hadamard
+    assert np.array_equal(O.sylvester(n), hadamard(n).astype(np.float64))
+
+
+def test_sylvester_golden():
+    g = read_golden("wht4.txt")
+    assert np.array_equal(O.sylvester(4), g["H4"])
+    assert np.array_equal(O.sylvester(2), np.array([[1.0, 1.0], [1.0, -1.0]]))
+    C = O.transform(g["v"].astype(np.float32))
+    assert np.array_equal(C, g["C"])
+
+
+def test_sylvester_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        O.sylvester(12)
+
+
+# --------------------------------------------------------- transform (O2/O3)
+
+def _fwht_recursive(v):
+    """Independent check: the textbook in-place butterfly recursion."""
+    a = np.array(v, dtype=np.float64)
+    h = 1
+    n = a.shape[-1]
+    while h < n:
+        for s in range(0, n, 2 * h):
+            x = a[..., s:s + h].copy()
+            y = a[..., s + h:s + 2 * h].copy()
+            a[..., s:s + h] = x + y
+            a[..., s + h:s + 2 * h] = x - y
+        h *= 2
+    return a
+
+
+def test_transform_matches_butterfly_recursion():
+    rng = np.random.default_rng(1)
+    dwq = rng.standard_normal((5, 64)).astype(np.float32)
+    C = O.transform(dwq)
+    assert np.allclose(C, _fwht_recursive(dwq.astype(np.float64)),
+                       rtol=0, atol=1e-12)
+
+
+def test_transform_parseval():
+    rng = np.random.default_rng(2)
+    dwq = (0.01 * rng.standard_normal((16, 256))).astype(np.float32)
+    C = O.transform(dwq)
+    w = O.row_norms(dwq)
+    lhs = np.sum(C * C, axis=1)
+    rhs = 256 * w * w
+    assert np.max(np.abs(lhs - rhs) / rhs) < 1e-12
+
+
+def test_transform_spike_and_constant():
+    n = 32
+    H = O.sylvester(n)
+    for j in [0, 5, 31]:
+        row = np.zeros((1, n), np.float32)
+        row[0, j] = 0.75
+        assert np.array_equal(O.transform(row)[0], 0.75 * H[j])
+    const = np.full((1, n), 0.125, np.float32)
+    C = O.transform(const)[0]
+    assert C[0] == n * 0.125 and np.all(C[1:] == 0)
+
+
+def test_row_norms():
+    dwq = np.array([[3, 4, 0, 0], [0, 0, 0, 0], [1, 1, 1, 1]], np.float32)
+    assert np.array_equal(O.row_norms(dwq), np.array([5.0, 0.0, 2.0]))
+
+
+# --------------------------------------------------------------- AdaAlloc (O4)
+
+def test_adaalloc_golden():
+    g = read_golden("adaalloc_hand.txt")
+    p, m, d_in = (int(v) for v in g["p m d_in"][0])
+    b = O.adaalloc(g["w"][0], p, d_in, m=m)
+    assert np.array_equal(b, g["budgets"][0].astype(np.int64))
+
+
+def _expected_unbounded(w, p):
+    """When neither the floor nor the cap binds the rule is a single
+    proportional floor pass plus the leftover to the smallest budgets."""
+    S = float(np.sum(w))
+    b = np.floor(p * w / S).astype(np.int64)
+    r = p - int(b.sum())
+    order = np.lexsort((np.arange(len(w)), b))
+    b[order[:r]] += 1
+    return b
+
+
+def test_adaalloc_reduces_to_proportional():
+    rng = np.random.default_rng(3)
+    w = rng.uniform(0.5, 2.0, size=257)
+    p = 257 * 40 + 123
+    b = O.adaalloc(w, p, 1024, m=3)
+    assert np.array_equal(b, _expected_unbounded(w, p))
+    assert b.sum() == p
+
+
+def test_adaalloc_invariants_random():
+    rng = np.random.default_rng(4)
+    for trial in range(30):
+        d_out = int(rng.integers(1, 200))
+        d_in = int(2 ** rng.integers(2, 9))
+        m = int(rng.integers(0, min(4, d_in) + 1))
+        p = int(rng.integers(m * d_out, d_in * d_out + 1))
+        w = rng.lognormal(0, 2, size=d_out) * (rng.random(d_out) > 0.1)
+        b = O.adaalloc(w, p, d_in, m=m)
+        assert b.sum() == p
+        assert np.all(b >= m) and np.all(b <= d_in)
+
+
+def test_adaalloc_floor_binds():
+    b = O.adaalloc(np.array([1e-6, 1.0, 1.0, 1.0]), 12, 8, m=3)
+    assert np.array_equal(b, [3, 3, 3, 3])
+
+
+def test_adaalloc_cap_binds_and_leftover_rounds():
+    # pass 1: floor(12*w/103) = (11, 0, 0, 0) -> rows 1..3 fixed at the floor 1
+    # pass 2: U = {0}, P = 9 > d_in = 4 -> row 0 fixed at the cap 4
+    # sum = 7, leftover 5 > 3 eligible rows: rounds (+1,+1,+1), then (+1,+1,0)
+    b = O.adaalloc(np.array([100.0, 1.0, 1.0, 1.0]), 12, 4, m=1)
+    assert np.array_equal(b, [4, 3, 3, 2])
+
+
+def test_adaalloc_zero_norms_split_evenly():
+    b = O.adaalloc(np.zeros(4), 10, 8, m=1)
+    # floor(10/4) = 2 each, leftover 2 to rows 0 and 1
+    assert np.array_equal(b, [3, 3, 2, 2])
+
+
+def test_adaalloc_temperature_flattens():
+    w = np.array([1.0, 4.0, 16.0])
+    b1 = O.adaalloc(w, 42, 64, m=0, t=1.0)
+    b2 = O.adaalloc(w, 42, 64, m=0, t=2.0)   # w^(1/2) = (1, 2, 4)
+    assert np.array_equal(b1, [2, 8, 32])
+    assert np.array_equal(b2, [6, 12, 24])
+
+
+def test_adaalloc_rejects_infeasible():
+    with pytest.raises(ValueError):
+        O.adaalloc(np.ones(4), 11, 8, m=3)       # p < m d_out
+    with pytest.raises(ValueError):
+        O.adaalloc(np.ones(4), 33, 8, m=3)       # p > d_in d_out
+
+
+# -------------------------------------------------------- selection (O5/O6)
+
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_select_is_best_sparse_approximation_bruteforce(n):
+    """Within a row, the chosen p_i columns minimise the least-squares error
+    ||v - x_S (H/n)[S,:]||^2 over all subsets of that size; the minimum is
+    (1/n) sum_{j not in S} C_j^2 and the LS solution is C[S] (refinement with
+    R = I is the identity)."""
+    rng = np.random.default_rng(10 + n)
+    H = O.sylvester(n)
+    B = H / n
+    for trial in range(4):
+        v = rng.standard_normal(n).astype(np.float32)
+        C = O.transform(v[None, :])[0]
+        for k in range(1, min(4, n) + 1):
+            _, E = O.select(C[None, :], np.array([k]))
+            S_or = tuple(int(j) for j in E[:, 1])
+            best, best_S = np.inf, None
+            for S in itertools.combinations(range(n), k):
+                x, *_ = np.linalg.lstsq(B[list(S)].T, v.astype(np.float64),
+                                        rcond=None)
+                res = float(np.sum((v - x @ B[list(S)]) ** 2))
+                if res < best - 1e-12:
+                    best, best_S = res, S
+            x_or = O.refine_ls(v, B, np.array(S_or))
+            res_or = float(np.sum((v - x_or @ B[list(S_or)]) ** 2))
+            assert res_or <= best + 1e-10
+            assert S_or == best_S
+            rest = [j for j in range(n) if j not in S_or]
+            assert abs(res_or - np.sum(C[rest] ** 2) / n) < 1e-10
+            assert np.allclose(x_or, C[list(S_or)], rtol=0, atol=1e-10)
+            assert np.array_equal(O.values(C[None, :], E),
+                                  x_or.astype(np.float32)) or \
+                np.allclose(O.values(C[None, :], E), x_or, rtol=1e-6)
+
+
+def test_select_ties_go_to_lower_column():
+    n = 16
+    row = np.zeros((1, n), np.float32)
+    row[0, 6] = 1.0            # spike: every |C| equals 1
+    C = O.transform(row)
+    for k in [1, 3, 16]:
+        _, E = O.select(C, np.array([k]))
+        assert np.array_equal(E[:, 1], np.arange(k))
+    # signed zeros are equal magnitudes
+    Cz = np.array([[0.0, -0.0, 0.0, -0.0]])
+    _, E = O.select(Cz, np.array([2]))
+    assert np.array_equal(E[:, 1], [0, 1])
+
+
+def test_select_orders_rows_and_columns():
+    rng = np.random.default_rng(5)
+    C = rng.standard_normal((6, 32))
+    b = np.array([1, 5, 3, 32, 2, 7])
+    row_ptr, E = O.select(C, b)
+    assert np.array_equal(np.diff(row_ptr), b)
+    for i in range(6):
+        seg = E[row_ptr[i]:row_ptr[i + 1]]
+        assert np.all(seg[:, 0] == i)
+        assert np.all(np.diff(seg[:, 1]) > 0)
+        chosen = np.abs(C[i, seg[:, 1]])
+        other = np.delete(np.abs(C[i]), seg[:, 1])
+        if other.size:
+            assert chosen.min() >= other.max()
+
+
+def test_csc_index():
+    rng = np.random.default_rng(6)
+    C = rng.standard_normal((20, 16))
+    row_ptr, E = O.select(C, rng.integers(1, 8, size=20))
+    col_ptr, perm = O.csc(E, 16)
+    assert col_ptr[-1] == len(E)
+    for j in range(16):
+        ks = perm[col_ptr[j]:col_ptr[j + 1]]
+        assert np.all(E[ks, 1] == j)
+        assert np.all(np.diff(ks) > 0)
+    assert np.array_equal(np.sort(perm), np.arange(len(E)))
+
+
+# ---------------------------------------------------------- golden whole init
+
+def test_init_materialize_fwd_bwd_golden():
+    g = read_golden("init_hand_2x4.txt")
+    dwq = g["dWq"].astype(np.float32)
+    p, m = (int(v) for v in g["p m"][0])
+    r = O.init_select(dwq, p, m=m)
+    assert np.array_equal(r["budgets"], g["budgets"][0].astype(np.int64))
+    assert np.array_equal(r["E"], g["E"].astype(np.int32))
+    assert np.array_equal(r["c"], g["c"][0].astype(np.float32))
+    dW = O.materialize(r["E"], r["c"], 2, 4, 1.0)
+    assert np.array_equal(dW, g["dW"])
+    y = O.forward(g["x"], dW)
+    dx, dc = O.backward(g["x"], g["dy"], r["E"], r["c"], 2, 4, 1.0)
+    assert np.allclose(y, g["y"], atol=1e-15)
+    assert np.allclose(dx, g["dx"], atol=1e-15)
+    assert np.allclose(dc, g["dc"][0], atol=1e-15)
+
+
+# ------------------------------------------------------ materialize (O7)
+
+def test_materialize_full_budget_reconstructs_error():
+    rng = np.random.default_rng(7)
+    d_out, n = 8, 32
+    dwq = (0.01 * rng.standard_normal((d_out, n))).astype(np.float32)
+    r = O.init_select(dwq, d_out * n, m=3)
+    C = O.transform(dwq)
+    dW = O.materialize(r["E"], C[r["E"][:, 0], r["E"][:, 1]], d_out, n, 1.0)
+    assert np.max(np.abs(dW - dwq.astype(np.float64))) < 1e-12
+
+
+def test_materialize_single_nonzero_and_alpha():
+    n = 64
+    H = O.sylvester(n)
+    E = np.array([[2, 9]], np.int32)
+    dW = O.materialize(E, np.array([0.5], np.float32), 4, n, alpha=2.0)
+    expect = np.zeros((4, n))
+    expect[2] = 2.0 * 0.5 / n * H[9]
+    assert np.array_equal(dW, expect)
+
+
+def test_materialize_matches_inverse():
+    rng = np.random.default_rng(8)
+    d_out, n = 6, 16
+    C = rng.standard_normal((d_out, n))
+    _, E = O.select(C, rng.integers(1, 6, size=d_out))
+    c = rng.standard_normal(len(E)).astype(np.float32)
+    F = O.scatter_dense(E, c, d_out, n)
+    ref = F @ np.linalg.inv(O.sylvester(n))
+    assert np.allclose(O.materialize(E, c, d_out, n), ref, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------- fwd / bwd (O8/O9)
+
+def _small_adapter(seed, d_out=12, n=32, T=7, alpha=1.0):
+    rng = np.random.default_rng(seed)
+    C = rng.standard_normal((d_out, n))
+    _, E = O.select(C, rng.integers(3, 9, size=d_out))
+    c = rng.standard_normal(len(E)).astype(np.float32)
+    x = rng.standard_normal((T, n))
+    dy = rng.standard_normal((T, d_out))
+    return E, c, x, dy
+
+
+def test_fwd_bwd_bilinear_identities():
+    for alpha in [1.0, 0.7]:
+        E, c, x, dy = _small_adapter(11, alpha=alpha)
+        dW = O.materialize(E, c, 12, 32, alpha)
+        y = O.forward(x, dW)
+        dx, dc = O.backward(x, dy, E, c, 12, 32, alpha)
+        L = float(np.sum(dy * y))
+        assert abs(float(np.sum(dx * x)) - L) < 1e-12 * max(1, abs(L))
+        assert abs(float(np.dot(dc, c.astype(np.float64))) - L) < \
+            1e-12 * max(1, abs(L))
+
+
+def test_fwd_bwd_against_torch_autograd_fp64():
+    torch = pytest.importorskip("torch")
+    alpha = 0.9
+    E, c, x, dy = _small_adapter(12, alpha=alpha)
+    d_out, n = 12, 32
+    H = torch.tensor(O.sylvester(n))
+    ct = torch.tensor(c.astype(np.float64), requires_grad=True)
+    xt = torch.tensor(x, requires_grad=True)
+    F = torch.zeros(d_out, n, dtype=torch.float64)
+    F = F.index_put((torch.tensor(E[:, 0]).long(), torch.tensor(E[:, 1]).long()),
+                    ct)
+    dW = alpha * F @ torch.linalg.inv(H)
+    y = xt @ dW.T
+    y.backward(torch.tensor(dy))
+    dx, dc = O.backward(x, dy, E, c, d_out, n, alpha)
+    assert np.allclose(y.detach().numpy(),
+                       O.forward(x, O.materialize(E, c, d_out, n, alpha)),
+                       rtol=0, atol=1e-12)
+    assert np.allclose(xt.grad.numpy(), dx, rtol=0, atol=1e-12)
+    assert np.allclose(ct.grad.numpy(), dc, rtol=0, atol=1e-12)
+
+
+def test_dc_finite_difference():
+    E, c, x, dy = _small_adapter(13)
+    d_out, n = 12, 32
+
+    def L(cv):
+        return float(np.sum(dy * O.forward(x, O.materialize(E, cv, d_out, n))))
+    _, dc = O.backward(x, dy, E, c, d_out, n)
+    c64 = c.astype(np.float64)
+    for k in [0, 3, len(c) - 1]:
+        e = np.zeros_like(c64)
+        e[k] = 0.5
+        # L is linear in c: the difference quotient is exact up to rounding
+        assert abs((L(c64 + e) - L(c64)) / 0.5 - dc[k]) < 1e-10
+
+
+def test_backward_dc_rows_matches_full():
+    E, c, x, dy = _small_adapter(14)
+    _, dc = O.backward(x, dy, E, c, 12, 32, 0.5)
+    ks, vals = O.backward_dc_rows(x, dy, E, np.array([0, 5, 11]), 32, 0.5)
+    assert np.allclose(vals, dc[ks], rtol=0, atol=1e-13)
+    assert set(E[ks, 0]) == {0, 5, 11}
+
+
+def test_sign_update():
+    c = np.array([1.0, -2.0, 0.5, 0.0], np.float32)
+    dc = np.array([0.3, -1e-30, 0.0, -4.0], np.float32)
+    out = O.sign_update(c, dc)
+    expect = np.array([1.0 + np.float32(1e-3), -2.0 - np.float32(1e-3), 0.5,
+                       -np.float32(1e-3)], np.float32)
+    assert np.array_equal(out, expect)
+
+
+def test_rel_err():
+    assert O.rel_err(np.array([1.0, 2.0]), np.array([1.0, 4.0])) == 0.5
+    assert O.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# ------------------------------------------------------------ rank of F
+
+_PRIME = 2147483647
+
+
+def _rank_mod_p(A):
+    """Exact rank over GF(2^31 - 1) by Gaussian elimination; a lower bound
+    on the rank over the reals for integer matrices."""
+    M = np.array(A, dtype=np.int64) % _PRIME
+    rows, cols = M.shape
+    r = 0
+    for c in range(cols):
+        piv = None
+        for i in range(r, rows):
+            if M[i, c] != 0:
+                piv = i
+                break
+        if piv is None:
+            continue
+        M[[r, piv]] = M[[piv, r]]
+        inv = pow(int(M[r, c]), _PRIME - 2, _PRIME)
+        M[r] = (M[r] * inv) % _PRIME
+        others = np.nonzero(M[:, c])[0]
+        others = others[others != r]
+        if len(others):
+            f = M[others, c][:, None]
+            M[others] = (M[others] - (f * M[r][None, :]) % _PRIME) % _PRIME
+        r += 1
+        if r == rows:
+            break
+    return r
+
+
+@pytest.mark.parametrize("shape", [(48, 48), (24, 64), (64, 24)])
+def test_rank_full_with_three_per_row_and_column(shape):
+    """QWHA notes 关键设计 1: F is full rank with high probability once every
+    row and column holds more than two nonzeros."""
+    d_out, n = shape
+    for seed in range(20):
+        rng = np.random.default_rng(100 + seed)
+        mask = np.zeros(shape, bool)
+        for i in range(d_out):
+            mask[i, rng.choice(n, 3, replace=False)] = True
+        for j in range(n):
+            need = 3 - int(mask[:, j].sum())
+            if need > 0:
+                free = np.nonzero(~mask[:, j])[0]
+                mask[rng.choice(free, need, replace=False), j] = True
+        F = np.where(mask, rng.integers(1, 1000, size=shape), 0)
+        assert _rank_mod_p(F) == min(shape)
+
+
+def test_rank_of_small_config_adapter():
+    import synth
+    spec = synth.config_specs("c1")[0]
+    layer = synth.make_layer(spec, seed=0)
+    r = O.init_select(layer.dwq, spec.p, m=3)
+    F = np.zeros((spec.d_out, spec.d_in), np.int64)
+    # integer surrogate with the same pattern (rank over GF(p) <= real rank)
+    rng = np.random.default_rng(0)
+    F[r["E"][:, 0], r["E"][:, 1]] = rng.integers(1, 1000, size=len(r["E"]))
+    assert _rank_mod_p(F) == 256
+    assert np.diff(r["row_ptr"]).min() >= 3
