@@ -1,0 +1,287 @@
+"""Throughput of the Walsh-Hadamard adapter hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch, every kernel in
+the library's HIP code, on torch's current stream:
+  init (row norms, AdaAlloc budgets, fp64 transform + in-row top-k, column
+  index) -> materialize dW -> forward (FWHT(x), gather-SpMM) -> backward
+  (gather-SpMM dz and dc partials, FWHT(dz) -> dx, dc reduction) ->
+  c += 1e-3 sign(dc) -> re-materialize dW.
+value = tokens per second of that step (T / step time), inputs resident in HBM.
+
+Workload (default): the 4096x4096 q_proj-shaped layer, 4-bit RTN (group 128)
+error with 0.1% x20 outliers, budget p = 524288 (rank-64 LoRA parameter
+count), 8192 bf16 tokens. Four copies of the inputs are rotated so the
+working set exceeds the 256 MB Infinity Cache.
+
+Per-kernel times come from HIP events recorded by the library around each
+kernel launch (qwha_profile_next), on the launch stream, over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X vector fp32 (packed FMA)
+
+K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_FWHT_X=3, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC_REDUCE=6,
+         INIT_SELECT=7, MATERIALIZE=8)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--sets", type=int, default=4, help="rotated input copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvents from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return ms.value
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in the design notes, not implemented)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import quantization_aware_sparse_amd as q
+    from quantization_aware_sparse_amd import check, lib
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    spec = synth.config_specs(args.config)[0]
+    d_out, d_in, p, T = spec.d_out, spec.d_in, spec.p, spec.T
+    act = q.QWHA_BF16 if spec.act == "bf16" else q.QWHA_F32
+    adt = torch.bfloat16 if spec.act == "bf16" else torch.float32
+    esz = 2 if spec.act == "bf16" else 4
+
+    t_gen = time.perf_counter()
+    layer = synth.make_layer(spec, seed=0)
+    x_np, dy_np = synth.make_activations(spec, seed=0)
+    gen_s = time.perf_counter() - t_gen
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    sets = []
+    base = (up(layer.dwq), up(x_np), up(dy_np))
+    for s in range(args.sets):
+        sets.append(tuple(b.clone() for b in base))
+    del base
+
+    i32 = dict(dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(d_out + 1, **i32)
+    E = torch.empty((p, 2), **i32)
+    c = torch.empty(p, dtype=torch.float32, device=dev)
+    col_ptr = torch.empty(d_in + 1, **i32)
+    perm = torch.empty(p, **i32)
+    dW = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d_out), dtype=adt, device=dev)
+    dx = torch.empty((T, d_in), dtype=adt, device=dev)
+    dc = torch.empty(p, dtype=torch.float32, device=dev)
+    ws_i = torch.empty(lib.qwha_init_workspace_bytes(d_out, d_in), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
+                       device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    hip = HipEvents()
+    ev = {name: (hip.create(), hip.create()) for name in K}
+    times = {name: [] for name in K}
+
+    def step(s, record):
+        dwq, x, dy = sets[s % len(sets)]
+        if record:
+            for name, kid in K.items():
+                check(lib.qwha_profile_next(kid, ev[name][0], ev[name][1]), "profile")
+        check(lib.qwha_init_select(dwq.data_ptr(), d_out, d_in, p, 3, 1.0, row_ptr.data_ptr(),
+                                   E.data_ptr(), c.data_ptr(), col_ptr.data_ptr(),
+                                   perm.data_ptr(), ws_i.data_ptr(), ws_i.numel(), stream),
+              "init")
+        check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
+                                   p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "materialize")
+        check(lib.qwha_fwd(x.data_ptr(), act, T, d_in, d_out, p, row_ptr.data_ptr(),
+                           E.data_ptr(), c.data_ptr(), 1.0, y.data_ptr(), 0, ws_f.data_ptr(),
+                           ws_f.numel(), stream), "fwd")
+        check(lib.qwha_bwd(x.data_ptr(), dy.data_ptr(), act, T, d_in, d_out, p,
+                           row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), col_ptr.data_ptr(),
+                           perm.data_ptr(), 1.0, dx.data_ptr(), 0, dc.data_ptr(),
+                           ws_b.data_ptr(), ws_b.numel(), stream), "bwd")
+        check(lib.qwha_sign_update(c.data_ptr(), dc.data_ptr(), p, 1e-3, stream), "update")
+        check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
+                                   p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "rematerialize")
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, True)
+        # the next step's requests reuse these events: read them first
+        torch.cuda.synchronize()
+        for name in K:
+            times[name].append(hip.elapsed_ms(*ev[name]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # clean timing without per-step host waits: the figure `value` reports
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, False)
+    torch.cuda.synchronize()
+    wall_clean = time.perf_counter() - t1
+    ms_step = 1e3 * wall_clean / args.steps
+    value = T / (ms_step / 1e3)
+
+    avg_us = {k: 1e3 * float(np.mean(v)) for k, v in times.items()}
+    # algorithmic work per launch
+    nbytes = {
+        "FWD_FWHT": T * d_in * (esz + 4),
+        "BWD_FWHT_X": T * d_in * (esz + 4),
+        "BWD_FWHT_DX": T * d_in * (4 + esz),
+        "INIT_SELECT": d_out * d_in * 4 + p * 12 + (d_out + 1) * 4,
+        "MATERIALIZE": p * 12 + (d_out + 1) * 4 + d_out * d_in * 4,
+        "BWD_DC_REDUCE": 0,
+    }
+    flops = {"FWD_SPMM": 2.0 * T * p, "BWD_SPMM": 4.0 * T * p}
+    kern = {}
+    for k, us in avg_us.items():
+        if k in flops:
+            a = flops[k] / (us * 1e-6) / 1e12
+            kern[k] = dict(avg_us=round(us, 2), bound="alu", achieved=round(a, 3),
+                           unit="TFLOP/s", peak=FP32_VECTOR_PEAK_TFLOPS,
+                           frac=round(a / FP32_VECTOR_PEAK_TFLOPS, 4))
+        elif nbytes.get(k):
+            a = nbytes[k] / (us * 1e-6) / 1e9
+            kern[k] = dict(avg_us=round(us, 2), bound="hbm", achieved=round(a, 1), unit="GB/s",
+                           peak=HBM_PEAK_GBS, frac=round(a / HBM_PEAK_GBS, 4))
+        else:
+            kern[k] = dict(avg_us=round(us, 2))
+    dom = max(avg_us, key=avg_us.get)
+    roof = dict(kern[dom])
+    roof.pop("avg_us", None)
+    roof["kernel"] = dom
+    roof["avg_us"] = round(avg_us[dom], 2)
+    roof["traffic"] = None
+
+    fwd_bwd_us = sum(avg_us[k] for k in ("FWD_FWHT", "FWD_SPMM", "BWD_FWHT_X", "BWD_SPMM",
+                                         "BWD_FWHT_DX", "BWD_DC_REDUCE"))
+    out = {
+        "metric": "adapter fwd+bwd tokens/s per layer; FWHT/gather achieved HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}: {d_out}x{d_in} layer, {spec.bits}-bit RTN g{spec.group} "
+                        f"error with {spec.outlier_frac:.1%} x{spec.outlier_mult:g} outliers, "
+                        f"p={p}, {T} {spec.act} tokens; step = init + materialize + fwd + bwd "
+                        "+ sign update + re-materialize",
+            "d_out": d_out, "d_in": d_in, "p": p, "tokens": T, "act": spec.act,
+            "input_sets_rotated": args.sets,
+        },
+        "roofline": roof,
+        "kernels": kern,
+        "fwd_bwd_kernels_us": round(fwd_bwd_us, 2),
+        "fwd_bwd_tokens_per_s": round(T / (fwd_bwd_us * 1e-6), 1),
+        "profiled_steps_ms": round(1e3 * wall / args.steps, 4),
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, layer, x_np, dy_np, n_tok):
+    """The fp64 oracle (as it stands) on the host cores: one step of the same
+    path on the full layer with a sample of n_tok tokens."""
+    import numpy as np
+    import oracle as O
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # noqa: BLE001
+        limiter = None
+    n_tok = min(n_tok, spec.T)
+    x = synth.act_to_f64(x_np[:n_tok])
+    dy = synth.act_to_f64(dy_np[:n_tok])
+    t0 = time.perf_counter()
+    r = O.init_select(layer.dwq, spec.p, m=3)
+    dW = O.materialize(r["E"], r["c"], spec.d_out, spec.d_in, 1.0)
+    O.forward(x, dW)
+    _, dc = O.backward(x, dy, r["E"], r["c"], spec.d_out, spec.d_in, 1.0, dW=dW)
+    c2 = O.sign_update(r["c"], dc)
+    O.materialize(r["E"], c2, spec.d_out, spec.d_in, 1.0)
+    sec = time.perf_counter() - t0
+    threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
+    except Exception:  # noqa: BLE001
+        pass
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": round(n_tok / sec, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one oracle step (init, materialize, fwd, bwd, update, re-materialize) on "
+                      f"the full {spec.d_out}x{spec.d_in} layer with {n_tok} of {spec.T} tokens; "
+                      f"{sec:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * qwha.h -- C-ABI of the MI355X (gfx950) Walsh-Hadamard adapter (WHA) library.
+ *
+ * The adapter of QWHA writes the weight update as dW = alpha * F H^-1 where
+ * H is the frozen Sylvester Walsh-Hadamard matrix (entries +-1, applied along
+ * the input dimension only, H^-1 = H / d_in) and F = Scatter(c, E) is a
+ * sparse d_out x d_in coefficient matrix with p nonzeros: positions E
+ * (p x 2) and values c (p). Only c is trained; W_Q and H stay frozen.
+ *   Sources: QWHA notes, papernotes.org (ICLR 2026), 方法详解 › 整体框架 and
+ *   关键设计 1-3, 损失函数 / 训练策略; QWHA technical summary, gist.science
+ *   (arXiv 2509.17428), §2.1 Adapter Design, §2.2 Quantization-Aware
+ *   Initialization.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: all array arguments are DEVICE pointers owned by the caller;
+ *    the library never allocates, frees or keeps a pointer past the work it
+ *    enqueues. Buffers must stay alive until that work has run.
+ *  - Asynchrony: work is enqueued on `stream` and the call returns at once.
+ *  - Validation: arguments are checked on the host before anything is
+ *    enqueued; a non-OK status means nothing was enqueued.
+ *    qwha_last_error() (thread-local) then says why.
+ *  - Layout: dense matrices are row-major and contiguous. E is int32 [p][2]
+ *    holding (row i, column j), sorted by (i, j). row_ptr is int32
+ *    [d_out + 1] (exclusive scan of the per-row budgets). col_ptr is int32
+ *    [d_in + 1] and csc_perm int32 [p] lists positions k of E column by
+ *    column, ascending k within a column.
+ *  - Alignment: dense activation / weight arrays and workspaces must be
+ *    16-byte aligned, index and value arrays 4-byte aligned
+ *    (QWHA_ERR_ALIGN otherwise).
+ *  - Shapes: d_in is a power of two in [2, 16384] (QWHA_ERR_SHAPE
+ *    otherwise; the pages only use power-of-two transform lengths),
+ *    1 <= d_out <= 1048576, T >= 0 (T == 0 is a no-op), p <= 2^31 - 1.
+ *  - Aliasing: inputs and outputs must not overlap, except that an output is
+ *    read back when its `accumulate` flag is set.
+ *  - Preconditions not checked (they would need device reads): inputs are
+ *    finite; row_ptr[d_out] == p; E / row_ptr / col_ptr / csc_perm are the
+ *    consistent output of qwha_init_select (or equivalent).
+ *  - Calls are reentrant; there is no global state apart from the
+ *    thread-local error string and the thread-local profiling request of
+ *    qwha_profile_next().
+ */
+#ifndef QWHA_H
+#define QWHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t; /* HIP's opaque stream handle; NULL = default stream */
+typedef struct ihipEvent_t* hipEvent_t;   /* HIP's opaque event handle */
+
+typedef enum qwha_status {
+  QWHA_OK = 0,
+  QWHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad flag or scalar */
+  QWHA_ERR_SHAPE = 2,       /* d_in not a power of two in [2,16384], d_out or T out of range */
+  QWHA_ERR_BUDGET = 3,      /* p outside its allowed range */
+  QWHA_ERR_DTYPE = 4,       /* unknown qwha_dtype */
+  QWHA_ERR_ALIGN = 5,       /* pointer not aligned as required */
+  QWHA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the *_workspace_bytes query */
+  QWHA_ERR_HIP = 7          /* a HIP launch failed; qwha_last_error() has the HIP message */
+} qwha_status;
+
+typedef enum qwha_dtype { QWHA_F32 = 0, QWHA_BF16 = 1 } qwha_dtype;
+
+/* Static strings; never NULL. */
+const char* qwha_status_string(qwha_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* qwha_last_error(void);
+/* Library ABI version (major * 100 + minor). */
+int32_t qwha_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Quantization-aware initialisation (papernotes.org, 关键设计 2 AdaAlloc and
+ * 3 Value Refinement; gist.science §2.2).
+ *
+ * From the quantization error dWq = W0 - W_Q (fp32 [d_out][d_in]):
+ *   1. w_i = ||dWq[i,:]||_2 (fp64): each output channel's error magnitude
+ *      (identity Hessian: no calibration activations).
+ *   2. AdaAlloc budgets p_i with sum p_i = p: p_i = floor(P s_i / S) with
+ *      s_i = w_i^(1/temperature) over rows not yet fixed, rows below
+ *      min_per_row fixed at min_per_row first, then rows above d_in fixed at
+ *      d_in, repeated until nothing is fixed; the leftover (< d_out) goes one
+ *      unit each to the rows with the smallest budget (lower row first, rows
+ *      at d_in skipped). The exact formula is missing from the pages; this is
+ *      the proportional reading (temperature 1 = linear).
+ *   3. Dense solution C = dWq H (fp64 fast WHT per row).
+ *   4. Row i keeps the p_i columns with the largest |C[i,j]|, ties to the
+ *      lower column; they are written to E ascending, and
+ *      c = fp32_RNE(C[i,j]) (value refinement with an identity Hessian
+ *      returns the dense solution at the chosen positions).
+ *   5. col_ptr / csc_perm: the column index of F (stable in k).
+ * Outputs: row_ptr [d_out+1], E [p][2], c [p], col_ptr [d_in+1], csc_perm [p].
+ * Requires min_per_row >= 0, min_per_row * d_out <= p <= d_in * d_out
+ * (QWHA_ERR_BUDGET), temperature > 0 and finite, and a workspace of at least
+ * qwha_init_workspace_bytes(d_out, d_in) bytes.
+ * --------------------------------------------------------------------------- */
+size_t qwha_init_workspace_bytes(int32_t d_out, int32_t d_in);
+qwha_status qwha_init_select(const float* dWq, int32_t d_out, int32_t d_in, int64_t p,
+                             int32_t min_per_row, double temperature, int32_t* row_ptr,
+                             int32_t* E, float* c, int32_t* col_ptr, int32_t* csc_perm,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Materialisation (papernotes.org, 方法详解 › 整体框架; gist.science §2.1):
+ *   dW = alpha * F H^-1 = (alpha / d_in) * Scatter(c, E) H
+ * written to dW [d_out][d_in] in out_dtype (QWHA_F32 or QWHA_BF16, rounded
+ * to nearest even); accumulate != 0 adds into the existing dW instead
+ * (dW += alpha F H^-1, e.g. merging into a dequantized weight).
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const float* c,
+                             int32_t d_out, int32_t d_in, int64_t p, float alpha,
+                             qwha_dtype out_dtype, void* dW, int32_t accumulate,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Forward through the adapter branch (papernotes.org, 方法详解 › 整体框架):
+ *   y = x dW^T = alpha * (FWHT(x) / d_in) F^T
+ * x [T][d_in] and y [T][d_out] share the activation dtype `act`; math is fp32.
+ * accumulate != 0 adds into y (the caller's base output x W_Q^T).
+ * Workspace: qwha_fwd_workspace_bytes(T, d_in, d_out, p) bytes.
+ * --------------------------------------------------------------------------- */
+size_t qwha_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p);
+qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+                     int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
+                     float alpha, void* y, int32_t accumulate, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward through the adapter branch, W_Q and H frozen, only c trainable
+ * (papernotes.org, 损失函数 / 训练策略):
+ *   dx   = dy dW = alpha * FWHT(dy F) / d_in               [T][d_in], dtype act
+ *   dc_k = alpha * sum_t dy[t, i_k] * (FWHT(x)/d_in)[t, j_k]  [p], fp32
+ * dx or dc may be NULL to skip that output; accumulate_dx != 0 adds into dx.
+ * dc is reduced in a fixed order (deterministic).
+ * Workspace: qwha_bwd_workspace_bytes(T, d_in, d_out, p) bytes.
+ * --------------------------------------------------------------------------- */
+size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p);
+qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, int32_t d_in,
+                     int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                     const float* c, const int32_t* col_ptr, const int32_t* csc_perm,
+                     float alpha, void* dx, int32_t accumulate_dx, float* dc, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Coefficient update of the attention-block training step:
+ *   c[k] += step * sign(dc[k])   (sign(0) = 0), fp32, in place.
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_sign_update(float* c, const float* dc, int64_t p, float step,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Profiling aid: the next launch of kernel `kernel` made by this thread
+ * (inside any entry point above) is bracketed by hipEventRecord(start) and
+ * hipEventRecord(stop) on that launch's stream; the request is then
+ * consumed. Requests for different kernel ids are independent (one pending
+ * request per id). kernel = QWHA_KERNEL_NONE cancels every pending request.
+ * Thread-local state; the events must outlive the launch they bracket.
+ * --------------------------------------------------------------------------- */
+typedef enum qwha_kernel {
+  QWHA_KERNEL_NONE = 0,
+  QWHA_KERNEL_FWD_FWHT = 1,     /* z = FWHT(x)/n inside qwha_fwd */
+  QWHA_KERNEL_FWD_SPMM = 2,     /* y = alpha z F^T inside qwha_fwd */
+  QWHA_KERNEL_BWD_FWHT_X = 3,   /* z recomputed inside qwha_bwd */
+  QWHA_KERNEL_BWD_SPMM = 4,     /* dz = dy F and the dc partials inside qwha_bwd */
+  QWHA_KERNEL_BWD_FWHT_DX = 5,  /* dx = alpha FWHT(dz)/n inside qwha_bwd */
+  QWHA_KERNEL_BWD_DC_REDUCE = 6,
+  QWHA_KERNEL_INIT_SELECT = 7,  /* fp64 transform + top-k inside qwha_init_select */
+  QWHA_KERNEL_MATERIALIZE = 8,
+  QWHA_KERNEL_FWHT = 9          /* qwha_fwht */
+} qwha_kernel;
+qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop);
+
+/* ---------------------------------------------------------------------------
+ * Standalone row-wise fast Walsh-Hadamard transform (the +-1 kernel H,
+ * papernotes.org 关键设计 1):
+ *   out[r][:] = scale * in[r][:] H   for r < rows, n a power of two <= 16384.
+ * in / out dtypes independent (QWHA_F32 / QWHA_BF16); math is fp32.
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_fwht(const void* in, qwha_dtype in_dtype, void* out, qwha_dtype out_dtype,
+                      int64_t rows, int32_t n, float scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWHA_H */

@@ -1,0 +1,170 @@
+"""Walsh-Hadamard adapter (WHA) of QWHA on MI355X: Python binding.
+
+Thin wrappers over the C-ABI in include/qwha.h (same names). They only
+marshal arguments: device memory comes from torch tensors, the stream is
+torch's current HIP stream, and every step runs in the library's HIP
+kernels. There is no CPU path.
+
+The adapter: dW = alpha * F H^-1, F = Scatter(c, E), H the Sylvester
+Walsh-Hadamard matrix along d_in (QWHA notes, papernotes.org, 方法详解 ›
+整体框架; gist.science summary §2.1).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from ._lib import QwhaError, check, lib  # noqa: F401
+
+__all__ = [
+    "QWHA_F32", "QWHA_BF16", "QwhaError", "lib",
+    "qwha_init_select", "qwha_materialize", "qwha_fwd", "qwha_bwd",
+    "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
+]
+
+QWHA_F32 = 0
+QWHA_BF16 = 1
+
+_DT = {torch.float32: QWHA_F32, torch.bfloat16: QWHA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """Caller-owned workspace buffer (the library never allocates)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- init
+def qwha_init_select(dWq: torch.Tensor, p: int, min_per_row: int = 3,
+                     temperature: float = 1.0,
+                     ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    d_out, d_in = dWq.shape
+    dev = dWq.device
+    row_ptr = torch.empty(d_out + 1, dtype=torch.int32, device=dev)
+    E = torch.empty((max(p, 1), 2), dtype=torch.int32, device=dev)[:p]
+    c = torch.empty(max(p, 1), dtype=torch.float32, device=dev)[:p]
+    col_ptr = torch.empty(d_in + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(p, 1), dtype=torch.int32, device=dev)[:p]
+    need = lib.qwha_init_workspace_bytes(d_out, d_in)
+    if ws is None:
+        ws = workspace(need, dev)
+    check(lib.qwha_init_select(_ptr(dWq), d_out, d_in, p, min_per_row, float(temperature),
+                               _ptr(row_ptr), E.data_ptr(), c.data_ptr(), _ptr(col_ptr),
+                               perm.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+          "qwha_init_select")
+    return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm)
+
+
+# ---------------------------------------------------------------- materialize
+def qwha_materialize(row_ptr, E, c, d_out: int, d_in: int, alpha: float = 1.0,
+                     out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                     accumulate: bool = False) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((d_out, d_in), dtype=out_dtype, device=c.device)
+    p = int(c.numel())
+    check(lib.qwha_materialize(_ptr(row_ptr), E.data_ptr(), c.data_ptr(), d_out, d_in, p,
+                               float(alpha), _dt(out), _ptr(out), int(accumulate), _stream()),
+          "qwha_materialize")
+    return out
+
+
+# ---------------------------------------------------------------- forward
+def qwha_fwd(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
+             y: Optional[torch.Tensor] = None, accumulate: bool = False,
+             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, d_in = x.shape
+    p = int(c.numel())
+    if y is None:
+        y = torch.empty((T, d_out), dtype=x.dtype, device=x.device)
+    need = lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p)
+    if ws is None:
+        ws = workspace(need, x.device)
+    check(lib.qwha_fwd(_ptr(x), _dt(x), T, d_in, d_out, p, _ptr(row_ptr), E.data_ptr(),
+                       c.data_ptr(), float(alpha), _ptr(y), int(accumulate), ws.data_ptr(),
+                       ws.numel(), _stream()), "qwha_fwd")
+    return y
+
+
+# ---------------------------------------------------------------- backward
+def qwha_bwd(x: torch.Tensor, dy: torch.Tensor, row_ptr, E, c, col_ptr, csc_perm,
+             alpha: float = 1.0, need_dx: bool = True, need_dc: bool = True,
+             dx: Optional[torch.Tensor] = None, accumulate_dx: bool = False,
+             dc: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    T, d_in = x.shape
+    d_out = dy.shape[1]
+    p = int(c.numel())
+    if need_dx and dx is None:
+        dx = torch.empty((T, d_in), dtype=x.dtype, device=x.device)
+    if need_dc and dc is None:
+        dc = torch.empty(max(p, 1), dtype=torch.float32, device=x.device)[:p]
+    if not need_dx:
+        dx = None
+    if not need_dc:
+        dc = None
+    need = lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p)
+    if ws is None:
+        ws = workspace(need, x.device)
+    check(lib.qwha_bwd(_ptr(x), _ptr(dy), _dt(dy), T, d_in, d_out, p, _ptr(row_ptr),
+                       E.data_ptr(), c.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(),
+                       float(alpha), _ptr(dx), int(accumulate_dx),
+                       dc.data_ptr() if dc is not None else None,
+                       ws.data_ptr(), ws.numel(), _stream()), "qwha_bwd")
+    return dx, dc
+
+
+# ---------------------------------------------------------------- update, fwht
+def qwha_sign_update(c: torch.Tensor, dc: torch.Tensor, step: float = 1e-3) -> torch.Tensor:
+    check(lib.qwha_sign_update(c.data_ptr(), dc.data_ptr(), int(c.numel()), float(step),
+                               _stream()), "qwha_sign_update")
+    return c
+
+
+def qwha_fwht(x: torch.Tensor, scale: float = 1.0, out_dtype=None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    rows = x.numel() // x.shape[-1]
+    n = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    check(lib.qwha_fwht(_ptr(x), _dt(x), _ptr(out), _dt(out), rows, n, float(scale),
+                        _stream()), "qwha_fwht")
+    return out
+
+
+# ---------------------------------------------------------------- autograd
+class WHAFunction(torch.autograd.Function):
+    """y = x dW^T for the adapter branch; gradients flow to x and c only
+    (W_Q and H frozen: papernotes.org, 损失函数 / 训练策略)."""
+
+    @staticmethod
+    def forward(ctx, x, c, row_ptr, E, col_ptr, csc_perm, d_out, alpha):
+        ctx.save_for_backward(x, c, row_ptr, E, col_ptr, csc_perm)
+        ctx.alpha = alpha
+        return qwha_fwd(x.contiguous(), d_out, row_ptr, E, c, alpha)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, c, row_ptr, E, col_ptr, csc_perm = ctx.saved_tensors
+        dx, dc = qwha_bwd(x, dy.contiguous(), row_ptr, E, c, col_ptr, csc_perm, ctx.alpha,
+                          need_dx=ctx.needs_input_grad[0], need_dc=ctx.needs_input_grad[1])
+        return dx, dc, None, None, None, None, None, None

@@ -1,0 +1,415 @@
+// C-ABI entry points: host-side validation, workspace carving, launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/qwha.h"
+#include "launch.h"
+
+using namespace qwha;
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+qwha_status fail(qwha_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qwha_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QWHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return QWHA_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// one-shot profiling requests (qwha_profile_next), one slot per kernel id
+struct Hook {
+  hipEvent_t start, stop;
+};
+constexpr int kNumKernelIds = 10;
+thread_local Hook g_hook[kNumKernelIds] = {};
+
+// Runs `launch` (a callable returning hipError_t) for kernel id `k`, with the
+// pending profiling events recorded around it when requested.
+template <typename Fn>
+hipError_t timed(int k, hipStream_t s, Fn&& launch) {
+  if (g_hook[k].start == nullptr) return launch();
+  const Hook h = g_hook[k];
+  g_hook[k] = Hook{nullptr, nullptr};
+  hipError_t e = hipEventRecord(h.start, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(h.stop, s);
+}
+
+int log2_pow2(int32_t n) {
+  if (n < 2 || n > 16384 || (n & (n - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < n) ++l;
+  return l;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qwha_status check_dims(int32_t d_out, int32_t d_in, int* log_n) {
+  *log_n = log2_pow2(d_in);
+  if (*log_n < 0) return fail(QWHA_ERR_SHAPE, "d_in=%d is not a power of two in [2, 16384]", d_in);
+  if (d_out < 1 || d_out > (1 << 20)) return fail(QWHA_ERR_SHAPE, "d_out=%d out of [1, 2^20]", d_out);
+  return QWHA_OK;
+}
+
+qwha_status check_p(int64_t p, int32_t d_out, int32_t d_in) {
+  if (p < 0 || p > INT32_MAX || p > static_cast<int64_t>(d_out) * d_in)
+    return fail(QWHA_ERR_BUDGET, "p=%lld outside [0, min(2^31-1, d_out*d_in)]",
+                static_cast<long long>(p));
+  return QWHA_OK;
+}
+
+qwha_status check_dt(int d, const char* name) {
+  if (d != QWHA_F32 && d != QWHA_BF16) return fail(QWHA_ERR_DTYPE, "%s: unknown dtype %d", name, d);
+  return QWHA_OK;
+}
+
+#define QWHA_TRY(expr)            \
+  do {                            \
+    qwha_status _s = (expr);      \
+    if (_s != QWHA_OK) return _s; \
+  } while (0)
+
+#define QWHA_NEED(ptr, align)                                                          \
+  do {                                                                                 \
+    if ((ptr) == nullptr) return fail(QWHA_ERR_INVALID_ARG, "%s is NULL", #ptr);       \
+    if (!aligned((ptr), (align)))                                                      \
+      return fail(QWHA_ERR_ALIGN, "%s is not %d-byte aligned", #ptr, (int)(align));    \
+  } while (0)
+
+// ---- workspace layouts
+struct InitWs {
+  size_t w, alloc, csc, total;
+};
+InitWs init_ws(int32_t d_out, int32_t d_in) {
+  InitWs l;
+  l.w = 0;
+  l.alloc = align256(static_cast<size_t>(d_out) * 8);
+  l.csc = l.alloc + align256(adaalloc_scratch_bytes(d_out));
+  l.total = l.csc + align256(csc_scratch_bytes(d_out, d_in));
+  return l;
+}
+
+struct FwdWs {
+  size_t z, prep, total;
+  SpmmPlan plan;
+};
+FwdWs fwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+  FwdWs l;
+  l.plan = spmm_plan(T, d_in, d_out);
+  l.z = 0;
+  l.prep = align256(static_cast<size_t>(T) * d_in * 4);
+  l.total = l.prep + align256(spmm_prep_bytes(p, d_out, l.plan));
+  return l;
+}
+
+struct BwdWs {
+  size_t z, dz, prep, partial, total;
+  SpmmPlan plan;
+};
+BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+  BwdWs l;
+  l.plan = spmm_plan(T, d_out, d_in);
+  const size_t zb = align256(static_cast<size_t>(T) * d_in * 4);
+  l.z = 0;
+  l.dz = zb;
+  l.prep = 2 * zb;
+  l.partial = l.prep + align256(spmm_prep_bytes(p, d_in, l.plan));
+  l.total = l.partial + align256(static_cast<size_t>(l.plan.ntiles) * static_cast<size_t>(p) * 4);
+  return l;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qwha_status_string(qwha_status s) {
+  switch (s) {
+    case QWHA_OK: return "ok";
+    case QWHA_ERR_INVALID_ARG: return "invalid argument";
+    case QWHA_ERR_SHAPE: return "unsupported shape";
+    case QWHA_ERR_BUDGET: return "budget out of range";
+    case QWHA_ERR_DTYPE: return "unknown dtype";
+    case QWHA_ERR_ALIGN: return "misaligned pointer";
+    case QWHA_ERR_WORKSPACE: return "workspace too small";
+    case QWHA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* qwha_last_error(void) { return g_err; }
+
+int32_t qwha_version(void) { return 100; }
+
+// ------------------------------------------------------------------ init
+size_t qwha_init_workspace_bytes(int32_t d_out, int32_t d_in) {
+  if (d_out < 1 || d_in < 1) return 0;
+  return init_ws(d_out, d_in).total;
+}
+
+qwha_status qwha_init_select(const float* dWq, int32_t d_out, int32_t d_in, int64_t p,
+                             int32_t min_per_row, double temperature, int32_t* row_ptr,
+                             int32_t* E, float* c, int32_t* col_ptr, int32_t* csc_perm,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  if (min_per_row < 0 || min_per_row > d_in)
+    return fail(QWHA_ERR_INVALID_ARG, "min_per_row=%d outside [0, d_in]", min_per_row);
+  if (!(temperature > 0.0) || !isfinite(temperature))
+    return fail(QWHA_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  QWHA_TRY(check_p(p, d_out, d_in));
+  if (p < static_cast<int64_t>(min_per_row) * d_out)
+    return fail(QWHA_ERR_BUDGET, "p=%lld < min_per_row*d_out=%lld", static_cast<long long>(p),
+                static_cast<long long>(min_per_row) * d_out);
+  QWHA_NEED(dWq, 16);
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(col_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+    QWHA_NEED(csc_perm, 4);
+  }
+  const InitWs l = init_ws(d_out, d_in);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(QWHA_ERR_WORKSPACE, "init workspace needs %zu bytes", l.total);
+  QWHA_NEED(workspace, 256);
+
+  double* w = reinterpret_cast<double*>(at(workspace, l.w));
+  QWHA_TRY(hip_check(launch_row_norms(dWq, d_out, d_in, w, stream), "row_norms"));
+  QWHA_TRY(hip_check(launch_adaalloc(w, d_out, d_in, p, min_per_row, temperature, row_ptr,
+                                     at(workspace, l.alloc), stream),
+                     "adaalloc"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_INIT_SELECT, stream,
+                           [&] { return launch_init_select(dWq, d_out, log_n, row_ptr, E, c, stream); }),
+                     "init_select"));
+  QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
+                                      at(workspace, l.csc), stream),
+                     "csc_build"));
+  return QWHA_OK;
+}
+
+// ------------------------------------------------------------------ materialize
+qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const float* c,
+                             int32_t d_out, int32_t d_in, int64_t p, float alpha,
+                             qwha_dtype out_dtype, void* dW, int32_t accumulate,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_dt(out_dtype, "out_dtype"));
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(QWHA_ERR_INVALID_ARG, "accumulate must be 0/1");
+  QWHA_NEED(row_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+  }
+  QWHA_NEED(dW, 16);
+  return hip_check(timed(QWHA_KERNEL_MATERIALIZE, stream,
+                         [&] {
+                           return launch_materialize(row_ptr, E, c, d_out, log_n, alpha,
+                                                     static_cast<Dt>(out_dtype), dW, accumulate,
+                                                     stream);
+                         }),
+                   "materialize");
+}
+
+// ------------------------------------------------------------------ forward
+size_t qwha_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  return fwd_ws(T, d_in, d_out, p).total;
+}
+
+qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+                     int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
+                     float alpha, void* y, int32_t accumulate, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_dt(act, "act"));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(QWHA_ERR_INVALID_ARG, "accumulate must be 0/1");
+  QWHA_NEED(row_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+  }
+  if (T == 0) return QWHA_OK;
+  QWHA_NEED(x, 16);
+  QWHA_NEED(y, 16);
+  const FwdWs l = fwd_ws(T, d_in, d_out, p);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(QWHA_ERR_WORKSPACE, "fwd workspace needs %zu bytes", l.total);
+  QWHA_NEED(workspace, 256);
+
+  float* z = reinterpret_cast<float*>(at(workspace, l.z));
+  void* prep = at(workspace, l.prep);
+  const Dt adt = static_cast<Dt>(act);
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
+                           [&] {
+                             return launch_fwht(x, adt, z, Dt::F32, T, log_n,
+                                                1.0f / static_cast<float>(d_in), 0, stream);
+                           }),
+                     "fwd fwht"));
+  QWHA_TRY(hip_check(launch_prep_csr(row_ptr, E, c, d_out, p, l.plan, prep, stream), "fwd prep"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_SPMM, stream,
+                           [&] {
+                             return launch_spmm(z, Dt::F32, T, d_in, prep, p, d_out, l.plan, alpha,
+                                                y, adt, accumulate, nullptr, nullptr, stream);
+                           }),
+                     "fwd spmm"));
+  return QWHA_OK;
+}
+
+// ------------------------------------------------------------------ backward
+size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  return bwd_ws(T, d_in, d_out, p).total;
+}
+
+qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, int32_t d_in,
+                     int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                     const float* c, const int32_t* col_ptr, const int32_t* csc_perm,
+                     float alpha, void* dx, int32_t accumulate_dx, float* dc, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_dt(act, "act"));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate_dx != 0 && accumulate_dx != 1)
+    return fail(QWHA_ERR_INVALID_ARG, "accumulate_dx must be 0/1");
+  (void)row_ptr;
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+    QWHA_NEED(csc_perm, 4);
+  }
+  QWHA_NEED(col_ptr, 4);
+  if (dx == nullptr && dc == nullptr) return QWHA_OK;
+  if (dc != nullptr && !aligned(dc, 4)) return fail(QWHA_ERR_ALIGN, "dc is not 4-byte aligned");
+  if (dx != nullptr && !aligned(dx, 16)) return fail(QWHA_ERR_ALIGN, "dx is not 16-byte aligned");
+  if (T == 0) {
+    // no tokens: dc is all zeros (a reduction over zero partials; no memset,
+    // so the call stays safe under stream capture)
+    if (dc != nullptr && p > 0)
+      return hip_check(launch_dc_reduce(nullptr, 0, p, csc_perm, alpha, dc, stream), "dc zero");
+    return QWHA_OK;
+  }
+  QWHA_NEED(dy, 16);
+  if (dc != nullptr) QWHA_NEED(x, 16);
+  const BwdWs l = bwd_ws(T, d_in, d_out, p);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", l.total);
+  QWHA_NEED(workspace, 256);
+
+  float* z = reinterpret_cast<float*>(at(workspace, l.z));
+  float* dz = reinterpret_cast<float*>(at(workspace, l.dz));
+  void* prep = at(workspace, l.prep);
+  float* partial = dc ? reinterpret_cast<float*>(at(workspace, l.partial)) : nullptr;
+  const Dt adt = static_cast<Dt>(act);
+  if (dc)
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_X, stream,
+                             [&] {
+                               return launch_fwht(x, adt, z, Dt::F32, T, log_n,
+                                                  1.0f / static_cast<float>(d_in), 0, stream);
+                             }),
+                       "bwd fwht(x)"));
+  QWHA_TRY(hip_check(launch_prep_csc(col_ptr, csc_perm, E, c, d_in, p, l.plan, prep, stream),
+                     "bwd prep"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_SPMM, stream,
+                           [&] {
+                             return launch_spmm(dy, adt, T, d_out, prep, p, d_in, l.plan, 1.0f, dz,
+                                                Dt::F32, 0, dc ? z : nullptr, partial, stream);
+                           }),
+                     "bwd spmm"));
+  if (dx)
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_DX, stream,
+                             [&] {
+                               return launch_fwht(dz, Dt::F32, dx, adt, T, log_n,
+                                                  alpha / static_cast<float>(d_in), accumulate_dx,
+                                                  stream);
+                             }),
+                       "bwd fwht(dz)"));
+  if (dc)
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_DC_REDUCE, stream,
+                             [&] {
+                               return launch_dc_reduce(partial, l.plan.ntiles, p, csc_perm, alpha,
+                                                       dc, stream);
+                             }),
+                       "dc reduce"));
+  return QWHA_OK;
+}
+
+// ------------------------------------------------------------------ update
+qwha_status qwha_sign_update(float* c, const float* dc, int64_t p, float step,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  if (p < 0 || p > INT32_MAX) return fail(QWHA_ERR_BUDGET, "p out of range");
+  if (!isfinite(step)) return fail(QWHA_ERR_INVALID_ARG, "step must be finite");
+  if (p == 0) return QWHA_OK;
+  QWHA_NEED(c, 4);
+  QWHA_NEED(dc, 4);
+  return hip_check(launch_sign_update(c, dc, p, step, stream), "sign_update");
+}
+
+// ------------------------------------------------------------------ fwht
+qwha_status qwha_fwht(const void* in, qwha_dtype in_dtype, void* out, qwha_dtype out_dtype,
+                      int64_t rows, int32_t n, float scale, hipStream_t stream) {
+  g_err[0] = 0;
+  const int log_n = log2_pow2(n);
+  if (log_n < 0) return fail(QWHA_ERR_SHAPE, "n=%d is not a power of two in [2, 16384]", n);
+  QWHA_TRY(check_dt(in_dtype, "in_dtype"));
+  QWHA_TRY(check_dt(out_dtype, "out_dtype"));
+  if (rows < 0 || rows > (static_cast<int64_t>(1) << 31))
+    return fail(QWHA_ERR_SHAPE, "rows out of range");
+  if (!isfinite(scale)) return fail(QWHA_ERR_INVALID_ARG, "scale must be finite");
+  if (rows == 0) return QWHA_OK;
+  QWHA_NEED(in, 16);
+  QWHA_NEED(out, 16);
+  return hip_check(timed(QWHA_KERNEL_FWHT, stream,
+                         [&] {
+                           return launch_fwht(in, static_cast<Dt>(in_dtype), out,
+                                              static_cast<Dt>(out_dtype), rows, log_n, scale, 0,
+                                              stream);
+                         }),
+                   "fwht");
+}
+
+qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
+  g_err[0] = 0;
+  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_FWHT || kernel >= kNumKernelIds)
+    return fail(QWHA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+  if (kernel == QWHA_KERNEL_NONE) {
+    for (int i = 0; i < kNumKernelIds; ++i) g_hook[i] = Hook{nullptr, nullptr};
+    return QWHA_OK;
+  }
+  if (start == nullptr || stop == nullptr)
+    return fail(QWHA_ERR_INVALID_ARG, "start/stop events are NULL");
+  g_hook[kernel] = Hook{start, stop};
+  return QWHA_OK;
+}
+
+}  // extern "C"

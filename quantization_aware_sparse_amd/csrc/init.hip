@@ -1,0 +1,505 @@
+// Quantization-aware init of the WHA adapter: per-row error norms, AdaAlloc
+// budgets, in-row top-magnitude selection of E and the values c, and the
+// column index of F.
+//   QWHA notes (papernotes.org), 方法详解 › 关键设计 2 (AdaAlloc) and 3 (Value
+//   Refinement: x0 = (dW_Q H)_i is the dense solution); gist.science summary
+//   §2.2 (budget proportional to the channel's error magnitude, a per-channel
+//   lower bound, top-magnitude coefficients within each channel).
+// With an identity Hessian the refined values equal the dense solution at
+// the chosen positions, so c = fp32_RNE(C[i, E_i]).
+#include "fwht_core.h"
+#include "launch.h"
+
+namespace qwha {
+
+// ------------------------------------------------------------ block helpers
+// Sum over the block; every thread gets the total. red must hold 2*16 ints;
+// alternate `parity` between consecutive calls so one barrier suffices.
+__device__ __forceinline__ int block_sum_i32(int v, int* red, int parity) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  v = wave_sum_i32(v);
+  if (lane == 0) red[parity * 16 + wid] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < nw; ++i) t += red[parity * 16 + i];
+  return t;
+}
+
+// Exclusive prefix over threads in threadIdx order; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan_i32(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  const int incl = wave_incl_scan_i32(v);
+  __syncthreads();                       // tmp free from any earlier use
+  if (lane == 63) tmp[wid] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int x = tmp[i];
+    if (i < wid) before += x;
+    all += x;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// ------------------------------------------------------------ row norms
+// w_i = sqrt(sum_j dWq[i][j]^2) in fp64; one wave per row.
+__global__ __launch_bounds__(256) void row_norms_kernel(const float* __restrict__ dWq, int d_out,
+                                                        int d_in, double* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_out) return;
+  const float* src = dWq + static_cast<int64_t>(row) * d_in;
+  double acc = 0.0;
+  if (d_in >= 4) {
+    for (int j = lane * 4; j < d_in; j += 256) {
+      const float4 f = *reinterpret_cast<const float4*>(src + j);
+      acc += static_cast<double>(f.x) * f.x;
+      acc += static_cast<double>(f.y) * f.y;
+      acc += static_cast<double>(f.z) * f.z;
+      acc += static_cast<double>(f.w) * f.w;
+    }
+  } else {
+    for (int j = lane; j < d_in; j += 64) acc += static_cast<double>(src[j]) * src[j];
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) w[row] = sqrt(acc);
+}
+
+hipError_t launch_row_norms(const float* dWq, int d_out, int d_in, double* w, hipStream_t s) {
+  hipLaunchKernelGGL(row_norms_kernel, dim3((d_out + 3) / 4), dim3(256), 0, s, dWq, d_out, d_in, w);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ AdaAlloc
+// One workgroup. Proportional passes p_i = floor(P s_i / S) over the rows not
+// yet fixed (s_i = w_i^(1/t)); rows below the floor m are fixed at m first,
+// then (only if none were) rows above d_in are fixed at d_in; repeat until a
+// pass fixes nothing. The leftover r = p - sum p_i (< d_out) goes one unit
+// each to the rows with the smallest budget, lower row index first, rows at
+// d_in skipped (in further rounds if r exceeds the eligible rows).
+// Finally row_ptr = exclusive scan of the budgets.
+constexpr int kAllocThreads = 1024;
+
+size_t adaalloc_scratch_bytes(int d_out) {
+  // s (double), budget (int64), fixed (int32)
+  return static_cast<size_t>(d_out) * (8 + 8 + 4) + 256;
+}
+
+__global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
+    const double* __restrict__ w, int d_out, int d_in, int64_t p, int m, double t,
+    int32_t* __restrict__ row_ptr, double* __restrict__ s, int64_t* __restrict__ budget,
+    int32_t* __restrict__ fixed) {
+  __shared__ double red_d[16];
+  __shared__ long long red_l[2][16];
+  __shared__ int red_i[2][16];
+  __shared__ int flags[4];
+  __shared__ int hist[16385 + 1];
+  __shared__ int scan_tmp[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  constexpr int NW = kAllocThreads / 64;
+
+  for (int i = tid; i < d_out; i += kAllocThreads) {
+    s[i] = (t == 1.0) ? w[i] : pow(w[i], 1.0 / t);
+    budget[i] = 0;
+    fixed[i] = 0;
+  }
+  __syncthreads();
+
+  int parity = 0;
+  for (;;) {
+    // S over unfixed rows (fp64, fixed order), budget sum over fixed rows,
+    // count of unfixed rows.
+    double ps = 0.0;
+    long long pf = 0;
+    int nu = 0;
+    for (int i = tid; i < d_out; i += kAllocThreads) {
+      if (fixed[i]) pf += budget[i];
+      else { ps += s[i]; ++nu; }
+    }
+    ps = wave_sum_f64(ps);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) pf += __shfl_xor(pf, off, 64);
+    nu = wave_sum_i32(nu);
+    if (lane == 0) { red_d[wid] = ps; red_l[parity][wid] = pf; red_i[parity][wid] = nu; }
+    if (tid < 4) flags[tid] = 0;
+    __syncthreads();
+    double S = 0.0;
+    long long F = 0;
+    int NU = 0;
+    for (int i = 0; i < NW; ++i) { S += red_d[i]; F += red_l[parity][i]; NU += red_i[parity][i]; }
+    parity ^= 1;
+    if (NU == 0) break;
+    const long long P = p - F;
+    int low = 0;
+    for (int i = tid; i < d_out; i += kAllocThreads) {
+      if (fixed[i]) continue;
+      long long b;
+      if (S > 0.0) b = static_cast<long long>(floor((static_cast<double>(P) * s[i]) / S));
+      else b = P / NU;
+      budget[i] = b;
+      if (b < m) low = 1;
+    }
+    if (low) flags[0] = 1;
+    __syncthreads();
+    if (flags[0]) {
+      for (int i = tid; i < d_out; i += kAllocThreads)
+        if (!fixed[i] && budget[i] < m) { budget[i] = m; fixed[i] = 1; }
+      __syncthreads();
+      continue;
+    }
+    int high = 0;
+    for (int i = tid; i < d_out; i += kAllocThreads)
+      if (!fixed[i] && budget[i] > d_in) high = 1;
+    if (high) flags[1] = 1;
+    __syncthreads();
+    if (flags[1]) {
+      for (int i = tid; i < d_out; i += kAllocThreads)
+        if (!fixed[i] && budget[i] > d_in) { budget[i] = d_in; fixed[i] = 1; }
+      __syncthreads();
+      continue;
+    }
+    break;
+  }
+  __syncthreads();
+
+  // leftover
+  for (;;) {
+    long long tot = 0;
+    for (int i = tid; i < d_out; i += kAllocThreads) tot += budget[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    if (lane == 0) red_l[parity][wid] = tot;
+    for (int v = tid; v <= d_in; v += kAllocThreads) hist[v] = 0;
+    __syncthreads();
+    long long TOT = 0;
+    for (int i = 0; i < NW; ++i) TOT += red_l[parity][i];
+    parity ^= 1;
+    long long r = p - TOT;
+    if (r <= 0) break;
+    for (int i = tid; i < d_out; i += kAllocThreads)
+      if (budget[i] < d_in) atomicAdd(&hist[budget[i]], 1);
+    __syncthreads();
+    // inclusive scan of hist over values 0..d_in (chunks of 1024, carried)
+    __shared__ long long carry;
+    __shared__ int vstar;
+    __shared__ long long below_star;
+    if (tid == 0) { carry = 0; vstar = -1; below_star = 0; }
+    __syncthreads();
+    for (int base = 0; base <= d_in; base += kAllocThreads) {
+      const int v = base + tid;
+      const int h = (v <= d_in) ? hist[v] : 0;
+      int tot_chunk;
+      const int ex = block_excl_scan_i32(h, scan_tmp, &tot_chunk);
+      const long long before = carry + ex;       // eligible rows with budget < v
+      const long long incl = before + h;
+      if (v <= d_in && h > 0 && before < r && incl >= r) { vstar = v; below_star = before; }
+      __syncthreads();
+      if (tid == 0) carry += tot_chunk;
+      __syncthreads();
+    }
+    const int vs = vstar;
+    if (vs < 0) {
+      // fewer eligible rows than the leftover: every eligible row gets one
+      for (int i = tid; i < d_out; i += kAllocThreads)
+        if (budget[i] < d_in) budget[i] += 1;
+      __syncthreads();
+      continue;
+    }
+    const long long need = r - below_star;       // rows at vs that get a unit
+    // rank rows with budget == vs by index (chunks, carried)
+    __shared__ long long rcarry;
+    if (tid == 0) rcarry = 0;
+    __syncthreads();
+    for (int base = 0; base < d_out; base += kAllocThreads) {
+      const int i = base + tid;
+      const long long b = (i < d_out) ? budget[i] : -1;
+      const int eq = (b == vs) ? 1 : 0;
+      int tot_chunk;
+      const int ex = block_excl_scan_i32(eq, scan_tmp, &tot_chunk);
+      if (i < d_out) {
+        if (b < vs) budget[i] = b + 1;
+        else if (eq && rcarry + ex < need) budget[i] = b + 1;
+      }
+      __syncthreads();
+      if (tid == 0) rcarry += tot_chunk;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  // row_ptr = exclusive scan of budgets
+  __shared__ long long pcarry;
+  if (tid == 0) pcarry = 0;
+  __syncthreads();
+  for (int base = 0; base < d_out; base += kAllocThreads) {
+    const int i = base + tid;
+    const int b = (i < d_out) ? static_cast<int>(budget[i]) : 0;
+    int tot_chunk;
+    const int ex = block_excl_scan_i32(b, scan_tmp, &tot_chunk);
+    if (i < d_out) row_ptr[i] = static_cast<int32_t>(pcarry + ex);
+    __syncthreads();
+    if (tid == 0) pcarry += tot_chunk;
+    __syncthreads();
+  }
+  if (tid == 0) row_ptr[d_out] = static_cast<int32_t>(pcarry);
+}
+
+hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int m, double t,
+                           int32_t* row_ptr, void* scratch, hipStream_t st) {
+  char* base = static_cast<char*>(scratch);
+  double* s = reinterpret_cast<double*>(base);
+  int64_t* budget = reinterpret_cast<int64_t*>(base + static_cast<size_t>(d_out) * 8);
+  int32_t* fixed = reinterpret_cast<int32_t*>(base + static_cast<size_t>(d_out) * 16);
+  hipLaunchKernelGGL(adaalloc_kernel, dim3(1), dim3(kAllocThreads), 0, st, w, d_out, d_in, p, m, t,
+                     row_ptr, s, budget, fixed);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ selection
+// One workgroup per row i: C = dWq[i] H in fp64 (LDS-staged FWHT), then the
+// k = p_i columns first in the order (-|C_j|, j) are emitted ascending as
+// E rows (i, j) with c = fp32_RNE(C_j). The k-th largest magnitude tau is
+// found by bisection on the IEEE bit pattern of |C| (monotone for
+// non-negative doubles; +0 and -0 share the pattern 0); every |C| > tau is
+// taken and the lowest-index columns with |C| == tau fill the rest.
+template <int LOG_N>
+struct SelCfg {
+  using F = Fwht<LOG_N>;
+  static constexpr int BLOCK = F::TPR < 64 ? 64 : F::TPR;
+};
+
+template <int LOG_N>
+__global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
+    const float* __restrict__ dWq, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ E,
+    float* __restrict__ c) {
+  using F = Fwht<LOG_N>;
+  __shared__ double lds[F::LDS];
+  __shared__ int red[32];
+  __shared__ int scan_tmp[16];
+  const int row = blockIdx.x;
+  const int u = threadIdx.x;
+  const bool active = u < F::TPR;
+  const int base = row_ptr[row];
+  const int k = row_ptr[row + 1] - base;
+
+  double v[F::EPT];
+  if (active) {
+    const float* src = dWq + static_cast<int64_t>(row) * F::N + u * F::EPT;
+    if constexpr (F::EPT == 16) {
+      load16(src, v);
+    } else {
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) v[r] = static_cast<double>(src[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) v[r] = 0.0;
+  }
+  F::run(v, lds, u, active);
+  // back to natural order, then to "EPT consecutive columns per thread"
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) lds[F::pad(F::out_index(u, r))] = v[r];
+  }
+  __syncthreads();
+  unsigned long long key[F::EPT];
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) {
+      v[r] = lds[F::pad(u * F::EPT + r)];
+      key[r] = static_cast<unsigned long long>(__double_as_longlong(v[r])) & 0x7FFFFFFFFFFFFFFFull;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) key[r] = 0;
+  }
+
+  unsigned long long tau = 0;
+  int need = 0;      // how many |C| == tau are taken (lowest index first)
+  bool all = (k >= F::N), none = (k <= 0);
+  int parity = 0;
+  if (!all && !none) {
+    unsigned long long lo = 0, hi = 1ull << 63;   // count(>=lo) >= k > count(>=hi)
+    while (hi - lo > 1) {
+      const unsigned long long mid = lo + ((hi - lo) >> 1);
+      int cnt = 0;
+      if (active) {
+#pragma unroll
+        for (int r = 0; r < F::EPT; ++r) cnt += (key[r] >= mid) ? 1 : 0;
+      }
+      cnt = block_sum_i32(cnt, red, parity);
+      parity ^= 1;
+      if (cnt >= k) lo = mid; else hi = mid;
+    }
+    tau = lo;
+    int gt = 0;
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) gt += (key[r] > tau) ? 1 : 0;
+    }
+    gt = block_sum_i32(gt, red, parity);
+    parity ^= 1;
+    need = k - gt;
+  }
+
+  // selection flags in column order
+  unsigned sel = 0;
+  int nsel = 0;
+  {
+    int neq = 0;
+    if (active && !all && !none) {
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) neq += (key[r] == tau) ? 1 : 0;
+    }
+    int tot;
+    const int eq_before = block_excl_scan_i32(neq, scan_tmp, &tot);
+    if (active) {
+      int e = eq_before;
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) {
+        bool take;
+        if (all) take = true;
+        else if (none) take = false;
+        else if (key[r] > tau) take = true;
+        else if (key[r] == tau) { take = e < need; ++e; }
+        else take = false;
+        if (take) { sel |= 1u << r; ++nsel; }
+      }
+    }
+  }
+  int tot;
+  const int pos0 = block_excl_scan_i32(nsel, scan_tmp, &tot);
+  if (active) {
+    int pos = base + pos0;
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) {
+      if (sel & (1u << r)) {
+        E[2 * static_cast<int64_t>(pos)] = row;
+        E[2 * static_cast<int64_t>(pos) + 1] = u * F::EPT + r;
+        c[pos] = __double2float_rn(v[r]);
+        ++pos;
+      }
+    }
+  }
+}
+
+hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
+                              int32_t* E, float* c, hipStream_t s) {
+  switch (log_n) {
+#define QWHA_CASE(L)                                                                        \
+  case L:                                                                                   \
+    hipLaunchKernelGGL(init_select_kernel<L>, dim3(d_out), dim3(SelCfg<L>::BLOCK), 0, s, dWq, \
+                       row_ptr, E, c);                                                      \
+    return hipGetLastError();
+    QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
+    QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
+    QWHA_CASE(14)
+#undef QWHA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------ CSC index
+// Stable counting sort of E by column: csc_perm lists k column by column,
+// ascending k (hence ascending row) within a column. Rows are cut into
+// chunks; per-chunk column histograms give each chunk its slot range per
+// column, and each chunk then places its rows in order (the columns within
+// one row are distinct, so a row's entries are placed in parallel).
+constexpr int kCscThreads = 256;
+
+static int csc_chunks(int d_out) { return d_out < 256 ? d_out : 256; }
+
+size_t csc_scratch_bytes(int d_out, int d_in) {
+  return static_cast<size_t>(csc_chunks(d_out)) * d_in * 4 + 256;
+}
+
+__global__ __launch_bounds__(kCscThreads) void csc_hist_kernel(const int32_t* __restrict__ row_ptr,
+                                                               const int32_t* __restrict__ E,
+                                                               int d_out, int d_in, int nchunks,
+                                                               int32_t* __restrict__ hist) {
+  extern __shared__ int h[];
+  const int ch = blockIdx.x;
+  const int r0 = static_cast<int>(static_cast<int64_t>(d_out) * ch / nchunks);
+  const int r1 = static_cast<int>(static_cast<int64_t>(d_out) * (ch + 1) / nchunks);
+  for (int j = threadIdx.x; j < d_in; j += kCscThreads) h[j] = 0;
+  __syncthreads();
+  for (int k = row_ptr[r0] + threadIdx.x; k < row_ptr[r1]; k += kCscThreads)
+    atomicAdd(&h[E[2 * static_cast<int64_t>(k) + 1]], 1);
+  __syncthreads();
+  for (int j = threadIdx.x; j < d_in; j += kCscThreads)
+    hist[static_cast<int64_t>(ch) * d_in + j] = h[j];
+}
+
+// col_ptr and, in place, hist[ch][j] -> first slot of chunk ch in column j
+__global__ __launch_bounds__(1024) void csc_colptr_kernel(int32_t* __restrict__ hist, int d_in,
+                                                          int nchunks, int32_t* __restrict__ col_ptr) {
+  __shared__ int scan_tmp[16];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < d_in; base += 1024) {
+    const int j = base + threadIdx.x;
+    int cnt = 0;
+    if (j < d_in)
+      for (int ch = 0; ch < nchunks; ++ch) cnt += hist[static_cast<int64_t>(ch) * d_in + j];
+    int tot;
+    const int ex = block_excl_scan_i32(cnt, scan_tmp, &tot);
+    if (j < d_in) {
+      int run = carry + ex;
+      col_ptr[j] = run;
+      for (int ch = 0; ch < nchunks; ++ch) {
+        const int64_t a = static_cast<int64_t>(ch) * d_in + j;
+        const int hv = hist[a];
+        hist[a] = run;
+        run += hv;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) col_ptr[d_in] = carry;
+}
+
+__global__ __launch_bounds__(kCscThreads) void csc_place_kernel(const int32_t* __restrict__ row_ptr,
+                                                                const int32_t* __restrict__ E,
+                                                                int d_out, int d_in, int nchunks,
+                                                                const int32_t* __restrict__ start,
+                                                                int32_t* __restrict__ perm) {
+  extern __shared__ int run[];
+  const int ch = blockIdx.x;
+  const int r0 = static_cast<int>(static_cast<int64_t>(d_out) * ch / nchunks);
+  const int r1 = static_cast<int>(static_cast<int64_t>(d_out) * (ch + 1) / nchunks);
+  for (int j = threadIdx.x; j < d_in; j += kCscThreads) run[j] = 0;
+  __syncthreads();
+  for (int r = r0; r < r1; ++r) {
+    for (int k = row_ptr[r] + threadIdx.x; k < row_ptr[r + 1]; k += kCscThreads) {
+      const int j = E[2 * static_cast<int64_t>(k) + 1];
+      const int slot = start[static_cast<int64_t>(ch) * d_in + j] + run[j];
+      run[j] += 1;
+      perm[slot] = k;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
+                            int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s) {
+  const int nchunks = csc_chunks(d_out);
+  int32_t* hist = static_cast<int32_t*>(scratch);
+  const size_t sh = static_cast<size_t>(d_in) * 4;
+  hipLaunchKernelGGL(csc_hist_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
+                     d_in, nchunks, hist);
+  hipLaunchKernelGGL(csc_colptr_kernel, dim3(1), dim3(1024), 0, s, hist, d_in, nchunks, col_ptr);
+  hipLaunchKernelGGL(csc_place_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
+                     d_in, nchunks, hist, csc_perm);
+  return hipGetLastError();
+}
+
+}  // namespace qwha

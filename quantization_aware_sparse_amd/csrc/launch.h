@@ -1,0 +1,68 @@
+// Internal launchers (C++), called by the C-ABI layer in api.hip after it
+// has validated every argument. Each returns the HIP error of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qwha {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+inline size_t dt_size(Dt d) { return d == Dt::F32 ? 4 : 2; }
+
+// out[r][:] = scale * FWHT(in[r][:]) (+ out[r][:] if accumulate)
+hipError_t launch_fwht(const void* in, Dt in_dt, void* out, Dt out_dt, int64_t rows,
+                       int log_n, float scale, int accumulate, hipStream_t s);
+
+// ---- init
+hipError_t launch_row_norms(const float* dWq, int d_out, int d_in, double* w, hipStream_t s);
+hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int m, double t,
+                           int32_t* row_ptr, void* scratch, hipStream_t s);
+size_t adaalloc_scratch_bytes(int d_out);
+hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
+                              int32_t* E, float* c, hipStream_t s);
+size_t csc_scratch_bytes(int d_out, int d_in);
+hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
+                            int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s);
+
+// ---- materialize
+hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
+                              int log_n, float alpha, Dt out_dt, void* dW, int accumulate,
+                              hipStream_t s);
+
+// ---- adapter forward / backward (gather SpMM / SDDMM)
+struct SpmmPlan {
+  int tt;        // tokens per tile
+  int jb;        // source columns per staged block
+  int rows_wg;   // output rows per workgroup
+  int nblk;      // source blocks
+  int64_t ntiles;
+};
+SpmmPlan spmm_plan(int64_t T, int n_src, int n_out);
+size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl);
+
+// CSR (forward): packed (LDS byte offset, value) per nonzero and per-(row, block)
+// segment starts, from row_ptr / E / c.
+hipError_t launch_prep_csr(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
+                           int64_t nnz, const SpmmPlan& pl, void* prep, hipStream_t s);
+// CSC (backward): same from col_ptr / csc_perm / E / c, keyed by rows i.
+hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* csc_perm, const int32_t* E,
+                           const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
+                           hipStream_t s);
+
+// out[t][o] (+)= alpha * sum_k val_k * src[t][col_k]; with zsrc, also
+// partial[tile][k] = sum_{t in tile} src[t][col_k] * zsrc[t][o].
+hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const void* prep,
+                       int64_t nnz, int n_out, const SpmmPlan& pl, float alpha, void* out,
+                       Dt out_dt, int accumulate, const float* zsrc, float* partial,
+                       hipStream_t s);
+
+// dc[perm[q]] = alpha * sum_tile partial[tile][q]   (fixed tile order)
+hipError_t launch_dc_reduce(const float* partial, int64_t ntiles, int64_t nnz,
+                            const int32_t* csc_perm, float alpha, float* dc, hipStream_t s);
+
+hipError_t launch_sign_update(float* c, const float* dc, int64_t p, float step, hipStream_t s);
+
+}  // namespace qwha

@@ -1,0 +1,122 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/qwha.h declares, and its host-side validation rejects bad arguments
+with the documented status before touching the GPU. No compute call is made
+(nothing here passes validation)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qwha.h")
+LIB = os.path.join(ROOT, "quantization_aware_sparse_amd", "libqwha.so")
+
+OK, INVALID, SHAPE, BUDGET, DTYPE, ALIGN, WORKSPACE, HIP = range(8)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwha_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not os.path.exists(LIB):
+        pytest.fail("libqwha.so is not built (run __graft_entry__.build())")
+    from quantization_aware_sparse_amd import _lib
+    return _lib.lib
+
+
+def test_exports_every_header_symbol(q):
+    names = header_functions()
+    assert len(names) >= 12
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+    from quantization_aware_sparse_amd import _lib
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings(q):
+    for s in range(8):
+        assert q.qwha_status_string(s)
+    assert q.qwha_status_string(OK) == b"ok"
+    assert q.qwha_version() >= 100
+
+
+def test_workspace_queries(q):
+    a = q.qwha_fwd_workspace_bytes(8192, 4096, 4096, 524288)
+    assert a >= 8192 * 4096 * 4 + 524288 * 8
+    b = q.qwha_bwd_workspace_bytes(8192, 4096, 4096, 524288)
+    assert b >= 2 * 8192 * 4096 * 4 + 524288 * 8
+    assert q.qwha_init_workspace_bytes(4096, 4096) >= 4096 * 8
+    assert q.qwha_fwd_workspace_bytes(-1, 4096, 4096, 1) == 0
+
+
+FAKE = 0x10000          # aligned, never dereferenced (validation fails first)
+
+
+def _fwd(q, **kw):
+    a = dict(x=FAKE, act=1, T=16, d_in=256, d_out=256, p=2048, row_ptr=FAKE, E=FAKE, c=FAKE,
+             alpha=1.0, y=FAKE, acc=0, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return q.qwha_fwd(a["x"], a["act"], a["T"], a["d_in"], a["d_out"], a["p"], a["row_ptr"],
+                      a["E"], a["c"], a["alpha"], a["y"], a["acc"], a["ws"], a["wsb"],
+                      a["stream"])
+
+
+def test_fwd_validation(q):
+    assert _fwd(q, d_in=12) == SHAPE
+    assert _fwd(q, d_in=32768) == SHAPE
+    assert _fwd(q, d_in=1) == SHAPE
+    assert _fwd(q, d_out=0) == SHAPE
+    assert _fwd(q, act=7) == DTYPE
+    assert _fwd(q, p=256 * 256 + 1) == BUDGET
+    assert _fwd(q, p=-1) == BUDGET
+    assert _fwd(q, x=None) == INVALID
+    assert _fwd(q, x=FAKE + 4) == ALIGN
+    assert _fwd(q, E=FAKE + 2) == ALIGN
+    assert _fwd(q, acc=2) == INVALID
+    assert _fwd(q, alpha=float("inf")) == INVALID
+    assert _fwd(q, ws=None) == WORKSPACE
+    assert _fwd(q, wsb=10) == WORKSPACE
+    assert b"workspace" in q.qwha_last_error()
+    assert _fwd(q, T=-3) == SHAPE
+
+
+def test_init_validation(q):
+    def call(**kw):
+        a = dict(dWq=FAKE, d_out=256, d_in=256, p=2048, m=3, t=1.0, row_ptr=FAKE, E=FAKE,
+                 c=FAKE, col_ptr=FAKE, perm=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_init_select(a["dWq"], a["d_out"], a["d_in"], a["p"], a["m"], a["t"],
+                                  a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["perm"],
+                                  a["ws"], a["wsb"], None)
+    assert call(p=3 * 256 - 1) == BUDGET            # below the per-row floor
+    assert call(p=256 * 256 + 1) == BUDGET
+    assert call(m=-1) == INVALID
+    assert call(t=0.0) == INVALID
+    assert call(t=float("nan")) == INVALID
+    assert call(d_in=100) == SHAPE
+    assert call(dWq=FAKE + 8) == ALIGN
+    assert call(E=None) == INVALID
+    assert call() == WORKSPACE                      # everything else fine, no workspace
+
+
+def test_bwd_materialize_fwht_validation(q):
+    assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 24, 8, 1.0, 0, FAKE, 0, None) == SHAPE
+    assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 16, 8, 1.0, 5, FAKE, 0, None) == DTYPE
+    assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 16, 8, 1.0, 0, None, 0, None) == INVALID
+    assert q.qwha_fwht(FAKE, 0, FAKE, 0, 4, 48, 1.0, None) == SHAPE
+    assert q.qwha_fwht(FAKE, 0, FAKE + 4, 0, 4, 64, 1.0, None) == ALIGN
+    assert q.qwha_sign_update(FAKE, FAKE, -1, 1e-3, None) == BUDGET
+    r = q.qwha_bwd(FAKE, FAKE, 1, 64, 256, 256, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0,
+                   FAKE, 0, FAKE, FAKE, 0, None)
+    assert r == WORKSPACE
+    r = q.qwha_bwd(FAKE, FAKE, 1, 64, 256, 256, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0,
+                   FAKE + 8, 0, FAKE, FAKE, 1 << 30, None)
+    assert r == ALIGN

@@ -1,0 +1,367 @@
+"""Parity of the HIP path (through the C-ABI) with the fp64 CPU oracle.
+
+Bars: indices / budgets / permutations bit-exact; floating outputs within the
+normwise relative error max|a-b|/max|b| of 1e-5 for fp32 activations and
+2e-2 for bf16 activations; dW and c always at 1e-5 (they depend only on fp32
+c). Small shapes are compared element by element on every output; the full
+layer configurations (the same launch configuration bench.py times) are
+compared on E/row_ptr/col_ptr/csc_perm in full and on sampled tokens (y, dx)
+and sampled rows of F (dc) that the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def q():
+    _need_gpu()
+    import quantization_aware_sparse_amd as qq
+    return qq
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+DEV = "cuda:0"
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_np(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def tol(act):
+    return 1e-5 if act == "f32" else 2e-2
+
+
+def init_both(q, dwq, p, m=3, t=1.0):
+    ref = O.init_select(dwq, p, m=m, t=t, with_diagnostics=True)
+    got = q.qwha_init_select(to_dev(dwq), p, m, t)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def assert_init_equal(ref, got):
+    for key in ("row_ptr", "E", "col_ptr", "csc_perm"):
+        a = got[key].cpu().numpy()
+        assert a.shape == ref[key].shape, key
+        if not np.array_equal(a, ref[key]):
+            bad = np.nonzero((a != ref[key]).reshape(len(a), -1).any(1))[0][:5]
+            raise AssertionError(f"{key} differs at {bad}")
+    assert O.rel_err(got["c"].cpu().numpy(), ref["c"]) <= 1e-6
+
+
+# ------------------------------------------------------------------ FWHT
+@pytest.mark.parametrize("log_n", list(range(1, 15)))
+@pytest.mark.parametrize("dts", [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"),
+                                 ("bf16", "bf16")])
+def test_fwht_parity(q, log_n, dts):
+    n = 1 << log_n
+    rows = 37 if n <= 4096 else 5
+    say("fwht", n, dts, rows)
+    rng = np.random.default_rng(log_n)
+    a = rng.standard_normal((rows, n)).astype(np.float32)
+    if dts[0] == "bf16":
+        a = synth.f32_to_bf16_bits(a)
+    x = to_dev(a)
+    out_dt = torch.float32 if dts[1] == "f32" else torch.bfloat16
+    scale = 1.0 / n
+    y = q.qwha_fwht(x, scale, out_dtype=out_dt)
+    torch.cuda.synchronize()
+    ref = synth.act_to_f64(a) @ O.sylvester(n) * scale
+    bound = 1e-5 if dts[1] == "f32" else 2e-2
+    assert O.rel_err(to_np(y), ref) <= bound
+
+
+# ------------------------------------------------------------------ init
+def _edge_dwq(d_out, d_in, seed):
+    rng = np.random.default_rng(seed)
+    a = (0.01 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    return a
+
+
+@pytest.mark.parametrize("d_out,d_in,p,m", [
+    (37, 2, 40, 1), (5, 4, 12, 2), (64, 16, 300, 3), (300, 64, 2500, 3),
+    (129, 128, 9000, 3), (17, 1024, 2000, 3), (3, 8192, 900, 3), (2, 16384, 1000, 3),
+    (64, 256, 64 * 256, 3), (50, 512, 150, 3)])
+def test_init_select_edges(q, d_out, d_in, p, m):
+    say("init edge", d_out, d_in, p, m)
+    dwq = _edge_dwq(d_out, d_in, d_out + d_in)
+    ref, got = init_both(q, dwq, p, m)
+    assert_init_equal(ref, got)
+
+
+def test_init_select_ties_zero_rows_and_bounds(q):
+    # spike rows (every |C| equal: ties to the lower column), all-zero rows
+    # (w = 0: the floor binds), one dominant row (the cap binds)
+    d_out, d_in = 40, 64
+    dwq = _edge_dwq(d_out, d_in, 7) * 0.01
+    dwq[3] = 0.0
+    dwq[3, 9] = 0.5
+    dwq[11] = 0.0
+    dwq[12] = 0.0
+    dwq[20] = 50.0 * np.sign(dwq[20] + 1e-9)
+    dwq[30] = 0.0
+    dwq[30, 0] = -0.25
+    say("init ties/zero/cap")
+    ref, got = init_both(q, dwq, 1500, 3)
+    assert ref["budgets"][20] == d_in and ref["budgets"][11] == 3
+    assert_init_equal(ref, got)
+
+
+def test_init_select_temperature_two(q):
+    dwq = _edge_dwq(100, 128, 3)
+    say("init t=2")
+    ref, got = init_both(q, dwq, 3000, 3, t=2.0)
+    if np.min(ref["budget_margin"]) > 1e-9:
+        assert_init_equal(ref, got)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5"])
+def test_init_select_configs(q, cfg):
+    for spec in synth.config_specs(cfg):
+        say("init config", spec.name)
+        layer = synth.make_layer(spec, seed=0)
+        ref, got = init_both(q, layer.dwq, spec.p, 3)
+        amb_gap = np.sum((ref["boundary_gap"] > 0) & (ref["boundary_gap"] < 1e-9))
+        amb_budget = np.sum(ref["budget_margin"] < 1e-9)
+        assert amb_gap == 0 and amb_budget == 0, "ambiguous rows at this seed"
+        assert_init_equal(ref, got)
+
+
+# ------------------------------------------------------------------ materialize
+@pytest.mark.parametrize("d_out,d_in,p", [(37, 2, 40), (300, 64, 2500), (17, 1024, 2000),
+                                          (3, 8192, 900), (2, 16384, 1000), (256, 256, 2048)])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_materialize(q, d_out, d_in, p, out_dt):
+    say("materialize", d_out, d_in, p, out_dt)
+    dwq = _edge_dwq(d_out, d_in, 11)
+    r = O.init_select(dwq, p, m=1)
+    dt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    alpha = 0.75
+    got = q.qwha_materialize(to_dev(r["row_ptr"]), to_dev(r["E"]), to_dev(r["c"]), d_out, d_in,
+                             alpha, out_dtype=dt)
+    torch.cuda.synchronize()
+    ref = O.materialize(r["E"], r["c"], d_out, d_in, alpha)
+    assert O.rel_err(to_np(got), ref) <= (1e-5 if out_dt == "f32" else 2e-2)
+    # accumulate mode: dW += alpha F H^-1
+    base = np.random.default_rng(1).standard_normal((d_out, d_in)).astype(np.float32)
+    acc = to_dev(base)
+    q.qwha_materialize(to_dev(r["row_ptr"]), to_dev(r["E"]), to_dev(r["c"]), d_out, d_in,
+                       alpha, out=acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert O.rel_err(to_np(acc), base + ref) <= 1e-5
+
+
+def test_materialize_full_budget_reconstructs(q):
+    d_out, d_in = 16, 128
+    dwq = _edge_dwq(d_out, d_in, 5)
+    r = O.init_select(dwq, d_out * d_in, m=3)
+    got = q.qwha_materialize(to_dev(r["row_ptr"]), to_dev(r["E"]), to_dev(r["c"]), d_out, d_in)
+    torch.cuda.synchronize()
+    assert O.rel_err(to_np(got), dwq.astype(np.float64)) <= 1e-5
+
+
+# ------------------------------------------------------------------ fwd / bwd small
+def _small_case(d_out, d_in, p, T, act, seed):
+    dwq = _edge_dwq(d_out, d_in, seed)
+    r = O.init_select(dwq, p, m=3)
+    rng = np.random.default_rng(seed + 1)
+    x = rng.standard_normal((T, d_in)).astype(np.float32)
+    dy = rng.standard_normal((T, d_out)).astype(np.float32)
+    if act == "bf16":
+        x, dy = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(dy)
+    return r, x, dy
+
+
+def _dev_adapter(r):
+    return {k: to_dev(r[k]) for k in ("row_ptr", "E", "c", "col_ptr", "csc_perm")}
+
+
+@pytest.mark.parametrize("d_out,d_in,p,T", [
+    (256, 256, 2048, 64), (300, 64, 2500, 77), (37, 2, 74, 130), (513, 128, 4000, 129),
+    (64, 1024, 6000, 200), (40, 8192, 2000, 9), (3, 16384, 300, 5), (1100, 32, 3300, 1)])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_fwd_bwd_small(q, d_out, d_in, p, T, act):
+    say("fwd/bwd small", d_out, d_in, p, T, act)
+    r, x, dy = _small_case(d_out, d_in, p, T, act, d_out + T)
+    a = _dev_adapter(r)
+    alpha = 1.25
+    xt, dyt = to_dev(x), to_dev(dy)
+    y = q.qwha_fwd(xt, d_out, a["row_ptr"], a["E"], a["c"], alpha)
+    dx, dc = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"],
+                        alpha)
+    torch.cuda.synchronize()
+    x64, dy64 = synth.act_to_f64(x), synth.act_to_f64(dy)
+    dW = O.materialize(r["E"], r["c"], d_out, d_in, alpha)
+    y_ref = O.forward(x64, dW)
+    dx_ref, dc_ref = O.backward(x64, dy64, r["E"], r["c"], d_out, d_in, alpha, dW=dW)
+    assert O.rel_err(to_np(y), y_ref) <= tol(act)
+    assert O.rel_err(to_np(dx), dx_ref) <= tol(act)
+    assert O.rel_err(to_np(dc), dc_ref) <= tol(act)
+
+
+def test_fwd_bwd_accumulate_and_partial_outputs(q):
+    say("accumulate")
+    r, x, dy = _small_case(300, 64, 2500, 77, "f32", 3)
+    a = _dev_adapter(r)
+    xt, dyt = to_dev(x), to_dev(dy)
+    base_y = np.random.default_rng(2).standard_normal((77, 300)).astype(np.float32)
+    base_dx = np.random.default_rng(3).standard_normal((77, 64)).astype(np.float32)
+    yt, dxt = to_dev(base_y), to_dev(base_dx)
+    q.qwha_fwd(xt, 300, a["row_ptr"], a["E"], a["c"], 1.0, y=yt, accumulate=True)
+    q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"], 1.0,
+               need_dc=False, dx=dxt, accumulate_dx=True)
+    _, dc_only = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"],
+                            a["csc_perm"], 1.0, need_dx=False)
+    torch.cuda.synchronize()
+    dW = O.materialize(r["E"], r["c"], 300, 64, 1.0)
+    dx_ref, dc_ref = O.backward(x, dy, r["E"], r["c"], 300, 64, 1.0, dW=dW)
+    assert O.rel_err(to_np(yt), base_y + O.forward(x, dW)) <= 1e-5
+    assert O.rel_err(to_np(dxt), base_dx + dx_ref) <= 1e-5
+    assert O.rel_err(to_np(dc_only), dc_ref) <= 1e-5
+
+
+def test_zero_tokens(q):
+    r, x, dy = _small_case(64, 32, 500, 4, "f32", 9)
+    a = _dev_adapter(r)
+    xt = torch.empty((0, 32), device=DEV)
+    dyt = torch.empty((0, 64), device=DEV)
+    y = q.qwha_fwd(xt, 64, a["row_ptr"], a["E"], a["c"], 1.0)
+    dc = torch.full((500,), 7.0, device=DEV)
+    q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"], 1.0,
+               need_dx=False, dc=dc)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+    assert torch.count_nonzero(dc).item() == 0
+
+
+def test_backward_deterministic(q):
+    say("determinism")
+    r, x, dy = _small_case(513, 128, 4000, 300, "bf16", 4)
+    a = _dev_adapter(r)
+    xt, dyt = to_dev(x), to_dev(dy)
+    outs = []
+    for _ in range(2):
+        dx, dc = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"],
+                            a["csc_perm"], 1.0)
+        y = q.qwha_fwd(xt, 513, a["row_ptr"], a["E"], a["c"], 1.0)
+        torch.cuda.synchronize()
+        outs.append((dx.clone(), dc.clone(), y.clone()))
+    for u, v in zip(outs[0], outs[1]):
+        assert torch.equal(u, v)
+
+
+def test_autograd_function(q):
+    say("autograd")
+    r, x, dy = _small_case(256, 256, 2048, 64, "f32", 6)
+    a = _dev_adapter(r)
+    xt = to_dev(x).requires_grad_(True)
+    ct = a["c"].clone().requires_grad_(True)
+    y = q.WHAFunction.apply(xt, ct, a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], 256, 1.0)
+    y.backward(to_dev(dy))
+    torch.cuda.synchronize()
+    dW = O.materialize(r["E"], r["c"], 256, 256, 1.0)
+    dx_ref, dc_ref = O.backward(x, dy, r["E"], r["c"], 256, 256, 1.0, dW=dW)
+    assert O.rel_err(to_np(y), O.forward(x, dW)) <= 1e-5
+    assert O.rel_err(to_np(xt.grad), dx_ref) <= 1e-5
+    assert O.rel_err(to_np(ct.grad), dc_ref) <= 1e-5
+
+
+# ------------------------------------------------------------------ full configs
+def _sample_tokens(T, k, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(k, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+def _sample_rows(d_out, k, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(d_out, size=min(k, d_out), replace=False).tolist()) | {0, d_out - 1}
+    return np.array(sorted(s))
+
+
+def _check_layer_full(q, spec, layer, x, dy, got_init=None):
+    """Init (bit-exact), materialize, fwd, bwd at full size; sampled checks."""
+    d_out, d_in, T = spec.d_out, spec.d_in, x.shape[0]
+    ref = O.init_select(layer.dwq, spec.p, m=3)
+    if got_init is None:
+        got_init = q.qwha_init_select(to_dev(layer.dwq), spec.p, 3, 1.0)
+    torch.cuda.synchronize()
+    assert_init_equal(ref, got_init)
+    a = got_init
+    xt, dyt = to_dev(x), to_dev(dy)
+    dW = q.qwha_materialize(a["row_ptr"], a["E"], a["c"], d_out, d_in, 1.0)
+    y = q.qwha_fwd(xt, d_out, a["row_ptr"], a["E"], a["c"], 1.0)
+    dx, dc = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"], 1.0)
+    torch.cuda.synchronize()
+    dW_ref = O.materialize(ref["E"], ref["c"], d_out, d_in, 1.0)
+    rows = _sample_rows(d_out, 64, 1)
+    assert O.rel_err(to_np(dW[rows]), dW_ref[rows]) <= 1e-5
+    toks = _sample_tokens(T, 48, 2)
+    x64 = synth.act_to_f64(x[toks])
+    dy64 = synth.act_to_f64(dy[toks])
+    assert O.rel_err(to_np(y[toks]), O.forward(x64, dW_ref)) <= tol(spec.act)
+    assert O.rel_err(to_np(dx[toks]), dy64 @ dW_ref) <= tol(spec.act)
+    drows = _sample_rows(d_out, 6, 3)
+    ks, vals = O.backward_dc_rows(synth.act_to_f64(x), synth.act_to_f64(dy), ref["E"], drows,
+                                  d_in, 1.0)
+    assert O.rel_err(to_np(dc)[ks], vals) <= tol(spec.act)
+    return a, dc
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
+def test_full_config_layer(q, cfg):
+    spec = synth.config_specs(cfg)[0]
+    say("full config", cfg)
+    layer = synth.make_layer(spec, seed=0)
+    x, dy = synth.make_activations(spec, seed=0)
+    _check_layer_full(q, spec, layer, x, dy)
+
+
+def test_full_config_attention_block_step(q):
+    """Training step of the GQA block: four adapters fwd+bwd, c += 1e-3 sign(dc),
+    dW re-materialised. The update is checked bitwise against the GPU's own dc
+    (an exactly-zero or near-zero dc would make the sign ambiguous); signs must
+    agree with the oracle wherever |dc_ref| exceeds the observed error; the
+    re-materialised dW is checked against the oracle fed the GPU's c'."""
+    specs = synth.config_specs("c5")
+    for spec in specs:
+        say("c5", spec.name)
+        layer = synth.make_layer(spec, seed=0)
+        x, dy = synth.make_activations(spec, seed=0, x_stream=synth.C5_X_STREAM[spec.name])
+        a, dc = _check_layer_full(q, spec, layer, x, dy)
+        c_old = a["c"].clone()
+        q.qwha_sign_update(a["c"], dc, 1e-3)
+        torch.cuda.synchronize()
+        c_new = a["c"].cpu().numpy()
+        assert np.array_equal(c_new, O.sign_update(c_old.cpu().numpy(), dc.cpu().numpy()))
+        dW2 = q.qwha_materialize(a["row_ptr"], a["E"], a["c"], spec.d_out, spec.d_in, 1.0)
+        torch.cuda.synchronize()
+        rows = _sample_rows(spec.d_out, 32, 4)
+        E_np = a["E"].cpu().numpy()
+        sel = np.isin(E_np[:, 0], rows)
+        ref_rows = O.materialize(E_np[sel], c_new[sel], spec.d_out, spec.d_in, 1.0)[rows]
+        assert O.rel_err(to_np(dW2[rows]), ref_rows) <= 1e-5
