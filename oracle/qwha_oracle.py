@@ -25,7 +25,8 @@ Readings of points the pages leave open (all listed in the design notes):
     p_i proportional to w_i^(1/t) (t = 1: proportional), floor rounding, a
     per-row floor m and cap d_in enforced by fix-and-reallocate passes (rows
     below the floor are fixed first; only when none are, rows above the cap
-    are fixed), then the leftover (< d_out) goes one unit each to the rows
+    are fixed and the floored rows released), i.e. the clamped proportional
+    split, then the leftover (< d_out) goes one unit each to the rows
     with the smallest budget, lower row index first, rows at the cap skipped.
   * "Activation error magnitude" without calibration data is the row's l2
     norm of dW_Q (identity Hessian).
@@ -106,10 +107,14 @@ def adaalloc(w: np.ndarray, p: int, d_in: int, m: int = 3,
              t: float = 1.0) -> np.ndarray:
     """Per-row budgets p_i with sum p_i = p.
 
-    Proportional pass: p_i = floor(P * s_i / S) over the rows U not yet fixed,
+    Proportional pass: share q_i = P * s_i / S over the rows U not yet fixed,
     with s_i = w_i^(1/t), P = p - (budgets of fixed rows), S = sum_U s_i
-    (floor(P/|U|) when S = 0). Rows below m are fixed at m; if there are none,
-    rows above d_in are fixed at d_in; repeat until a pass fixes nothing.
+    (q_i = floor(P/|U|) when S = 0), and p_i = floor(q_i). Rows with q_i < m
+    are fixed at m; if there are none, rows with q_i > d_in are fixed at
+    d_in and every row fixed at the floor is
+    released again (capping raises the others' share); repeat until a pass
+    fixes nothing. This reaches the clamped proportional split
+    p_i = clamp(lambda * s_i, m, d_in) before rounding.
     The leftover r = p - sum p_i goes one unit each to the rows with the
     smallest p_i (lower row index first), skipping rows at d_in; if r exceeds
     the eligible rows, it is handed out in further such rounds."""
@@ -120,23 +125,27 @@ def adaalloc(w: np.ndarray, p: int, d_in: int, m: int = 3,
     s = w if t == 1.0 else w ** (1.0 / t)
     budget = np.zeros(d_out, dtype=np.int64)
     fixed = np.zeros(d_out, dtype=bool)
+    capped = np.zeros(d_out, dtype=bool)
     while not fixed.all():
         U = ~fixed
         P = int(p - budget[fixed].sum())
         S = float(np.sum(s[U]))
+        share = np.zeros(d_out)
         if S > 0.0:
-            budget[U] = np.floor((float(P) * s[U]) / S).astype(np.int64)
+            share[U] = (float(P) * s[U]) / S
         else:
-            budget[U] = P // int(U.sum())
-        low = U & (budget < m)
+            share[U] = float(P // int(U.sum()))
+        budget[U] = np.floor(share[U]).astype(np.int64)
+        low = U & (share < m)
         if low.any():
             budget[low] = m
             fixed |= low
             continue
-        high = U & (budget > d_in)
+        high = U & (share > d_in)
         if high.any():
             budget[high] = d_in
-            fixed |= high
+            capped |= high
+            fixed = capped.copy()          # release the rows fixed at the floor
             continue
         break
     r = int(p - budget.sum())
@@ -161,26 +170,29 @@ def adaalloc_margins(w: np.ndarray, p: int, d_in: int, m: int = 3,
     budget = np.zeros(d_out, dtype=np.int64)
     fixed = np.zeros(d_out, dtype=bool)
     margin = np.full(d_out, np.inf)
+    capped = np.zeros(d_out, dtype=bool)
     while not fixed.all():
         U = ~fixed
         P = int(p - budget[fixed].sum())
         S = float(np.sum(s[U]))
+        share = np.zeros(d_out)
         if S > 0.0:
-            q = (float(P) * s[U]) / S
-            budget[U] = np.floor(q).astype(np.int64)
+            share[U] = (float(P) * s[U]) / S
             margin[:] = np.inf
-            margin[U] = np.abs(q - np.rint(q))
+            margin[U] = np.abs(share[U] - np.rint(share[U]))
         else:
-            budget[U] = P // int(U.sum())
-        low = U & (budget < m)
+            share[U] = float(P // int(U.sum()))
+        budget[U] = np.floor(share[U]).astype(np.int64)
+        low = U & (share < m)
         if low.any():
             budget[low] = m
             fixed |= low
             continue
-        high = U & (budget > d_in)
+        high = U & (share > d_in)
         if high.any():
             budget[high] = d_in
-            fixed |= high
+            capped |= high
+            fixed = capped.copy()
             continue
         break
     margin[fixed] = np.inf

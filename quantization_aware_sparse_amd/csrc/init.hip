@@ -74,10 +74,12 @@ hipError_t launch_row_norms(const float* dWq, int d_out, int d_in, double* w, hi
 }
 
 // ------------------------------------------------------------ AdaAlloc
-// One workgroup. Proportional passes p_i = floor(P s_i / S) over the rows not
-// yet fixed (s_i = w_i^(1/t)); rows below the floor m are fixed at m first,
-// then (only if none were) rows above d_in are fixed at d_in; repeat until a
-// pass fixes nothing. The leftover r = p - sum p_i (< d_out) goes one unit
+// One workgroup. Proportional passes over the rows not yet fixed: share
+// q_i = P s_i / S (s_i = w_i^(1/t)), p_i = floor(q_i). Rows with q_i < m are
+// held at m; if there are none, rows with q_i > d_in are held at d_in and the
+// rows held at the floor are released (capping raises the others' share);
+// repeat until a pass holds nothing. This is the clamped proportional split
+// clamp(lambda s_i, m, d_in) before rounding. The leftover r = p - sum p_i (< d_out) goes one unit
 // each to the rows with the smallest budget, lower row index first, rows at
 // d_in skipped (in further rounds if r exceeds the eligible rows).
 // Finally row_ptr = exclusive scan of the budgets.
@@ -134,31 +136,35 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
     parity ^= 1;
     if (NU == 0) break;
     const long long P = p - F;
-    int low = 0;
+    // share q_i = P s_i / S (unfloored), budget = floor(q_i); fixed: 0 free,
+    // 1 held at the floor m, 2 held at the cap d_in
+    int low = 0, high = 0;
     for (int i = tid; i < d_out; i += kAllocThreads) {
       if (fixed[i]) continue;
-      long long b;
-      if (S > 0.0) b = static_cast<long long>(floor((static_cast<double>(P) * s[i]) / S));
-      else b = P / NU;
-      budget[i] = b;
-      if (b < m) low = 1;
+      const double qi = (S > 0.0) ? (static_cast<double>(P) * s[i]) / S
+                                  : static_cast<double>(P / NU);
+      budget[i] = static_cast<long long>(floor(qi));
+      if (qi < static_cast<double>(m)) { low = 1; fixed[i] = -1; }           // tentative
+      else if (qi > static_cast<double>(d_in)) { high = 1; fixed[i] = -2; }  // tentative
     }
     if (low) flags[0] = 1;
+    if (high) flags[1] = 1;
     __syncthreads();
     if (flags[0]) {
-      for (int i = tid; i < d_out; i += kAllocThreads)
-        if (!fixed[i] && budget[i] < m) { budget[i] = m; fixed[i] = 1; }
+      // rows below the floor are held at m; tentative caps are dropped
+      for (int i = tid; i < d_out; i += kAllocThreads) {
+        if (fixed[i] == -1) { budget[i] = m; fixed[i] = 1; }
+        else if (fixed[i] == -2) fixed[i] = 0;
+      }
       __syncthreads();
       continue;
     }
-    int high = 0;
-    for (int i = tid; i < d_out; i += kAllocThreads)
-      if (!fixed[i] && budget[i] > d_in) high = 1;
-    if (high) flags[1] = 1;
-    __syncthreads();
     if (flags[1]) {
-      for (int i = tid; i < d_out; i += kAllocThreads)
-        if (!fixed[i] && budget[i] > d_in) { budget[i] = d_in; fixed[i] = 1; }
+      // rows above the cap are held at d_in and rows at the floor released
+      for (int i = tid; i < d_out; i += kAllocThreads) {
+        if (fixed[i] == -2) { budget[i] = d_in; fixed[i] = 2; }
+        else if (fixed[i] == 1) fixed[i] = 0;
+      }
       __syncthreads();
       continue;
     }
@@ -413,7 +419,7 @@ hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int3
 // one row are distinct, so a row's entries are placed in parallel).
 constexpr int kCscThreads = 256;
 
-static int csc_chunks(int d_out) { return d_out < 256 ? d_out : 256; }
+static int csc_chunks(int d_out) { return d_out < 64 ? d_out : 64; }
 
 size_t csc_scratch_bytes(int d_out, int d_in) {
   return static_cast<size_t>(csc_chunks(d_out)) * d_in * 4 + 256;
@@ -436,30 +442,34 @@ __global__ __launch_bounds__(kCscThreads) void csc_hist_kernel(const int32_t* __
     hist[static_cast<int64_t>(ch) * d_in + j] = h[j];
 }
 
-// col_ptr and, in place, hist[ch][j] -> first slot of chunk ch in column j
-__global__ __launch_bounds__(1024) void csc_colptr_kernel(int32_t* __restrict__ hist, int d_in,
-                                                          int nchunks, int32_t* __restrict__ col_ptr) {
+// Per column j (one thread each): hist[ch][j] -> number of entries of column
+// j in chunks before ch; the column's total goes to cnt[j].
+__global__ __launch_bounds__(256) void csc_colsum_kernel(int32_t* __restrict__ hist, int d_in,
+                                                         int nchunks, int32_t* __restrict__ cnt) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d_in) return;
+  int run = 0;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int64_t a = static_cast<int64_t>(ch) * d_in + j;
+    const int hv = hist[a];
+    hist[a] = run;
+    run += hv;
+  }
+  cnt[j] = run;
+}
+
+// col_ptr = exclusive scan of the column counts (cnt may alias col_ptr).
+__global__ __launch_bounds__(1024) void csc_scan_kernel(int32_t* __restrict__ col_ptr, int d_in) {
   __shared__ int scan_tmp[16];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   for (int base = 0; base < d_in; base += 1024) {
     const int j = base + threadIdx.x;
-    int cnt = 0;
-    if (j < d_in)
-      for (int ch = 0; ch < nchunks; ++ch) cnt += hist[static_cast<int64_t>(ch) * d_in + j];
+    const int c = (j < d_in) ? col_ptr[j] : 0;
     int tot;
-    const int ex = block_excl_scan_i32(cnt, scan_tmp, &tot);
-    if (j < d_in) {
-      int run = carry + ex;
-      col_ptr[j] = run;
-      for (int ch = 0; ch < nchunks; ++ch) {
-        const int64_t a = static_cast<int64_t>(ch) * d_in + j;
-        const int hv = hist[a];
-        hist[a] = run;
-        run += hv;
-      }
-    }
+    const int ex = block_excl_scan_i32(c, scan_tmp, &tot);
+    if (j < d_in) col_ptr[j] = carry + ex;
     __syncthreads();
     if (threadIdx.x == 0) carry += tot;
     __syncthreads();
@@ -470,7 +480,8 @@ __global__ __launch_bounds__(1024) void csc_colptr_kernel(int32_t* __restrict__ 
 __global__ __launch_bounds__(kCscThreads) void csc_place_kernel(const int32_t* __restrict__ row_ptr,
                                                                 const int32_t* __restrict__ E,
                                                                 int d_out, int d_in, int nchunks,
-                                                                const int32_t* __restrict__ start,
+                                                                const int32_t* __restrict__ col_ptr,
+                                                                const int32_t* __restrict__ before,
                                                                 int32_t* __restrict__ perm) {
   extern __shared__ int run[];
   const int ch = blockIdx.x;
@@ -481,7 +492,7 @@ __global__ __launch_bounds__(kCscThreads) void csc_place_kernel(const int32_t* _
   for (int r = r0; r < r1; ++r) {
     for (int k = row_ptr[r] + threadIdx.x; k < row_ptr[r + 1]; k += kCscThreads) {
       const int j = E[2 * static_cast<int64_t>(k) + 1];
-      const int slot = start[static_cast<int64_t>(ch) * d_in + j] + run[j];
+      const int slot = col_ptr[j] + before[static_cast<int64_t>(ch) * d_in + j] + run[j];
       run[j] += 1;
       perm[slot] = k;
     }
@@ -496,9 +507,11 @@ hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out,
   const size_t sh = static_cast<size_t>(d_in) * 4;
   hipLaunchKernelGGL(csc_hist_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
                      d_in, nchunks, hist);
-  hipLaunchKernelGGL(csc_colptr_kernel, dim3(1), dim3(1024), 0, s, hist, d_in, nchunks, col_ptr);
+  hipLaunchKernelGGL(csc_colsum_kernel, dim3((d_in + 255) / 256), dim3(256), 0, s, hist, d_in,
+                     nchunks, col_ptr);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, col_ptr, d_in);
   hipLaunchKernelGGL(csc_place_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
-                     d_in, nchunks, hist, csc_perm);
+                     d_in, nchunks, col_ptr, hist, csc_perm);
   return hipGetLastError();
 }
 

@@ -9,15 +9,13 @@
 //                    papernotes.org, 损失函数 / 训练策略).
 //
 // Kernel shape (gfx950, wave64): one workgroup = 8 waves = a tile of TT = 128
-// tokens x (8 * R) output rows. Lane l owns tokens 2l and 2l+1 of the tile;
-// each wave owns R output rows and keeps their accumulators in registers.
-// The source matrix (z for the forward, dy for the backward) is staged
-// through LDS in blocks of JB = 128 source columns, token-minor, so that one
-// nonzero (col, val) -- broadcast to the wave through scalar loads -- costs
-// one conflict-free ds_read_b64 and two FMAs per lane. Staging is double
-// buffered: the next block's global loads are in flight while the current
-// block is consumed. The nonzeros of every (output row, source block) pair
-// are contiguous in a packed stream prepared per call.
+// tokens x (8 * 64) output rows (8 * 32 with dc partials); every output row's
+// accumulators for the tile's tokens live in registers. The source matrix (z
+// for the forward, dy for the backward) is staged through LDS in blocks of
+// JB = 128 source columns, token-minor, double buffered: the next block's
+// global loads are in flight while the current block is consumed. The
+// nonzeros of every (output row, source block) pair are contiguous in a
+// packed stream (LDS byte offset of the column, value) prepared per call.
 #include "common.h"
 #include "launch.h"
 
@@ -27,14 +25,14 @@ constexpr int kTT = 128;          // tokens per tile
 constexpr int kJB = 128;          // source columns per staged block
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRfwd = 64;         // output rows per wave, plain SpMM
-constexpr int kRdc = 32;          // output rows per wave when dc partials are also produced
+constexpr int kSfwd = 12;         // rows per 16-lane group, plain SpMM (48 per wave)
+constexpr int kSdc = 8;           // rows per group when dc partials are also produced
 
 SpmmPlan spmm_plan_impl(int64_t T, int n_src, int n_out, bool dc) {
   SpmmPlan pl;
   pl.tt = kTT;
   pl.jb = kJB;
-  pl.rows_wg = kWaves * (dc ? kRdc : kRfwd);
+  pl.rows_wg = kWaves * 4 * (dc ? kSdc : kSfwd);
   pl.nblk = (n_src + kJB - 1) / kJB;
   pl.ntiles = (T + kTT - 1) / kTT;
   (void)n_out;
@@ -175,7 +173,53 @@ struct Stage {
 };
 
 // ------------------------------------------------------------ main kernel
-template <int R, typename SrcT, typename OutT, bool DC>
+// Wave layout: 4 groups of 16 lanes. Group g owns the rows o0 + g*S + s
+// (s < S); lane gl of the group owns tokens t0 + 8*gl .. +7 of the tile, so
+// the 16 lanes of a group cover all 128 tokens. A nonzero of the group's
+// current row is read by the group's 16 lanes as two ds_read_b128 each (512
+// contiguous bytes of the staged block: conflict-free) and costs 8 FMAs per
+// lane. Nonzeros are fetched per lane with vector loads, a batch of 4 at a
+// time, and the first batch of the next row is in flight while the current
+// row is processed. With zsrc (backward), each nonzero also yields
+// sum_{t in lane} src[t][col] * zsrc[t][o], reduced over the group's 16 lanes
+// with four DPP row shifts into lane 15, which stores the tile's partial.
+constexpr int kGroups = 4;
+constexpr int kTPL = 8;          // tokens per lane
+constexpr int kBatch = 4;        // nonzeros fetched per vector load batch
+
+__device__ __forceinline__ float dpp_row_shr(float v, int n) {
+  int r;
+  switch (n) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true); break;
+  }
+  return __int_as_float(r);
+}
+
+// Inclusive prefix over each row of 16 lanes: lane 15 of a row ends with the
+// row's total.
+__device__ __forceinline__ float row16_total(float v) {
+  v += dpp_row_shr(v, 1);
+  v += dpp_row_shr(v, 2);
+  v += dpp_row_shr(v, 4);
+  v += dpp_row_shr(v, 8);
+  return v;
+}
+
+struct Batch {
+  int2 e[kBatch];
+};
+
+__device__ __forceinline__ Batch load_batch(const int2* __restrict__ nz, int k, int k1) {
+  Batch b;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) b.e[u] = (k + u < k1) ? nz[k + u] : make_int2(0, 0);
+  return b;
+}
+
+template <int S, typename SrcT, typename OutT, bool DC>
 __global__ __launch_bounds__(kThreads) void spmm_kernel(
     const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ nz,
     const int32_t* __restrict__ bptr, int64_t nnz, int n_out, int nblk, float alpha,
@@ -183,27 +227,41 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
     float* __restrict__ partial) {
   __shared__ float stage[2][kJB * kTT];
   const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int gl = lane & 15;
   const int w = uniform(threadIdx.x >> 6);
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTT;
-  const int o0 = static_cast<int>(blockIdx.y) * (kWaves * R) + w * R;
+  const int rows_wg = kWaves * kGroups * S;
+  const int orow = static_cast<int>(blockIdx.y) * rows_wg + w * (kGroups * S) + g * S;
   const bool vec_ok = (n_src % Stage<SrcT>::VEC) == 0;
+  const int lds_lane = gl * (kTPL * 4);      // byte offset of the lane's 8 tokens
 
-  float acc[R][2];
+  float acc[S][kTPL];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int q = 0; q < kTPL; ++q) acc[s][q] = 0.f;
 
-  float zr[DC ? R : 1][2];
+  float zr[DC ? S : 1][kTPL];
   if constexpr (DC) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t t = t0 + 2 * lane + q;
+    for (int q = 0; q < kTPL; ++q) {
+      const int64_t t = t0 + kTPL * gl + q;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int o = o0 + r;
-        zr[r][q] = (t < T && o < n_out) ? zsrc[t * n_out + o] : 0.f;
+      for (int s = 0; s < S; ++s) {
+        const int o = orow + s;
+        zr[s][q] = (t < T && o < n_out) ? zsrc[t * n_out + o] : 0.f;
       }
     }
+  }
+
+  // per-slot cursor into the packed stream: start of the current block
+  int kcur[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int o = orow + s;
+    kcur[s] = (o < n_out) ? bptr[static_cast<int64_t>(o) * (nblk + 1)] : 0;
   }
 
   Stage<SrcT> pf;
@@ -213,41 +271,56 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
     pf.store(st);
     __syncthreads();
     if (b + 1 < nblk) pf.load(src, T, n_src, t0, b + 1, vec_ok);
-    const char* sb = reinterpret_cast<const char*>(st) + lane * 8;
+    int kend[S];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int o = o0 + r;
-      if (o >= n_out) break;
-      const int64_t bo = static_cast<int64_t>(o) * (nblk + 1) + b;
-      const int k0 = bptr[bo];
-      const int k1 = bptr[bo + 1];
-      for (int k = k0; k < k1; ++k) {
-        const int2 e = nz[k];
-        const float2 v = *reinterpret_cast<const float2*>(sb + e.x);
-        const float cv = __int_as_float(e.y);
-        acc[r][0] = fmaf(cv, v.x, acc[r][0]);
-        acc[r][1] = fmaf(cv, v.y, acc[r][1]);
-        if constexpr (DC) {
-          float sdc = fmaf(v.x, zr[r][0], v.y * zr[r][1]);
+    for (int s = 0; s < S; ++s) {
+      const int o = orow + s;
+      kend[s] = (o < n_out) ? bptr[static_cast<int64_t>(o) * (nblk + 1) + b + 1] : 0;
+    }
+    const char* sb = reinterpret_cast<const char*>(st) + lds_lane;
+    Batch next = load_batch(nz, kcur[0], kend[0]);
 #pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) sdc += __shfl_xor(sdc, off, 64);
-          if (lane == 0) partial[tile * nnz + k] = sdc;
+    for (int s = 0; s < S; ++s) {
+      Batch cur = next;
+      if (s + 1 < S) next = load_batch(nz, kcur[s + 1], kend[s + 1]);
+      const int k1 = kend[s];
+      for (int kb = kcur[s]; kb < k1; kb += kBatch) {
+        if (kb != kcur[s]) cur = load_batch(nz, kb, k1);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (kb + u < k1) {
+            const int2 e = cur.e[u];
+            const float4 v0 = *reinterpret_cast<const float4*>(sb + e.x);
+            const float4 v1 = *reinterpret_cast<const float4*>(sb + e.x + 16);
+            const float cv = __int_as_float(e.y);
+            const float v[kTPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int q = 0; q < kTPL; ++q) acc[s][q] = fmaf(cv, v[q], acc[s][q]);
+            if constexpr (DC) {
+              float d = v[0] * zr[s][0];
+#pragma unroll
+              for (int q = 1; q < kTPL; ++q) d = fmaf(v[q], zr[s][q], d);
+              d = row16_total(d);
+              if (gl == 15) partial[tile * nnz + kb + u] = d;
+            }
+          }
         }
       }
+      kcur[s] = k1;
     }
   }
 
-  // epilogue: out[t][o0 .. o0+R) for the lane's two tokens
+  // epilogue: lane writes rows orow .. orow+S-1 (contiguous) of its 8 tokens
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t t = t0 + 2 * lane + q;
+  for (int q = 0; q < kTPL; ++q) {
+    const int64_t t = t0 + kTPL * gl + q;
     if (t >= T) continue;
     OutT* dst = out + t * n_out;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int o = o0 + r;
+    for (int s = 0; s < S; ++s) {
+      const int o = orow + s;
       if (o < n_out) {
-        float val = alpha * acc[r][q];
+        float val = alpha * acc[s][q];
         if (accumulate) val += Elem<OutT>::ld(dst, o);
         Elem<OutT>::st(dst, o, val);
       }
@@ -255,13 +328,14 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
   }
 }
 
-template <int R, typename SrcT, typename OutT, bool DC>
+template <int S, typename SrcT, typename OutT, bool DC>
 static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
                          const float* zsrc, float* partial, hipStream_t s) {
-  const int gy = (n_out + kWaves * R - 1) / (kWaves * R);
+  constexpr int rows_wg = kWaves * kGroups * S;
+  const int gy = (n_out + rows_wg - 1) / rows_wg;
   void* pp = const_cast<void*>(prep);
-  hipLaunchKernelGGL((spmm_kernel<R, SrcT, OutT, DC>), dim3(static_cast<unsigned>(pl.ntiles), gy),
+  hipLaunchKernelGGL((spmm_kernel<S, SrcT, OutT, DC>), dim3(static_cast<unsigned>(pl.ntiles), gy),
                      dim3(kThreads), 0, s, static_cast<const SrcT*>(src), T, n_src,
                      prep_packed(pp), prep_bptr(pp, nnz), nnz, n_out, pl.nblk, alpha,
                      static_cast<OutT*>(out), acc, zsrc, partial);
@@ -276,23 +350,23 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
   const bool dc = partial != nullptr;
   if (dc) {
     if (src_dt == Dt::F32 && out_dt == Dt::F32)
-      return spmm_t<kRdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+      return spmm_t<kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                               accumulate, zsrc, partial, s);
     if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-      return spmm_t<kRdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+      return spmm_t<kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                  accumulate, zsrc, partial, s);
     return hipErrorInvalidValue;
   }
   if (src_dt == Dt::F32 && out_dt == Dt::F32)
-    return spmm_t<kRfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_t<kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                               accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::F32 && out_dt == Dt::BF16)
-    return spmm_t<kRfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_t<kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                  accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-    return spmm_t<kRfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_t<kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                  accumulate, nullptr, nullptr, s);
-  return spmm_t<kRfwd, uint16_t, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+  return spmm_t<kSfwd, uint16_t, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                   accumulate, nullptr, nullptr, s);
 }
 

@@ -127,7 +127,8 @@ def test_init_select_ties_zero_rows_and_bounds(q):
     dwq[30, 0] = -0.25
     say("init ties/zero/cap")
     ref, got = init_both(q, dwq, 1500, 3)
-    assert ref["budgets"][20] == d_in and ref["budgets"][11] == 3
+    assert ref["budgets"][20] == d_in
+    assert abs(int(ref["budgets"][11]) - int(ref["budgets"][12])) <= 1
     assert_init_equal(ref, got)
 
 
@@ -187,7 +188,7 @@ def test_materialize_full_budget_reconstructs(q):
 # ------------------------------------------------------------------ fwd / bwd small
 def _small_case(d_out, d_in, p, T, act, seed):
     dwq = _edge_dwq(d_out, d_in, seed)
-    r = O.init_select(dwq, p, m=3)
+    r = O.init_select(dwq, p, m=min(3, d_in))
     rng = np.random.default_rng(seed + 1)
     x = rng.standard_normal((T, d_in)).astype(np.float32)
     dy = rng.standard_normal((T, d_out)).astype(np.float32)

@@ -145,12 +145,44 @@ def test_adaalloc_floor_binds():
     assert np.array_equal(b, [3, 3, 3, 3])
 
 
-def test_adaalloc_cap_binds_and_leftover_rounds():
+def test_adaalloc_cap_binds():
     # pass 1: floor(12*w/103) = (11, 0, 0, 0) -> rows 1..3 fixed at the floor 1
-    # pass 2: U = {0}, P = 9 > d_in = 4 -> row 0 fixed at the cap 4
-    # sum = 7, leftover 5 > 3 eligible rows: rounds (+1,+1,+1), then (+1,+1,0)
+    # pass 2: U = {0}, P = 9 > d_in = 4 -> row 0 capped at 4, rows 1..3 released
+    # pass 3: P = 8 over (1, 1, 1): floor(8/3) = 2 each; leftover 2 -> rows 1, 2
     b = O.adaalloc(np.array([100.0, 1.0, 1.0, 1.0]), 12, 4, m=1)
     assert np.array_equal(b, [4, 3, 3, 2])
+
+
+def test_adaalloc_cap_keeps_others_proportional():
+    # the capped row's excess is shared in proportion to the others' norms:
+    # after capping row 0 at 8, P = 12 over w = (1, 2, 3): (2, 4, 6) exactly
+    b = O.adaalloc(np.array([100.0, 1.0, 2.0, 3.0]), 20, 8, m=1)
+    assert np.array_equal(b, [8, 2, 4, 6])
+
+
+def test_adaalloc_is_clamped_proportional_split():
+    """Brute-force pin of the floor/cap reading: before rounding the budgets
+    are clamp(lambda s_i, m, d_in) with lambda solving sum = p (bisection)."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        d_out = int(rng.integers(2, 40))
+        d_in = int(2 ** rng.integers(2, 7))
+        m = int(rng.integers(0, 4))
+        m = min(m, d_in)
+        p = int(rng.integers(m * d_out, d_in * d_out + 1))
+        w = rng.lognormal(0, 2.5, size=d_out)
+        b = O.adaalloc(w, p, d_in, m=m)
+        lo, hi = 0.0, 1e30
+        for _ in range(400):
+            lam = 0.5 * (lo + hi)
+            if np.clip(lam * w, m, d_in).sum() < p:
+                lo = lam
+            else:
+                hi = lam
+        cont = np.clip(hi * w, m, d_in)
+        # rounding moves each budget by less than one unit from the split
+        assert np.all(np.abs(b - cont) < 1.0 + 1e-6), (b, cont)
+        assert b.sum() == p
 
 
 def test_adaalloc_zero_norms_split_evenly():
