@@ -109,7 +109,7 @@ struct FwdWs {
 };
 FwdWs fwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
   FwdWs l;
-  l.plan = spmm_plan(T, d_in, d_out);
+  l.plan = spmm_plan(T, d_in, d_out, p, false);
   l.z = 0;
   l.prep = align256(static_cast<size_t>(T) * d_in * 4);
   l.total = l.prep + align256(spmm_prep_bytes(p, d_out, l.plan));
@@ -122,7 +122,7 @@ struct BwdWs {
 };
 BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
   BwdWs l;
-  l.plan = spmm_plan(T, d_out, d_in);
+  l.plan = spmm_plan(T, d_out, d_in, p, true);
   const size_t zb = align256(static_cast<size_t>(T) * d_in * 4);
   l.z = 0;
   l.dz = zb;
@@ -356,8 +356,9 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
   if (dc)
     QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_DC_REDUCE, stream,
                              [&] {
-                               return launch_dc_reduce(partial, l.plan.ntiles, p, csc_perm, alpha,
-                                                       dc, stream);
+                               return launch_dc_reduce(partial, l.plan.ntiles, p,
+                                                       spmm_prep_korig(prep, p, d_in, l.plan),
+                                                       alpha, dc, stream);
                              }),
                        "dc reduce"));
   return QWHA_OK;

@@ -40,28 +40,30 @@ struct SpmmPlan {
   int nblk;      // source blocks
   int64_t ntiles;
 };
-SpmmPlan spmm_plan(int64_t T, int n_src, int n_out);
+SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc);
 size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl);
+// index k in E of each entry of the prepared stream (stream order)
+const int32_t* spmm_prep_korig(const void* prep, int64_t nnz, int n_out, const SpmmPlan& pl);
 
-// CSR (forward): packed (LDS byte offset, value) per nonzero and per-(row, block)
-// segment starts, from row_ptr / E / c.
+// Rows of F (forward): the column-block-major stream of (LDS byte offset of
+// the column within its block, value) from row_ptr / E / c.
 hipError_t launch_prep_csr(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                            int64_t nnz, const SpmmPlan& pl, void* prep, hipStream_t s);
-// CSC (backward): same from col_ptr / csc_perm / E / c, keyed by rows i.
+// Columns of F (backward): the same from col_ptr / csc_perm / E / c.
 hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* csc_perm, const int32_t* E,
                            const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
                            hipStream_t s);
 
 // out[t][o] (+)= alpha * sum_k val_k * src[t][col_k]; with zsrc, also
-// partial[tile][k] = sum_{t in tile} src[t][col_k] * zsrc[t][o].
+// partial[tile][q] = sum_{t in tile} src[t][col_q] * zsrc[t][o] per stream entry q.
 hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const void* prep,
                        int64_t nnz, int n_out, const SpmmPlan& pl, float alpha, void* out,
                        Dt out_dt, int accumulate, const float* zsrc, float* partial,
                        hipStream_t s);
 
-// dc[perm[q]] = alpha * sum_tile partial[tile][q]   (fixed tile order)
+// dc[korig[q]] = alpha * sum_tile partial[tile][q]   (fixed tile order)
 hipError_t launch_dc_reduce(const float* partial, int64_t ntiles, int64_t nnz,
-                            const int32_t* csc_perm, float alpha, float* dc, hipStream_t s);
+                            const int32_t* korig, float alpha, float* dc, hipStream_t s);
 
 hipError_t launch_sign_update(float* c, const float* dc, int64_t p, float step, hipStream_t s);
 

@@ -2,81 +2,126 @@
 //
 // With dW = alpha F H / n (QWHA notes, papernotes.org, 方法详解 › 整体框架) and
 // z = x H / n (H symmetric), the adapter branch is
-//   forward   y  = x dW^T  = alpha * z F^T            (gather-SpMM, CSR)
-//   backward  dx = dy dW   = alpha * FWHT(dy F) / n   (gather-SpMM, CSC)
+//   forward   y  = x dW^T  = alpha * z F^T            (gather-SpMM over rows of F)
+//   backward  dx = dy dW   = alpha * FWHT(dy F) / n   (gather-SpMM over columns of F)
 //             dc_k = alpha * sum_t dy[t, i_k] z[t, j_k] (sampled dense-dense
 //                    product at E: only c is trainable, W_Q and H frozen,
 //                    papernotes.org, 损失函数 / 训练策略).
 //
-// Kernel shape (gfx950, wave64): one workgroup = 8 waves = a tile of TT = 128
-// tokens x (8 * 64) output rows (8 * 32 with dc partials); every output row's
-// accumulators for the tile's tokens live in registers. The source matrix (z
-// for the forward, dy for the backward) is staged through LDS in blocks of
-// JB = 128 source columns, token-minor, double buffered: the next block's
-// global loads are in flight while the current block is consumed. The
-// nonzeros of every (output row, source block) pair are contiguous in a
-// packed stream (LDS byte offset of the column, value) prepared per call.
+// One kernel serves both directions: out[t][o] = alpha * sum over the
+// nonzeros (o, col, val) of segment o of val * src[t][col], where the
+// segments are the rows of F (forward; src = z) or its columns (backward;
+// src = dy), optionally with the dc partials.
+//
+// Work decomposition (gfx950, wave64). A workgroup owns a tile of TT = 128
+// tokens and 8 * 4 * S output rows. The source is staged through LDS in
+// blocks of JB columns, token-minor (row jj of the staged block holds the
+// 128 tokens of source column jj), double buffered. Each wave is four groups
+// of 16 lanes; a group owns S consecutive output rows and lane gl of a group
+// owns tokens 4gl..4gl+3 and 64+4gl..64+4gl+3, so the group covers the tile and every
+// output row's accumulators for the tile live in registers. A nonzero costs
+// the group's lanes two conflict-free ds_read_b128 (512 contiguous bytes)
+// and eight FMAs each.
+//
+// The nonzeros are re-laid out per call "column-block major": for block b,
+// the segments of all output rows in row order. A group's row segment for a
+// block is then one coalesced 16-entry load (lane gl holds entry gl) and each
+// entry reaches all 16 lanes through a DPP row broadcast. All of a block's
+// entry loads are issued before the next block's staging loads, so waiting
+// for an entry never waits for the staging traffic (vector memory counters
+// drain in issue order).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace qwha {
 
-constexpr int kTT = 128;          // tokens per tile
-constexpr int kJB = 128;          // source columns per staged block
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kSfwd = 12;         // rows per 16-lane group, plain SpMM (48 per wave)
-constexpr int kSdc = 8;           // rows per group when dc partials are also produced
-
-SpmmPlan spmm_plan_impl(int64_t T, int n_src, int n_out, bool dc) {
-  SpmmPlan pl;
-  pl.tt = kTT;
-  pl.jb = kJB;
-  pl.rows_wg = kWaves * 4 * (dc ? kSdc : kSfwd);
-  pl.nblk = (n_src + kJB - 1) / kJB;
-  pl.ntiles = (T + kTT - 1) / kTT;
-  (void)n_out;
-  return pl;
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
 }
 
-SpmmPlan spmm_plan(int64_t T, int n_src, int n_out) { return spmm_plan_impl(T, n_src, n_out, false); }
+constexpr int kTT = 128;          // tokens per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kGroups = 4;        // 16-lane groups per wave
+constexpr int kTPL = 8;           // tokens per lane
+constexpr int kSfwd = 12;         // rows per group, plain SpMM
+constexpr int kSdc = 8;           // rows per group with dc partials
+constexpr int kChunk = 16;        // entries per group load
+constexpr int kPad = 16;          // padding entries after the stream
+constexpr int kHalfTile = kTT * 2;  // bytes of 64 fp32 tokens
+
+// Token (within the tile) held in accumulator q of lane gl of a group: lanes
+// take 4 consecutive tokens in each half of the tile, so a wave's
+// ds_read_b128 touches consecutive 16-byte chunks (no bank conflicts).
+__device__ __forceinline__ int lane_token(int gl, int q) {
+  return (q < 4) ? 4 * gl + q : kTT / 2 + 4 * gl + (q - 4);
+}
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl) {
-  return align256(static_cast<size_t>(nnz) * 8) +
-         align256(static_cast<size_t>(n_out) * (pl.nblk + 1) * 4);
+SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
+  SpmmPlan pl;
+  pl.tt = kTT;
+  // Column block: 128 unless a (row, block) segment would average more than
+  // six entries; longer segments need extra 16-entry rounds.
+  const double per_row = n_out > 0 ? static_cast<double>(nnz) / n_out : 0.0;
+  int jb = 128;
+  if (n_src > 0 && per_row * 128.0 / n_src > 6.0) jb = 64;
+  pl.jb = jb;
+  pl.rows_wg = kWaves * kGroups * (dc ? kSdc : kSfwd);
+  pl.nblk = (n_src + jb - 1) / jb;
+  pl.ntiles = (T + kTT - 1) / kTT;
+  return pl;
 }
 
-static int2* prep_packed(void* prep) { return static_cast<int2*>(prep); }
-static int32_t* prep_bptr(void* prep, int64_t nnz) {
-  return reinterpret_cast<int32_t*>(static_cast<char*>(prep) + align256(static_cast<size_t>(nnz) * 8));
+// prep layout: [stream int2 x (nnz+pad)] [korig int32 x nnz]
+//              [bptr int32 x n_out*(nblk+1)] [ptr int32 x nblk*(n_out+1)] [base int32 x nblk+1]
+struct PrepLayout {
+  size_t stream, korig, bptr, ptr, base, total;
+};
+static PrepLayout prep_layout(int64_t nnz, int n_out, const SpmmPlan& pl) {
+  PrepLayout l;
+  l.stream = 0;
+  l.korig = align256(static_cast<size_t>(nnz + kPad) * 8);
+  l.bptr = l.korig + align256(static_cast<size_t>(nnz) * 4);
+  l.ptr = l.bptr + align256(static_cast<size_t>(n_out) * (pl.nblk + 1) * 4);
+  l.base = l.ptr + align256(static_cast<size_t>(pl.nblk) * (n_out + 1) * 4);
+  l.total = l.base + align256(static_cast<size_t>(pl.nblk + 1) * 4);
+  return l;
+}
+
+size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl) {
+  return prep_layout(nnz, n_out, pl).total;
+}
+
+const int32_t* spmm_prep_korig(const void* prep, int64_t nnz, int n_out, const SpmmPlan& pl) {
+  return reinterpret_cast<const int32_t*>(static_cast<const char*>(prep) +
+                                          prep_layout(nnz, n_out, pl).korig);
+}
+
+template <typename T>
+static T* at(void* prep, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(prep) + off);
 }
 
 // ------------------------------------------------------------ prep
-__global__ void pack_csr_kernel(const int32_t* __restrict__ E, const float* __restrict__ c,
-                                int64_t nnz, int2* __restrict__ packed) {
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (k >= nnz) return;
-  const int col = E[2 * k + 1];
-  const int jj = col % kJB;
-  packed[k] = make_int2(jj * kTT * 4, __float_as_int(c[k]));
+// Segment o of the source structure: positions [seg_ptr[o], seg_ptr[o+1]);
+// the source column of position q is E[2q+1] (rows of F) or E[2 perm[q]]
+// (columns of F, perm = csc_perm); columns ascend within a segment.
+__device__ __forceinline__ int seg_key(const int32_t* E, const int32_t* perm, int64_t q) {
+  return perm ? E[2 * static_cast<int64_t>(perm[q])] : E[2 * q + 1];
 }
 
-__global__ void pack_csc_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ E,
-                                const float* __restrict__ c, int64_t nnz, int2* __restrict__ packed) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (q >= nnz) return;
-  const int k = perm[q];
-  const int row = E[2 * static_cast<int64_t>(k)];
-  const int ii = row % kJB;
-  packed[q] = make_int2(ii * kTT * 4, __float_as_int(c[k]));
-}
-
-// bptr[o][b] = first position in segment o whose source column is >= b*JB.
-// key(pos) = E[2*pos + 1] (CSR) or E[2*perm[pos]] (CSC).
+// bptr[o][b] = first position of segment o whose column is >= b*JB
 __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ E,
-                            const int32_t* __restrict__ perm, int n_out, int nblk,
+                            const int32_t* __restrict__ perm, int n_out, int nblk, int jb,
                             int32_t* __restrict__ bptr) {
   const int64_t id = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(n_out) * (nblk + 1);
@@ -84,69 +129,172 @@ __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* 
   const int o = static_cast<int>(id / (nblk + 1));
   const int b = static_cast<int>(id % (nblk + 1));
   int lo = seg_ptr[o], hi = seg_ptr[o + 1];
-  const int target = b * kJB;
+  const int target = b * jb;
   while (lo < hi) {
     const int mid = lo + ((hi - lo) >> 1);
-    const int key = perm ? E[2 * static_cast<int64_t>(perm[mid])] : E[2 * static_cast<int64_t>(mid) + 1];
-    if (key < target) lo = mid + 1; else hi = mid;
+    if (seg_key(E, perm, mid) < target) lo = mid + 1; else hi = mid;
   }
   bptr[id] = lo;
 }
 
+// Per block b: ptr[b][o] = entries of block b in rows before o (exclusive
+// scan over rows), ptr[b][n_out] and base[b] = the block's total.
+__global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restrict__ bptr,
+                                                        int n_out, int nblk,
+                                                        int32_t* __restrict__ ptr,
+                                                        int32_t* __restrict__ base) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  int32_t* pb = ptr + static_cast<int64_t>(b) * (n_out + 1);
+  for (int o0 = 0; o0 < n_out; o0 += 1024) {
+    const int o = o0 + threadIdx.x;
+    int cnt = 0;
+    if (o < n_out) {
+      const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
+      cnt = bptr[r + 1] - bptr[r];
+    }
+    const int incl = wave_incl_scan_i32(cnt);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int v = wsum[i];
+      if (i < wid) before += v;
+      all += v;
+    }
+    if (o < n_out) pb[o] = carry + before + incl - cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += all;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    pb[n_out] = carry;
+    base[b] = carry;
+  }
+}
+
+// base[b] <- exclusive scan of the block totals (base[nblk] = nnz)
+__global__ __launch_bounds__(1024) void blk_base_kernel(int32_t* __restrict__ base, int nblk) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < nblk; b0 += 1024) {
+    const int b = b0 + threadIdx.x;
+    const int v = (b < nblk) ? base[b] : 0;
+    const int incl = wave_incl_scan_i32(v);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int x = wsum[i];
+      if (i < wid) before += x;
+      all += x;
+    }
+    __syncthreads();
+    if (b < nblk) base[b] = carry + before + incl - v;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += all;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) base[nblk] = carry;
+}
+
+// Scatter every nonzero into the column-block-major stream.
+// Rows of F: position q = k, row o = E[2k], column E[2k+1], value c[k].
+// Columns of F: position q, row o = E[2 perm[q] + 1] (a column of F),
+// column E[2 perm[q]] (a row of F), value c[perm[q]].
+// korig[pos] keeps the nonzero's index k in E.
+__global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __restrict__ c,
+                               const int32_t* __restrict__ perm, int64_t nnz, int n_out, int nblk,
+                               int jb, const int32_t* __restrict__ bptr,
+                               const int32_t* __restrict__ ptr, const int32_t* __restrict__ base,
+                               int2* __restrict__ stream, int32_t* __restrict__ korig) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= nnz) {
+    if (q < nnz + kPad) stream[q] = make_int2(0, 0);
+    return;
+  }
+  const int64_t k = perm ? perm[q] : q;
+  const int o = perm ? E[2 * k + 1] : E[2 * k];
+  const int col = perm ? E[2 * k] : E[2 * k + 1];
+  const int b = col / jb;
+  const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
+  const int64_t pos = static_cast<int64_t>(base[b]) +
+                      ptr[static_cast<int64_t>(b) * (n_out + 1) + o] + (q - bptr[r]);
+  stream[pos] = make_int2((col - b * jb) * kTT * 4, __float_as_int(c[k]));
+  korig[pos] = static_cast<int32_t>(k);
+}
+
+static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const float* c,
+                              const int32_t* perm, int n_out, int64_t nnz, const SpmmPlan& pl,
+                              void* prep, hipStream_t s) {
+  const PrepLayout l = prep_layout(nnz, n_out, pl);
+  int32_t* bptr = at<int32_t>(prep, l.bptr);
+  int32_t* ptr = at<int32_t>(prep, l.ptr);
+  int32_t* base = at<int32_t>(prep, l.base);
+  const int64_t nb = static_cast<int64_t>(n_out) * (pl.nblk + 1);
+  hipLaunchKernelGGL(bptr_kernel, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256), 0, s,
+                     seg_ptr, E, perm, n_out, pl.nblk, pl.jb, bptr);
+  hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out, pl.nblk, ptr,
+                     base);
+  hipLaunchKernelGGL(blk_base_kernel, dim3(1), dim3(1024), 0, s, base, pl.nblk);
+  const int64_t ns = nnz + kPad;
+  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((ns + 255) / 256)), dim3(256), 0, s,
+                     E, c, perm, nnz, n_out, pl.nblk, pl.jb, bptr, ptr, base,
+                     at<int2>(prep, l.stream), at<int32_t>(prep, l.korig));
+  return hipGetLastError();
+}
+
 hipError_t launch_prep_csr(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                            int64_t nnz, const SpmmPlan& pl, void* prep, hipStream_t s) {
-  if (nnz > 0)
-    hipLaunchKernelGGL(pack_csr_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0,
-                       s, E, c, nnz, prep_packed(prep));
-  const int64_t total = static_cast<int64_t>(d_out) * (pl.nblk + 1);
-  hipLaunchKernelGGL(bptr_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
-                     row_ptr, E, nullptr, d_out, pl.nblk, prep_bptr(prep, nnz));
-  return hipGetLastError();
+  return prep_common(row_ptr, E, c, nullptr, d_out, nnz, pl, prep, s);
 }
 
 hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* perm, const int32_t* E,
                            const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
                            hipStream_t s) {
-  if (nnz > 0)
-    hipLaunchKernelGGL(pack_csc_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0,
-                       s, perm, E, c, nnz, prep_packed(prep));
-  const int64_t total = static_cast<int64_t>(d_in) * (pl.nblk + 1);
-  hipLaunchKernelGGL(bptr_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
-                     col_ptr, E, perm, d_in, pl.nblk, prep_bptr(prep, nnz));
-  return hipGetLastError();
+  return prep_common(col_ptr, E, c, perm, d_in, nnz, pl, prep, s);
 }
 
 // ------------------------------------------------------------ staging
-template <typename SrcT>
+// Thread -> token tt = tid % 128, column group g = tid / 128 (0..3); load q
+// covers local columns (q*4 + g)*VEC .. +VEC-1 of the block. Loads are
+// unconditional (addresses clamped into the source) so the compiler can
+// count them; out-of-range elements are zeroed when stored to LDS.
+template <typename SrcT, int JB, bool VEC_OK>
 struct Stage {
-  static constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));   // elements per 16-byte load
-  static constexpr int NL = kJB / (4 * VEC);                         // loads per thread per block
+  static constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));   // elements per 16 bytes
+  static constexpr int NL = JB / (4 * VEC);                          // 16-byte loads per thread
   uint4 raw[NL];
 
-  // thread -> token tt = tid % 128, column group g = tid / 128 (0..3);
-  // load q covers local columns (q*4 + g)*VEC .. +VEC-1.
   __device__ __forceinline__ void load(const SrcT* __restrict__ src, int64_t T, int n_src,
-                                       int64_t t0, int b, bool vec_ok) {
+                                       int64_t t0, int b) {
     const int tt = threadIdx.x & (kTT - 1);
     const int g = threadIdx.x >> 7;
-    const int64_t t = t0 + tt;
+    const int64_t t = t0 + tt < T ? t0 + tt : T - 1;
+    const SrcT* row = src + t * n_src;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const int col = b * kJB + (q * 4 + g) * VEC;
-      if (t < T && vec_ok && col + VEC <= n_src) {
-        raw[q] = *reinterpret_cast<const uint4*>(src + t * n_src + col);
+      const int col = b * JB + (q * 4 + g) * VEC;
+      if constexpr (VEC_OK) {
+        const int cc = col + VEC <= n_src ? col : n_src - VEC;
+        raw[q] = *reinterpret_cast<const uint4*>(row + cc);
       } else {
         uint32_t w[4] = {0, 0, 0, 0};
-        if (t < T) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            if (col + e < n_src) {
-              uint32_t bits;
-              if constexpr (sizeof(SrcT) == 4) bits = __float_as_uint(static_cast<float>(src[t * n_src + col + e]));
-              else bits = static_cast<uint32_t>(src[t * n_src + col + e]);
-              if constexpr (sizeof(SrcT) == 4) w[e] = bits;
-              else w[e >> 1] |= bits << (16 * (e & 1));
-            }
+        for (int e = 0; e < VEC; ++e) {
+          const int cc = col + e < n_src ? col + e : n_src - 1;
+          if constexpr (sizeof(SrcT) == 4) {
+            w[e] = __float_as_uint(reinterpret_cast<const float*>(row)[cc]);
+          } else {
+            const uint32_t bits = reinterpret_cast<const uint16_t*>(row)[cc];
+            w[e >> 1] |= bits << (16 * (e & 1));
           }
         }
         raw[q] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -154,173 +302,192 @@ struct Stage {
     }
   }
 
-  __device__ __forceinline__ void store(float* __restrict__ st) const {
+  __device__ __forceinline__ void store(float* __restrict__ st, int64_t T, int n_src, int64_t t0,
+                                        int b) const {
     const int tt = threadIdx.x & (kTT - 1);
     const int g = threadIdx.x >> 7;
+    const bool tok_ok = t0 + tt < T;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
       const int cl = (q * 4 + g) * VEC;
+      const int col = b * JB + cl;
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float f;
         if constexpr (sizeof(SrcT) == 4) f = __uint_as_float(w[e]);
         else f = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
-        st[(cl + e) * kTT + tt] = f;
+        // with VEC_OK a clamped load means the whole group is past the end
+        const bool ok = tok_ok && (VEC_OK ? (col + VEC <= n_src) : (col + e < n_src));
+        st[(cl + e) * kTT + tt] = ok ? f : 0.f;
       }
     }
   }
 };
 
-// ------------------------------------------------------------ main kernel
-// Wave layout: 4 groups of 16 lanes. Group g owns the rows o0 + g*S + s
-// (s < S); lane gl of the group owns tokens t0 + 8*gl .. +7 of the tile, so
-// the 16 lanes of a group cover all 128 tokens. A nonzero of the group's
-// current row is read by the group's 16 lanes as two ds_read_b128 each (512
-// contiguous bytes of the staged block: conflict-free) and costs 8 FMAs per
-// lane. Nonzeros are fetched per lane with vector loads, a batch of 4 at a
-// time, and the first batch of the next row is in flight while the current
-// row is processed. With zsrc (backward), each nonzero also yields
-// sum_{t in lane} src[t][col] * zsrc[t][o], reduced over the group's 16 lanes
-// with four DPP row shifts into lane 15, which stores the tile's partial.
-constexpr int kGroups = 4;
-constexpr int kTPL = 8;          // tokens per lane
-constexpr int kBatch = 4;        // nonzeros fetched per vector load batch
-
-__device__ __forceinline__ float dpp_row_shr(float v, int n) {
-  int r;
-  switch (n) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true); break;
-    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true); break;
-  }
-  return __int_as_float(r);
+// ------------------------------------------------------------ helpers
+template <int U>
+__device__ __forceinline__ int row_bcast(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + U, 0xF, 0xF, false);  // row_newbcast:U
 }
 
-// Inclusive prefix over each row of 16 lanes: lane 15 of a row ends with the
-// row's total.
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
+}
+
+// inclusive prefix over each 16-lane row: lane 15 ends with the row total
 __device__ __forceinline__ float row16_total(float v) {
-  v += dpp_row_shr(v, 1);
-  v += dpp_row_shr(v, 2);
-  v += dpp_row_shr(v, 4);
-  v += dpp_row_shr(v, 8);
+  v += dpp_row_shr<1>(v);
+  v += dpp_row_shr<2>(v);
+  v += dpp_row_shr<4>(v);
+  v += dpp_row_shr<8>(v);
   return v;
 }
 
-struct Batch {
-  int2 e[kBatch];
+template <int S, bool DC>
+struct Acc {
+  float a[S][kTPL];
+  float z[DC ? S : 1][kTPL];
 };
 
-__device__ __forceinline__ Batch load_batch(const int2* __restrict__ nz, int k, int k1) {
-  Batch b;
+// Entries u in [U0, U0+4) of a 16-entry chunk (lane gl of the group holds
+// entry gl); groups with fewer than u+1 entries are masked off.
+template <int U0, int S, bool DC>
+__device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int cnt,
+                                     const char* sb, float* __restrict__ prow, int gl) {
+  float4 v[4][2];
+  int off[4];
+  off[0] = row_bcast<U0 + 0>(ent.x);
+  off[1] = row_bcast<U0 + 1>(ent.x);
+  off[2] = row_bcast<U0 + 2>(ent.x);
+  off[3] = row_bcast<U0 + 3>(ent.x);
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) b.e[u] = (k + u < k1) ? nz[k + u] : make_int2(0, 0);
-  return b;
+  for (int u = 0; u < 4; ++u) {
+    if (U0 + u < cnt) {
+      v[u][0] = *reinterpret_cast<const float4*>(sb + off[u]);
+      v[u][1] = *reinterpret_cast<const float4*>(sb + off[u] + kHalfTile);
+    }
+  }
+  float cv[4];
+  cv[0] = __int_as_float(row_bcast<U0 + 0>(ent.y));
+  cv[1] = __int_as_float(row_bcast<U0 + 1>(ent.y));
+  cv[2] = __int_as_float(row_bcast<U0 + 2>(ent.y));
+  cv[3] = __int_as_float(row_bcast<U0 + 3>(ent.y));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (U0 + u < cnt) {
+      const float x[kTPL] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                             v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+      for (int q = 0; q < kTPL; ++q) A.a[s][q] = fmaf(cv[u], x[q], A.a[s][q]);
+      if constexpr (DC) {
+        float d = x[0] * A.z[s][0];
+#pragma unroll
+        for (int q = 1; q < kTPL; ++q) d = fmaf(x[q], A.z[s][q], d);
+        d = row16_total(d);
+        if (gl == 15) prow[U0 + u] = d;
+      }
+    }
+  }
 }
 
-template <int S, typename SrcT, typename OutT, bool DC>
+// One 16-entry chunk of slot s with cnt valid entries (cnt may be <= 0).
+template <int S, bool DC>
+__device__ __forceinline__ void chunk16(Acc<S, DC>& A, int s, const int2& ent, int cnt,
+                                        const char* sb, float* __restrict__ prow, int gl) {
+  if (cnt > 0) quad<0>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 4) quad<4>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 8) quad<8>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 12) quad<12>(A, s, ent, cnt, sb, prow, gl);
+}
+
+// ------------------------------------------------------------ main kernel
+template <int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
 __global__ __launch_bounds__(kThreads) void spmm_kernel(
-    const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ nz,
-    const int32_t* __restrict__ bptr, int64_t nnz, int n_out, int nblk, float alpha,
-    OutT* __restrict__ out, int accumulate, const float* __restrict__ zsrc,
-    float* __restrict__ partial) {
-  __shared__ float stage[2][kJB * kTT];
+    const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
+    int nblk, float alpha, OutT* __restrict__ out, int accumulate,
+    const float* __restrict__ zsrc, float* __restrict__ partial) {
+  __shared__ float stage[2][JB * kTT];
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
   const int gl = lane & 15;
+  const int g = lane >> 4;
   const int w = uniform(threadIdx.x >> 6);
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTT;
   const int rows_wg = kWaves * kGroups * S;
-  const int orow = static_cast<int>(blockIdx.y) * rows_wg + w * (kGroups * S) + g * S;
-  const bool vec_ok = (n_src % Stage<SrcT>::VEC) == 0;
-  const int lds_lane = gl * (kTPL * 4);      // byte offset of the lane's 8 tokens
+  const int orow = static_cast<int>(blockIdx.y) * rows_wg + (w * kGroups + g) * S;
+  const int lds_lane = gl * 16;      // lane's first 4 tokens; the other 4 are kHalfTile later
 
-  float acc[S][kTPL];
+  Acc<S, DC> A;
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int q = 0; q < kTPL; ++q) acc[s][q] = 0.f;
-
-  float zr[DC ? S : 1][kTPL];
+    for (int q = 0; q < kTPL; ++q) A.a[s][q] = 0.f;
   if constexpr (DC) {
 #pragma unroll
     for (int q = 0; q < kTPL; ++q) {
-      const int64_t t = t0 + kTPL * gl + q;
+      const int64_t t = t0 + lane_token(gl, q);
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int o = orow + s;
-        zr[s][q] = (t < T && o < n_out) ? zsrc[t * n_out + o] : 0.f;
+        A.z[s][q] = (t < T && o < n_out) ? zsrc[t * n_out + o] : 0.f;
       }
     }
   }
 
-  // per-slot cursor into the packed stream: start of the current block
-  int kcur[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int o = orow + s;
-    kcur[s] = (o < n_out) ? bptr[static_cast<int64_t>(o) * (nblk + 1)] : 0;
-  }
+  // Lane gl (<= S) of a group holds the stream start of row orow + gl in
+  // the current block; rows past n_out read the block's end (empty segments).
+  const int rsel = orow + (gl <= S ? gl : S);
+  const int prow_idx = rsel < n_out ? rsel : n_out;
+  int pv = ptr[prow_idx] + base[0];
 
-  Stage<SrcT> pf;
-  pf.load(src, T, n_src, t0, 0, vec_ok);
+  Stage<SrcT, JB, VEC_OK> pf;
+  pf.load(src, T, n_src, t0, 0);
   for (int b = 0; b < nblk; ++b) {
     float* st = stage[b & 1];
-    pf.store(st);
+    pf.store(st, T, n_src, t0, b);
     __syncthreads();
-    if (b + 1 < nblk) pf.load(src, T, n_src, t0, b + 1, vec_ok);
-    int kend[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int o = orow + s;
-      kend[s] = (o < n_out) ? bptr[static_cast<int64_t>(o) * (nblk + 1) + b + 1] : 0;
-    }
+    // this block's segments: slot s spans [lane s's pv, lane s+1's pv)
+    int k0[S], cnt[S];
+    int2 ent[S];
+    static_for<0, S>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      k0[s] = row_bcast<s>(pv);
+      cnt[s] = row_bcast<s + 1>(pv) - k0[s];
+      ent[s] = stream[k0[s] + gl];
+    });
+    // next block's segment starts, then the next block's staging loads
+    // (issued after every entry load of this block)
+    const int bn = b + 1 < nblk ? b + 1 : b;
+    pv = ptr[static_cast<int64_t>(bn) * (n_out + 1) + prow_idx] + base[bn];
+    pf.load(src, T, n_src, t0, bn);
+
     const char* sb = reinterpret_cast<const char*>(st) + lds_lane;
-    Batch next = load_batch(nz, kcur[0], kend[0]);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      Batch cur = next;
-      if (s + 1 < S) next = load_batch(nz, kcur[s + 1], kend[s + 1]);
-      const int k1 = kend[s];
-      for (int kb = kcur[s]; kb < k1; kb += kBatch) {
-        if (kb != kcur[s]) cur = load_batch(nz, kb, k1);
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (kb + u < k1) {
-            const int2 e = cur.e[u];
-            const float4 v0 = *reinterpret_cast<const float4*>(sb + e.x);
-            const float4 v1 = *reinterpret_cast<const float4*>(sb + e.x + 16);
-            const float cv = __int_as_float(e.y);
-            const float v[kTPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int q = 0; q < kTPL; ++q) acc[s][q] = fmaf(cv, v[q], acc[s][q]);
-            if constexpr (DC) {
-              float d = v[0] * zr[s][0];
-#pragma unroll
-              for (int q = 1; q < kTPL; ++q) d = fmaf(v[q], zr[s][q], d);
-              d = row16_total(d);
-              if (gl == 15) partial[tile * nnz + kb + u] = d;
-            }
-          }
-        }
+    static_for<0, S>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      float* prow = DC ? partial + tile * nnz + k0[s] : nullptr;
+      chunk16<S, DC>(A, s, ent[s], cnt[s], sb, prow, gl);
+      // segments longer than one chunk: further 16-entry rounds
+      for (int kk = kChunk; kk < cnt[s]; kk += kChunk) {
+        const int2 e2 = stream[k0[s] + kk + gl];
+        chunk16<S, DC>(A, s, e2, cnt[s] - kk, sb, DC ? prow + kk : nullptr, gl);
       }
-      kcur[s] = k1;
-    }
+    });
   }
 
   // epilogue: lane writes rows orow .. orow+S-1 (contiguous) of its 8 tokens
 #pragma unroll
   for (int q = 0; q < kTPL; ++q) {
-    const int64_t t = t0 + kTPL * gl + q;
+    const int64_t t = t0 + lane_token(gl, q);
     if (t >= T) continue;
     OutT* dst = out + t * n_out;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int o = orow + s;
       if (o < n_out) {
-        float val = alpha * acc[s][q];
+        float val = alpha * A.a[s][q];
         if (accumulate) val += Elem<OutT>::ld(dst, o);
         Elem<OutT>::st(dst, o, val);
       }
@@ -328,18 +495,38 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
   }
 }
 
-template <int S, typename SrcT, typename OutT, bool DC>
+template <int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
 static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
                          const float* zsrc, float* partial, hipStream_t s) {
   constexpr int rows_wg = kWaves * kGroups * S;
   const int gy = (n_out + rows_wg - 1) / rows_wg;
   void* pp = const_cast<void*>(prep);
-  hipLaunchKernelGGL((spmm_kernel<S, SrcT, OutT, DC>), dim3(static_cast<unsigned>(pl.ntiles), gy),
-                     dim3(kThreads), 0, s, static_cast<const SrcT*>(src), T, n_src,
-                     prep_packed(pp), prep_bptr(pp, nnz), nnz, n_out, pl.nblk, alpha,
+  const PrepLayout l = prep_layout(nnz, n_out, pl);
+  hipLaunchKernelGGL((spmm_kernel<S, JB, VEC_OK, SrcT, OutT, DC>),
+                     dim3(static_cast<unsigned>(pl.ntiles), gy), dim3(kThreads), 0, s,
+                     static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
+                     at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out, pl.nblk, alpha,
                      static_cast<OutT*>(out), acc, zsrc, partial);
   return hipGetLastError();
+}
+
+template <int S, typename SrcT, typename OutT, bool DC>
+static hipError_t spmm_jb(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
+                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
+                          const float* zsrc, float* partial, hipStream_t s) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
+  const bool vec_ok = n_src % VEC == 0 && n_src >= VEC;
+  if (pl.jb == 128) {
+    return vec_ok ? spmm_t<S, 128, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+                                                         out, acc, zsrc, partial, s)
+                  : spmm_t<S, 128, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl,
+                                                          alpha, out, acc, zsrc, partial, s);
+  }
+  return vec_ok ? spmm_t<S, 64, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+                                                      out, acc, zsrc, partial, s)
+                : spmm_t<S, 64, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+                                                       out, acc, zsrc, partial, s);
 }
 
 hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const void* prep,
@@ -347,45 +534,43 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
                        Dt out_dt, int accumulate, const float* zsrc, float* partial,
                        hipStream_t s) {
   if (pl.ntiles == 0) return hipSuccess;
-  const bool dc = partial != nullptr;
-  if (dc) {
-    if (src_dt == Dt::F32 && out_dt == Dt::F32)
-      return spmm_t<kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                              accumulate, zsrc, partial, s);
-    if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-      return spmm_t<kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                 accumulate, zsrc, partial, s);
-    return hipErrorInvalidValue;
+  if (partial != nullptr) {
+    if (out_dt != Dt::F32) return hipErrorInvalidValue;
+    return src_dt == Dt::F32
+               ? spmm_jb<kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+                                                   accumulate, zsrc, partial, s)
+               : spmm_jb<kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+                                                      out, accumulate, zsrc, partial, s);
   }
   if (src_dt == Dt::F32 && out_dt == Dt::F32)
-    return spmm_t<kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                              accumulate, nullptr, nullptr, s);
+    return spmm_jb<kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+                                               accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::F32 && out_dt == Dt::BF16)
-    return spmm_t<kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                 accumulate, nullptr, nullptr, s);
-  if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-    return spmm_t<kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                 accumulate, nullptr, nullptr, s);
-  return spmm_t<kSfwd, uint16_t, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_jb<kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                   accumulate, nullptr, nullptr, s);
+  if (src_dt == Dt::BF16 && out_dt == Dt::F32)
+    return spmm_jb<kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+                                                  accumulate, nullptr, nullptr, s);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------ dc reduction
+// dc[korig[q]] = alpha * sum over tiles of partial[tile][q], tiles in order
 __global__ void dc_reduce_kernel(const float* __restrict__ partial, int64_t ntiles, int64_t nnz,
-                                 const int32_t* __restrict__ perm, float alpha,
+                                 const int32_t* __restrict__ korig, float alpha,
                                  float* __restrict__ dc) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= nnz) return;
   float s = 0.f;
   for (int64_t t = 0; t < ntiles; ++t) s += partial[t * nnz + q];
-  dc[perm[q]] = alpha * s;
+  dc[korig[q]] = alpha * s;
 }
 
 hipError_t launch_dc_reduce(const float* partial, int64_t ntiles, int64_t nnz,
-                            const int32_t* csc_perm, float alpha, float* dc, hipStream_t s) {
+                            const int32_t* korig, float alpha, float* dc, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
   hipLaunchKernelGGL(dc_reduce_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0,
-                     s, partial, ntiles, nnz, csc_perm, alpha, dc);
+                     s, partial, ntiles, nnz, korig, alpha, dc);
   return hipGetLastError();
 }
 
