@@ -39,6 +39,7 @@ struct SpmmPlan {
   int rows_wg;   // output rows per workgroup
   int nblk;      // source blocks
   int64_t ntiles;
+  int pad4;      // segments padded to multiples of 4 (plain SpMM only)
 };
 SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc);
 size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl);

@@ -13,8 +13,8 @@
 // segments are the rows of F (forward; src = z) or its columns (backward;
 // src = dy), optionally with the dc partials.
 //
-// Work decomposition (gfx950, wave64). A workgroup owns a tile of TT = 128
-// tokens and 8 * 4 * S output rows. The source is staged through LDS in
+// Work decomposition (gfx950, wave64). A workgroup of W waves (16, or 8
+// with dc partials) owns a tile of TT = 128 tokens and W * 4 * S output rows. The source is staged through LDS in
 // blocks of JB columns, token-minor (row jj of the staged block holds the
 // 128 tokens of source column jj), double buffered. Each wave is four groups
 // of 16 lanes; a group owns S consecutive output rows and lane gl of a group
@@ -47,11 +47,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kTT = 128;          // tokens per tile
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+constexpr int kWavesFwd = 16;     // waves per workgroup, plain SpMM
+constexpr int kWavesDc = 8;       // waves per workgroup with dc partials
 constexpr int kGroups = 4;        // 16-lane groups per wave
 constexpr int kTPL = 8;           // tokens per lane
-constexpr int kSfwd = 12;         // rows per group, plain SpMM
+constexpr int kSfwd = 6;          // rows per group, plain SpMM
 constexpr int kSdc = 8;           // rows per group with dc partials
 constexpr int kChunk = 16;        // entries per group load
 constexpr int kPad = 16;          // padding entries after the stream
@@ -75,22 +75,31 @@ SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
   int jb = 128;
   if (n_src > 0 && per_row * 128.0 / n_src > 6.0) jb = 64;
   pl.jb = jb;
-  pl.rows_wg = kWaves * kGroups * (dc ? kSdc : kSfwd);
+  pl.rows_wg = dc ? kWavesDc * kGroups * kSdc : kWavesFwd * kGroups * kSfwd;
   pl.nblk = (n_src + jb - 1) / jb;
   pl.ntiles = (T + kTT - 1) / kTT;
+  pl.pad4 = dc ? 0 : 1;
   return pl;
 }
 
-// prep layout: [stream int2 x (nnz+pad)] [korig int32 x nnz]
+// prep layout: [stream int2 x (cap+pad)] [korig int32 x cap]
 //              [bptr int32 x n_out*(nblk+1)] [ptr int32 x nblk*(n_out+1)] [base int32 x nblk+1]
 struct PrepLayout {
   size_t stream, korig, bptr, ptr, base, total;
+  int64_t cap;   // stream entries (padding included)
 };
+
+// With pad4, every (row, block) segment is padded to a multiple of 4 with
+// zero entries (LDS offset 0, value 0) so quads need no per-entry masks.
+static int64_t stream_cap(int64_t nnz, int n_out, const SpmmPlan& pl) {
+  return pl.pad4 ? nnz + 3 * static_cast<int64_t>(n_out) * pl.nblk : nnz;
+}
 static PrepLayout prep_layout(int64_t nnz, int n_out, const SpmmPlan& pl) {
   PrepLayout l;
   l.stream = 0;
-  l.korig = align256(static_cast<size_t>(nnz + kPad) * 8);
-  l.bptr = l.korig + align256(static_cast<size_t>(nnz) * 4);
+  l.cap = stream_cap(nnz, n_out, pl);
+  l.korig = align256(static_cast<size_t>(l.cap + kPad) * 8);
+  l.bptr = l.korig + align256(static_cast<size_t>(l.cap) * 4);
   l.ptr = l.bptr + align256(static_cast<size_t>(n_out) * (pl.nblk + 1) * 4);
   l.base = l.ptr + align256(static_cast<size_t>(pl.nblk) * (n_out + 1) * 4);
   l.total = l.base + align256(static_cast<size_t>(pl.nblk + 1) * 4);
@@ -140,7 +149,7 @@ __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* 
 // Per block b: ptr[b][o] = entries of block b in rows before o (exclusive
 // scan over rows), ptr[b][n_out] and base[b] = the block's total.
 __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restrict__ bptr,
-                                                        int n_out, int nblk,
+                                                        int n_out, int nblk, int pad4,
                                                         int32_t* __restrict__ ptr,
                                                         int32_t* __restrict__ base) {
   __shared__ int wsum[16];
@@ -156,6 +165,7 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restric
     if (o < n_out) {
       const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
       cnt = bptr[r + 1] - bptr[r];
+      if (pad4) cnt = (cnt + 3) & ~3;
     }
     const int incl = wave_incl_scan_i32(cnt);
     if (lane == 63) wsum[wid] = incl;
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restric
   }
 }
 
-// base[b] <- exclusive scan of the block totals (base[nblk] = nnz)
+// base[b] <- exclusive scan of the block totals (base[nblk] = stream length)
 __global__ __launch_bounds__(1024) void blk_base_kernel(int32_t* __restrict__ base, int nblk) {
   __shared__ int wsum[16];
   __shared__ int carry;
@@ -216,10 +226,7 @@ __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __res
                                const int32_t* __restrict__ ptr, const int32_t* __restrict__ base,
                                int2* __restrict__ stream, int32_t* __restrict__ korig) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (q >= nnz) {
-    if (q < nnz + kPad) stream[q] = make_int2(0, 0);
-    return;
-  }
+  if (q >= nnz) return;
   const int64_t k = perm ? perm[q] : q;
   const int o = perm ? E[2 * k + 1] : E[2 * k];
   const int col = perm ? E[2 * k] : E[2 * k + 1];
@@ -229,6 +236,15 @@ __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __res
                       ptr[static_cast<int64_t>(b) * (n_out + 1) + o] + (q - bptr[r]);
   stream[pos] = make_int2((col - b * jb) * kTT * 4, __float_as_int(c[k]));
   korig[pos] = static_cast<int32_t>(k);
+}
+
+// zero entries everywhere (padding), korig = -1 for them
+__global__ void fill_stream_kernel(int2* __restrict__ stream, int32_t* __restrict__ korig,
+                                   int64_t cap, int64_t n) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= n) return;
+  stream[q] = make_int2(0, 0);
+  if (q < cap) korig[q] = -1;
 }
 
 static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const float* c,
@@ -241,11 +257,13 @@ static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const fl
   const int64_t nb = static_cast<int64_t>(n_out) * (pl.nblk + 1);
   hipLaunchKernelGGL(bptr_kernel, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256), 0, s,
                      seg_ptr, E, perm, n_out, pl.nblk, pl.jb, bptr);
-  hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out, pl.nblk, ptr,
-                     base);
+  hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out, pl.nblk,
+                     pl.pad4, ptr, base);
   hipLaunchKernelGGL(blk_base_kernel, dim3(1), dim3(1024), 0, s, base, pl.nblk);
-  const int64_t ns = nnz + kPad;
-  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((ns + 255) / 256)), dim3(256), 0, s,
+  const int64_t nf = l.cap + kPad;
+  hipLaunchKernelGGL(fill_stream_kernel, dim3(static_cast<unsigned>((nf + 255) / 256)), dim3(256), 0,
+                     s, at<int2>(prep, l.stream), at<int32_t>(prep, l.korig), l.cap, nf);
+  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0, s,
                      E, c, perm, nnz, n_out, pl.nblk, pl.jb, bptr, ptr, base,
                      at<int2>(prep, l.stream), at<int32_t>(prep, l.korig));
   return hipGetLastError();
@@ -263,14 +281,15 @@ hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* perm, const in
 }
 
 // ------------------------------------------------------------ staging
-// Thread -> token tt = tid % 128, column group g = tid / 128 (0..3); load q
-// covers local columns (q*4 + g)*VEC .. +VEC-1 of the block. Loads are
+// Thread -> token tt = tid % 128, column group g = tid / 128; load q covers
+// local columns (q*kColGroups + g)*VEC .. +VEC-1 of the block. Loads are
 // unconditional (addresses clamped into the source) so the compiler can
 // count them; out-of-range elements are zeroed when stored to LDS.
-template <typename SrcT, int JB, bool VEC_OK>
+template <typename SrcT, int JB, bool VEC_OK, int THREADS>
 struct Stage {
+  static constexpr int kColGroups = THREADS / kTT;                  // column groups
   static constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));   // elements per 16 bytes
-  static constexpr int NL = JB / (4 * VEC);                          // 16-byte loads per thread
+  static constexpr int NL = JB / (kColGroups * VEC);                 // 16-byte loads per thread
   uint4 raw[NL];
 
   __device__ __forceinline__ void load(const SrcT* __restrict__ src, int64_t T, int n_src,
@@ -281,7 +300,7 @@ struct Stage {
     const SrcT* row = src + t * n_src;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const int col = b * JB + (q * 4 + g) * VEC;
+      const int col = b * JB + (q * kColGroups + g) * VEC;
       if constexpr (VEC_OK) {
         const int cc = col + VEC <= n_src ? col : n_src - VEC;
         raw[q] = *reinterpret_cast<const uint4*>(row + cc);
@@ -309,7 +328,7 @@ struct Stage {
     const bool tok_ok = t0 + tt < T;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const int cl = (q * 4 + g) * VEC;
+      const int cl = (q * kColGroups + g) * VEC;
       const int col = b * JB + cl;
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
@@ -353,7 +372,8 @@ struct Acc {
 
 // Entries u in [U0, U0+4) of a 16-entry chunk (lane gl of the group holds
 // entry gl); groups with fewer than u+1 entries are masked off.
-template <int U0, int S, bool DC>
+// PADDED: the segment length is a multiple of 4, so no entry is masked.
+template <int U0, int S, bool DC, bool PADDED>
 __device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int cnt,
                                      const char* sb, float* __restrict__ prow, int gl) {
   float4 v[4][2];
@@ -364,7 +384,7 @@ __device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int 
   off[3] = row_bcast<U0 + 3>(ent.x);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (U0 + u < cnt) {
+    if (PADDED || U0 + u < cnt) {
       v[u][0] = *reinterpret_cast<const float4*>(sb + off[u]);
       v[u][1] = *reinterpret_cast<const float4*>(sb + off[u] + kHalfTile);
     }
@@ -376,7 +396,7 @@ __device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int 
   cv[3] = __int_as_float(row_bcast<U0 + 3>(ent.y));
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (U0 + u < cnt) {
+    if (PADDED || U0 + u < cnt) {
       const float x[kTPL] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
                              v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
@@ -393,18 +413,18 @@ __device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int 
 }
 
 // One 16-entry chunk of slot s with cnt valid entries (cnt may be <= 0).
-template <int S, bool DC>
+template <int S, bool DC, bool PADDED>
 __device__ __forceinline__ void chunk16(Acc<S, DC>& A, int s, const int2& ent, int cnt,
                                         const char* sb, float* __restrict__ prow, int gl) {
-  if (cnt > 0) quad<0>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 4) quad<4>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 8) quad<8>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 12) quad<12>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 0) quad<0, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 4) quad<4, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 8) quad<8, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
+  if (cnt > 12) quad<12, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
 }
 
 // ------------------------------------------------------------ main kernel
-template <int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
-__global__ __launch_bounds__(kThreads) void spmm_kernel(
+template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC, bool PADDED>
+__global__ __launch_bounds__(WAVES * 64) void spmm_kernel(
     const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
     int nblk, float alpha, OutT* __restrict__ out, int accumulate,
@@ -416,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
   const int w = uniform(threadIdx.x >> 6);
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTT;
-  const int rows_wg = kWaves * kGroups * S;
+  const int rows_wg = WAVES * kGroups * S;
   const int orow = static_cast<int>(blockIdx.y) * rows_wg + (w * kGroups + g) * S;
   const int lds_lane = gl * 16;      // lane's first 4 tokens; the other 4 are kHalfTile later
 
@@ -443,23 +463,21 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
   const int prow_idx = rsel < n_out ? rsel : n_out;
   int pv = ptr[prow_idx] + base[0];
 
-  Stage<SrcT, JB, VEC_OK> pf;
+  Stage<SrcT, JB, VEC_OK, WAVES * 64> pf;
   pf.load(src, T, n_src, t0, 0);
   for (int b = 0; b < nblk; ++b) {
     float* st = stage[b & 1];
     pf.store(st, T, n_src, t0, b);
     __syncthreads();
     // this block's segments: slot s spans [lane s's pv, lane s+1's pv)
-    int k0[S], cnt[S];
     int2 ent[S];
     static_for<0, S>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      k0[s] = row_bcast<s>(pv);
-      cnt[s] = row_bcast<s + 1>(pv) - k0[s];
-      ent[s] = stream[k0[s] + gl];
+      ent[s] = stream[row_bcast<s>(pv) + gl];
     });
     // next block's segment starts, then the next block's staging loads
     // (issued after every entry load of this block)
+    const int pvb = pv;
     const int bn = b + 1 < nblk ? b + 1 : b;
     pv = ptr[static_cast<int64_t>(bn) * (n_out + 1) + prow_idx] + base[bn];
     pf.load(src, T, n_src, t0, bn);
@@ -467,12 +485,15 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
     const char* sb = reinterpret_cast<const char*>(st) + lds_lane;
     static_for<0, S>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
-      float* prow = DC ? partial + tile * nnz + k0[s] : nullptr;
-      chunk16<S, DC>(A, s, ent[s], cnt[s], sb, prow, gl);
+      // slot s spans [lane s's start, lane s+1's start) of the block's stream
+      const int k0 = row_bcast<s>(pvb);
+      const int cnt = row_bcast<s + 1>(pvb) - k0;
+      float* prow = DC ? partial + tile * nnz + k0 : nullptr;
+      chunk16<S, DC, PADDED>(A, s, ent[s], cnt, sb, prow, gl);
       // segments longer than one chunk: further 16-entry rounds
-      for (int kk = kChunk; kk < cnt[s]; kk += kChunk) {
-        const int2 e2 = stream[k0[s] + kk + gl];
-        chunk16<S, DC>(A, s, e2, cnt[s] - kk, sb, DC ? prow + kk : nullptr, gl);
+      for (int kk = kChunk; kk < cnt; kk += kChunk) {
+        const int2 e2 = stream[k0 + kk + gl];
+        chunk16<S, DC, PADDED>(A, s, e2, cnt - kk, sb, DC ? prow + kk : nullptr, gl);
       }
     });
   }
@@ -495,37 +516,43 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(
   }
 }
 
-template <int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
+template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
 static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
                          const float* zsrc, float* partial, hipStream_t s) {
-  constexpr int rows_wg = kWaves * kGroups * S;
+  constexpr int rows_wg = WAVES * kGroups * S;
   const int gy = (n_out + rows_wg - 1) / rows_wg;
   void* pp = const_cast<void*>(prep);
   const PrepLayout l = prep_layout(nnz, n_out, pl);
-  hipLaunchKernelGGL((spmm_kernel<S, JB, VEC_OK, SrcT, OutT, DC>),
-                     dim3(static_cast<unsigned>(pl.ntiles), gy), dim3(kThreads), 0, s,
-                     static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
-                     at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out, pl.nblk, alpha,
-                     static_cast<OutT*>(out), acc, zsrc, partial);
+  const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
+  if (!DC && pl.pad4)
+    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, true>), grid,
+                       dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
+                       at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
+                       nnz, n_out, pl.nblk, alpha, static_cast<OutT*>(out), acc, zsrc, partial);
+  else
+    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, false>), grid,
+                       dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
+                       at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
+                       nnz, n_out, pl.nblk, alpha, static_cast<OutT*>(out), acc, zsrc, partial);
   return hipGetLastError();
 }
 
-template <int S, typename SrcT, typename OutT, bool DC>
+template <int WAVES, int S, typename SrcT, typename OutT, bool DC>
 static hipError_t spmm_jb(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                           int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
                           const float* zsrc, float* partial, hipStream_t s) {
   constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
   const bool vec_ok = n_src % VEC == 0 && n_src >= VEC;
   if (pl.jb == 128) {
-    return vec_ok ? spmm_t<S, 128, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+    return vec_ok ? spmm_t<WAVES, S, 128, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
                                                          out, acc, zsrc, partial, s)
-                  : spmm_t<S, 128, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl,
+                  : spmm_t<WAVES, S, 128, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl,
                                                           alpha, out, acc, zsrc, partial, s);
   }
-  return vec_ok ? spmm_t<S, 64, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+  return vec_ok ? spmm_t<WAVES, S, 64, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
                                                       out, acc, zsrc, partial, s)
-                : spmm_t<S, 64, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+                : spmm_t<WAVES, S, 64, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
                                                        out, acc, zsrc, partial, s);
 }
 
@@ -537,19 +564,19 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
   if (partial != nullptr) {
     if (out_dt != Dt::F32) return hipErrorInvalidValue;
     return src_dt == Dt::F32
-               ? spmm_jb<kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+               ? spmm_jb<kWavesDc, kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                    accumulate, zsrc, partial, s)
-               : spmm_jb<kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha,
+               : spmm_jb<kWavesDc, kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha,
                                                       out, accumulate, zsrc, partial, s);
   }
   if (src_dt == Dt::F32 && out_dt == Dt::F32)
-    return spmm_jb<kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_jb<kWavesFwd, kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::F32 && out_dt == Dt::BF16)
-    return spmm_jb<kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_jb<kWavesFwd, kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                   accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-    return spmm_jb<kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
+    return spmm_jb<kWavesFwd, kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                   accumulate, nullptr, nullptr, s);
   return hipErrorInvalidValue;
 }
@@ -563,7 +590,8 @@ __global__ void dc_reduce_kernel(const float* __restrict__ partial, int64_t ntil
   if (q >= nnz) return;
   float s = 0.f;
   for (int64_t t = 0; t < ntiles; ++t) s += partial[t * nnz + q];
-  dc[korig[q]] = alpha * s;
+  const int k = korig[q];
+  if (k >= 0) dc[k] = alpha * s;
 }
 
 hipError_t launch_dc_reduce(const float* partial, int64_t ntiles, int64_t nnz,
