@@ -43,8 +43,11 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--sets", type=int, default=4, help="rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
-                    help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0: all of the workload's)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain fp32 copy kernel of this size (read + write) after the "
+                         "warmup, to calibrate HBM byte counters")
     return ap.parse_args()
 
 
@@ -155,6 +158,14 @@ def main():
     for s in range(args.warmup):
         step(s, False)
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
     print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
           flush=True)
 
@@ -207,7 +218,7 @@ def main():
     roof.pop("avg_us", None)
     roof["kernel"] = dom
     roof["avg_us"] = round(avg_us[dom], 2)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, args.config)
 
     fwd_bwd_us = sum(avg_us[k] for k in ("FWD_FWHT", "FWD_SPMM", "BWD_FWHT_X", "BWD_SPMM",
                                          "BWD_FWHT_DX", "BWD_DC_REDUCE"))
@@ -241,46 +252,88 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens or T)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(spec, layer, x_np, dy_np, n_tok):
-    """The fp64 oracle (as it stands) on the host cores: one step of the same
-    path on the full layer with a sample of n_tok tokens."""
+def source_digest():
+    """sha256 over the HIP sources and headers of the library: a traffic
+    figure measured on other sources is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantization_aware_sparse_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, config):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
+    None when there is none for this workload and these exact sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic:"):
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if kv.get("kernel") == kernel and kv.get("sources") == digest:
+                    return int(kv["bytes"])
+    return None
+
+
+def cpu_baseline(spec, layer, x_np, dy_np, n_tok, min_seconds=10.0):
+    """The fp64 oracle (as it stands) on the host cores: whole steps of the
+    same path (init, materialize, fwd, bwd, update, re-materialize) on the
+    full layer with n_tok of the workload's tokens, repeated until at least
+    min_seconds have passed. With n_tok < T the fwd+bwd share is scaled
+    linearly to T tokens."""
     import numpy as np
     import oracle as O
     import synth
     cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_limits
+        from threadpoolctl import threadpool_info, threadpool_limits
         limiter = threadpool_limits(limits=cores)
     except Exception:  # noqa: BLE001
-        limiter = None
+        threadpool_info = limiter = None
     n_tok = min(n_tok, spec.T)
     x = synth.act_to_f64(x_np[:n_tok])
     dy = synth.act_to_f64(dy_np[:n_tok])
-    t0 = time.perf_counter()
-    r = O.init_select(layer.dwq, spec.p, m=3)
-    dW = O.materialize(r["E"], r["c"], spec.d_out, spec.d_in, 1.0)
-    O.forward(x, dW)
-    _, dc = O.backward(x, dy, r["E"], r["c"], spec.d_out, spec.d_in, 1.0, dW=dW)
-    c2 = O.sign_update(r["c"], dc)
-    O.materialize(r["E"], c2, spec.d_out, spec.d_in, 1.0)
-    sec = time.perf_counter() - t0
+    fixed, tok, reps = 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t_start < min_seconds:
+        t0 = time.perf_counter()
+        r = O.init_select(layer.dwq, spec.p, m=3)
+        dW = O.materialize(r["E"], r["c"], spec.d_out, spec.d_in, 1.0)
+        t1 = time.perf_counter()
+        O.forward(x, dW)
+        _, dc = O.backward(x, dy, r["E"], r["c"], spec.d_out, spec.d_in, 1.0, dW=dW)
+        t2 = time.perf_counter()
+        c2 = O.sign_update(r["c"], dc)
+        O.materialize(r["E"], c2, spec.d_out, spec.d_in, 1.0)
+        t3 = time.perf_counter()
+        fixed += (t1 - t0) + (t3 - t2)
+        tok += t2 - t1
+        reps += 1
+    sec = time.perf_counter() - t_start
+    fixed /= reps
+    tok /= reps
+    step_s = fixed + tok * spec.T / n_tok
     threads = cores
-    try:
-        from threadpoolctl import threadpool_info
+    if threadpool_info is not None:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
-    except Exception:  # noqa: BLE001
-        pass
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": round(n_tok / sec, 2), "unit": "tokens/s", "cores": int(threads),
+    del limiter
+    scaled = "" if n_tok == spec.T else f", scaled to {spec.T} tokens"
+    return {"value": round(spec.T / step_s, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one oracle step (init, materialize, fwd, bwd, update, re-materialize) on "
-                      f"the full {spec.d_out}x{spec.d_in} layer with {n_tok} of {spec.T} tokens; "
-                      f"{sec:.1f} s"}
+            "sample": f"{reps} oracle step(s) on the full {spec.d_out}x{spec.d_in} layer with "
+                      f"{n_tok} of {spec.T} tokens ({sec:.1f} s): init + materialize + update + "
+                      f"re-materialize {fixed:.2f} s, fwd + bwd {tok:.2f} s per step{scaled}"}
 
 
 if __name__ == "__main__":

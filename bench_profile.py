@@ -1,0 +1,149 @@
+"""Turn rocprofv3 output of a bench.py run into the short text summaries kept
+under profiles/.
+
+  python bench_profile.py stats KERNEL_STATS_CSV OUT_MD --title T --command C
+      per-kernel call count and average / min / max duration
+  python bench_profile.py traffic FETCH_CSV WRITE_CSV OUT_MD --config c2 \\
+          --calib-mib 256 --command-fetch C1 --command-write C2
+      HBM bytes per launch of each library kernel from two counter runs
+      (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by
+      what the same counter reads for a plain fp32 copy of known size
+      (bench.py --calib-copy-mib). Writes one `traffic:` line per kernel,
+      tagged with the digest of the library's sources, which bench.py reads.
+
+The library's kernels are named by the profiling ids bench.py reports.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import re
+
+import bench
+
+# kernel symbol prefix -> profiling ids (spmm and fwht resolved by template arguments)
+KERNEL_IDS = {
+    "init_select_kernel": ["INIT_SELECT"],
+    "materialize_kernel": ["MATERIALIZE"],
+    "dc_reduce_kernel": ["BWD_DC_REDUCE"],
+}
+
+
+def short(name: str) -> str:
+    n = re.sub(r"\(.*", "", name)
+    return n.replace("qwha::", "").replace("void ", "")
+
+
+def template_args(n: str):
+    return [a.strip() for a in n[n.index("<") + 1:n.rindex(">")].split(",")]
+
+
+def kernel_ids(name: str):
+    n = short(name)
+    if n.startswith("spmm_kernel<"):
+        return ["BWD_SPMM" if template_args(n)[6] == "true" else "FWD_SPMM"]
+    if n.startswith("fwht_rows_kernel<"):
+        # FWHT(x) -> fp32 z in forward and backward; FWHT(dz) -> activations
+        return ["FWD_FWHT", "BWD_FWHT_X"] if template_args(n)[2] == "float" else ["BWD_FWHT_DX"]
+    for key, kids in KERNEL_IDS.items():
+        if n.startswith(key):
+            return kids
+    return []
+
+
+def cmd_stats(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    with open(a.out, "w") as f:
+        f.write(f"# {a.title}\n\n")
+        f.write("Command (from /tmp with TMPDIR=/tmp, one MI355X; $REPO is the repository "
+                "root):\n\n```\n" + a.command + "\n```\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | % of traced GPU time |\n"
+                "|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                    f"{float(r['Percentage']):.2f} |\n")
+    print("wrote", a.out)
+
+
+def per_kernel(path, counter):
+    """mean counter value per dispatch, by demangled kernel name"""
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[(r["Kernel_Name"], r.get("Dispatch_Id", ""))].append(float(r["Counter_Value"]))
+    by_name = collections.defaultdict(list)
+    for (name, _), vals in acc.items():
+        by_name[name].append(sum(vals))   # summed over dimensions / instances
+    return {n: sum(v) / len(v) for n, v in by_name.items()}
+
+
+def cmd_traffic(a):
+    fetch = per_kernel(a.fetch_csv, "FETCH_SIZE")
+    write = per_kernel(a.write_csv, "WRITE_SIZE")
+    known_kib = a.calib_mib * 1024.0
+    calib = [n for n in fetch if "elementwise" in n and "Mul" in n] or \
+            [n for n in fetch if "elementwise" in n]
+    if not calib:
+        raise SystemExit("no copy kernel in the FETCH_SIZE run (bench.py --calib-copy-mib)")
+    cname = max(calib, key=lambda n: fetch[n])
+    f_fetch = known_kib / fetch[cname]
+    f_write = known_kib / write[cname]
+    digest = bench.source_digest()
+    lines = []
+    table = []
+    for name in sorted(set(fetch) & set(write)):
+        kids = kernel_ids(name)
+        if not kids:
+            continue
+        fb = fetch[name] * f_fetch * 1024.0
+        wb = write[name] * f_write * 1024.0
+        table.append(("/".join(kids), short(name), fetch[name], write[name], fb, wb))
+        for kid in kids:
+            lines.append(f"traffic: kernel={kid} config={a.config} bytes={int(round(fb + wb))} "
+                         f"fetch={int(round(fb))} write={int(round(wb))} sources={digest}")
+    with open(a.out, "w") as f:
+        f.write(f"# HBM traffic per launch, workload {a.config}\n\n")
+        f.write("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc) in two runs, "
+                "each scaled by its reading for a plain fp32 copy of "
+                f"{a.calib_mib} MiB read + {a.calib_mib} MiB written in the same run.\n\n")
+        f.write("Commands (from /tmp with TMPDIR=/tmp, one MI355X; $REPO is the repository "
+                "root):\n\n```\n" + a.command_fetch + "\n" + a.command_write + "\n```\n\n")
+        f.write(f"Copy kernel `{short(cname)}`: FETCH_SIZE {fetch[cname]:.0f} KiB, WRITE_SIZE "
+                f"{write[cname]:.0f} KiB for {known_kib:.0f} KiB each way; scale factors "
+                f"fetch {f_fetch:.4f}, write {f_write:.4f}.\n\n")
+        f.write("| id | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch MB (scaled) | "
+                "write MB (scaled) |\n|---|---|---|---|---|---|\n")
+        for kid, n, fk, wk, fb, wb in table:
+            f.write(f"| {kid} | `{n}` | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |\n")
+        f.write("\nMachine-readable lines (sources = digest of the library's HIP sources when "
+                "the counters were taken; bench.py reports traffic only while it matches):\n\n")
+        for ln in lines:
+            f.write(ln + "\n")
+    print("wrote", a.out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--config", required=True)
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    a = ap.parse_args()
+    (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -525,8 +525,8 @@ static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep
   void* pp = const_cast<void*>(prep);
   const PrepLayout l = prep_layout(nnz, n_out, pl);
   const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
-  if (!DC && pl.pad4)
-    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, true>), grid,
+  if (pl.pad4)
+    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, !DC>), grid,
                        dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
                        at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
                        nnz, n_out, pl.nblk, alpha, static_cast<OutT*>(out), acc, zsrc, partial);
