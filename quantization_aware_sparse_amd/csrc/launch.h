@@ -34,12 +34,14 @@ hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const fl
 
 // ---- adapter forward / backward (gather SpMM / SDDMM)
 struct SpmmPlan {
+  int kind;      // 0: 16-lane row groups (dc partials), 1: wave-uniform rows
   int tt;        // tokens per tile
   int jb;        // source columns per staged block
   int rows_wg;   // output rows per workgroup
   int nblk;      // source blocks
   int64_t ntiles;
-  int pad4;      // segments padded to multiples of 4 (plain SpMM only)
+  int seg_mult;  // (row, block) segments padded with zero entries to a multiple of this
+  int ptr_stride;  // per-block segment table stride (>= n_out + 1)
 };
 SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc);
 size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl);

@@ -57,6 +57,13 @@ constexpr int kChunk = 16;        // entries per group load
 constexpr int kPad = 16;          // padding entries after the stream
 constexpr int kHalfTile = kTT * 2;  // bytes of 64 fp32 tokens
 
+// wave-uniform rows (plain SpMM)
+constexpr int kRT = 256;          // tokens per tile: 64 lanes x 4
+constexpr int kRJB = 64;          // source columns per staged block (64 KiB fp32)
+constexpr int kRW = 16;           // waves per workgroup
+constexpr int kRR = 16;           // output rows per wave
+constexpr int kEntCap = 1536;     // stream entries staged in LDS per block
+
 // Token (within the tile) held in accumulator q of lane gl of a group: lanes
 // take 4 consecutive tokens in each half of the tile, so a wave's
 // ds_read_b128 touches consecutive 16-byte chunks (no bank conflicts).
@@ -68,31 +75,43 @@ static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 
 SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
   SpmmPlan pl;
-  pl.tt = kTT;
-  // Column block: 128 unless a (row, block) segment would average more than
-  // six entries; longer segments need extra 16-entry rounds.
-  const double per_row = n_out > 0 ? static_cast<double>(nnz) / n_out : 0.0;
-  int jb = 128;
-  if (n_src > 0 && per_row * 128.0 / n_src > 6.0) jb = 64;
-  pl.jb = jb;
-  pl.rows_wg = dc ? kWavesDc * kGroups * kSdc : kWavesFwd * kGroups * kSfwd;
-  pl.nblk = (n_src + jb - 1) / jb;
-  pl.ntiles = (T + kTT - 1) / kTT;
-  pl.pad4 = dc ? 0 : 1;
+  if (!dc) {
+    // wave-uniform rows: 256-token tiles, 64-column blocks
+    pl.kind = 1;
+    pl.tt = kRT;
+    pl.jb = kRJB;
+    pl.rows_wg = kRW * kRR;
+    pl.seg_mult = 2;
+  } else {
+    pl.kind = 0;
+    pl.tt = kTT;
+    // Column block: 128 unless a (row, block) segment would average more
+    // than six entries; longer segments need extra 16-entry rounds.
+    const double per_row = n_out > 0 ? static_cast<double>(nnz) / n_out : 0.0;
+    int jb = 128;
+    if (n_src > 0 && per_row * 128.0 / n_src > 6.0) jb = 64;
+    pl.jb = jb;
+    pl.rows_wg = kWavesDc * kGroups * kSdc;
+    pl.seg_mult = 1;
+  }
+  pl.nblk = (n_src + pl.jb - 1) / pl.jb;
+  pl.ntiles = (T + pl.tt - 1) / pl.tt;
+  const int n_out_pad = (n_out + pl.rows_wg - 1) / pl.rows_wg * pl.rows_wg;
+  pl.ptr_stride = n_out_pad + 1;
   return pl;
 }
 
 // prep layout: [stream int2 x (cap+pad)] [korig int32 x cap]
-//              [bptr int32 x n_out*(nblk+1)] [ptr int32 x nblk*(n_out+1)] [base int32 x nblk+1]
+//              [bptr int32 x n_out*(nblk+1)] [ptr int32 x nblk*ptr_stride] [base int32 x nblk+1]
 struct PrepLayout {
   size_t stream, korig, bptr, ptr, base, total;
   int64_t cap;   // stream entries (padding included)
 };
 
-// With pad4, every (row, block) segment is padded to a multiple of 4 with
-// zero entries (LDS offset 0, value 0) so quads need no per-entry masks.
+// Every (row, block) segment is padded with zero entries (LDS offset 0,
+// value 0) to a multiple of seg_mult.
 static int64_t stream_cap(int64_t nnz, int n_out, const SpmmPlan& pl) {
-  return pl.pad4 ? nnz + 3 * static_cast<int64_t>(n_out) * pl.nblk : nnz;
+  return nnz + static_cast<int64_t>(pl.seg_mult - 1) * n_out * pl.nblk;
 }
 static PrepLayout prep_layout(int64_t nnz, int n_out, const SpmmPlan& pl) {
   PrepLayout l;
@@ -101,7 +120,7 @@ static PrepLayout prep_layout(int64_t nnz, int n_out, const SpmmPlan& pl) {
   l.korig = align256(static_cast<size_t>(l.cap + kPad) * 8);
   l.bptr = l.korig + align256(static_cast<size_t>(l.cap) * 4);
   l.ptr = l.bptr + align256(static_cast<size_t>(n_out) * (pl.nblk + 1) * 4);
-  l.base = l.ptr + align256(static_cast<size_t>(pl.nblk) * (n_out + 1) * 4);
+  l.base = l.ptr + align256(static_cast<size_t>(pl.nblk) * pl.ptr_stride * 4);
   l.total = l.base + align256(static_cast<size_t>(pl.nblk + 1) * 4);
   return l;
 }
@@ -148,8 +167,9 @@ __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* 
 
 // Per block b: ptr[b][o] = entries of block b in rows before o (exclusive
 // scan over rows), ptr[b][n_out] and base[b] = the block's total.
+// Rows n_out .. stride-2 (padding up to a whole workgroup of rows) are empty.
 __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restrict__ bptr,
-                                                        int n_out, int nblk, int pad4,
+                                                        int n_out, int stride, int nblk, int mult,
                                                         int32_t* __restrict__ ptr,
                                                         int32_t* __restrict__ base) {
   __shared__ int wsum[16];
@@ -158,14 +178,15 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restric
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
-  int32_t* pb = ptr + static_cast<int64_t>(b) * (n_out + 1);
-  for (int o0 = 0; o0 < n_out; o0 += 1024) {
+  int32_t* pb = ptr + static_cast<int64_t>(b) * stride;
+  const int n_rows = stride - 1;
+  for (int o0 = 0; o0 < n_rows; o0 += 1024) {
     const int o = o0 + threadIdx.x;
     int cnt = 0;
     if (o < n_out) {
       const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
       cnt = bptr[r + 1] - bptr[r];
-      if (pad4) cnt = (cnt + 3) & ~3;
+      cnt = (cnt + mult - 1) / mult * mult;
     }
     const int incl = wave_incl_scan_i32(cnt);
     if (lane == 63) wsum[wid] = incl;
@@ -176,13 +197,13 @@ __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restric
       if (i < wid) before += v;
       all += v;
     }
-    if (o < n_out) pb[o] = carry + before + incl - cnt;
+    if (o < n_rows) pb[o] = carry + before + incl - cnt;
     __syncthreads();
     if (threadIdx.x == 0) carry += all;
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    pb[n_out] = carry;
+    pb[n_rows] = carry;
     base[b] = carry;
   }
 }
@@ -221,8 +242,8 @@ __global__ __launch_bounds__(1024) void blk_base_kernel(int32_t* __restrict__ ba
 // column E[2 perm[q]] (a row of F), value c[perm[q]].
 // korig[pos] keeps the nonzero's index k in E.
 __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __restrict__ c,
-                               const int32_t* __restrict__ perm, int64_t nnz, int n_out, int nblk,
-                               int jb, const int32_t* __restrict__ bptr,
+                               const int32_t* __restrict__ perm, int64_t nnz, int stride, int nblk,
+                               int jb, int tt, const int32_t* __restrict__ bptr,
                                const int32_t* __restrict__ ptr, const int32_t* __restrict__ base,
                                int2* __restrict__ stream, int32_t* __restrict__ korig) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -233,8 +254,8 @@ __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __res
   const int b = col / jb;
   const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
   const int64_t pos = static_cast<int64_t>(base[b]) +
-                      ptr[static_cast<int64_t>(b) * (n_out + 1) + o] + (q - bptr[r]);
-  stream[pos] = make_int2((col - b * jb) * kTT * 4, __float_as_int(c[k]));
+                      ptr[static_cast<int64_t>(b) * stride + o] + (q - bptr[r]);
+  stream[pos] = make_int2((col - b * jb) * tt * 4, __float_as_int(c[k]));
   korig[pos] = static_cast<int32_t>(k);
 }
 
@@ -257,14 +278,14 @@ static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const fl
   const int64_t nb = static_cast<int64_t>(n_out) * (pl.nblk + 1);
   hipLaunchKernelGGL(bptr_kernel, dim3(static_cast<unsigned>((nb + 255) / 256)), dim3(256), 0, s,
                      seg_ptr, E, perm, n_out, pl.nblk, pl.jb, bptr);
-  hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out, pl.nblk,
-                     pl.pad4, ptr, base);
+  hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out,
+                     pl.ptr_stride, pl.nblk, pl.seg_mult, ptr, base);
   hipLaunchKernelGGL(blk_base_kernel, dim3(1), dim3(1024), 0, s, base, pl.nblk);
   const int64_t nf = l.cap + kPad;
   hipLaunchKernelGGL(fill_stream_kernel, dim3(static_cast<unsigned>((nf + 255) / 256)), dim3(256), 0,
                      s, at<int2>(prep, l.stream), at<int32_t>(prep, l.korig), l.cap, nf);
   hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0, s,
-                     E, c, perm, nnz, n_out, pl.nblk, pl.jb, bptr, ptr, base,
+                     E, c, perm, nnz, pl.ptr_stride, pl.nblk, pl.jb, pl.tt, bptr, ptr, base,
                      at<int2>(prep, l.stream), at<int32_t>(prep, l.korig));
   return hipGetLastError();
 }
@@ -427,7 +448,7 @@ template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, b
 __global__ __launch_bounds__(WAVES * 64) void spmm_kernel(
     const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
-    int nblk, float alpha, OutT* __restrict__ out, int accumulate,
+    int ptr_stride, int nblk, float alpha, OutT* __restrict__ out, int accumulate,
     const float* __restrict__ zsrc, float* __restrict__ partial) {
   __shared__ float stage[2][JB * kTT];
   const int lane = threadIdx.x & 63;
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(WAVES * 64) void spmm_kernel(
     // (issued after every entry load of this block)
     const int pvb = pv;
     const int bn = b + 1 < nblk ? b + 1 : b;
-    pv = ptr[static_cast<int64_t>(bn) * (n_out + 1) + prow_idx] + base[bn];
+    pv = ptr[static_cast<int64_t>(bn) * ptr_stride + prow_idx] + base[bn];
     pf.load(src, T, n_src, t0, bn);
 
     const char* sb = reinterpret_cast<const char*>(st) + lds_lane;
@@ -516,6 +537,395 @@ __global__ __launch_bounds__(WAVES * 64) void spmm_kernel(
   }
 }
 
+// ------------------------------------------------------------ wave-uniform rows
+// Plain SpMM (no dc partials). A workgroup of 16 waves owns a tile of 256
+// tokens and 256 output rows; wave w owns rows row0 .. row0+15 and lane l
+// owns tokens 4l .. 4l+3 of the tile, so a row's segment is the same for the
+// whole wave: its entries are read with scalar loads and each costs one
+// conflict-free ds_read_b128 (1 KiB per wave), one address add and four FMAs
+// with the value as a scalar operand. No entry is masked or padded.
+//
+// Staging: block b of 64 source columns is held token-minor (row jj of the
+// block is the 256 tokens of column jj), double buffered; thread tid loads
+// 16 columns of token tid % 256 (16-byte loads), the next block's loads are
+// in flight while the current block is consumed.
+template <typename SrcT, bool VEC_OK>
+struct StageRows {
+  static constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));  // elements per 16 bytes
+  static constexpr int NL = 16 / VEC;                                // 16-byte loads per thread
+  static constexpr int NH = NL / 2;                                  // loads per half
+  uint4 raw[NH];
+
+  // half h covers the thread's columns g*16 + h*8 .. +7
+  __device__ __forceinline__ void load(const SrcT* __restrict__ src, int64_t T, int n_src,
+                                       int64_t t0, int b, int h) {
+    const int tt = threadIdx.x & (kRT - 1);
+    const int g = threadIdx.x / kRT;
+    const int64_t t = t0 + tt < T ? t0 + tt : T - 1;
+    const SrcT* row = src + t * n_src;
+#pragma unroll
+    for (int q = 0; q < NH; ++q) {
+      const int col = b * kRJB + g * 16 + h * 8 + q * VEC;
+      if constexpr (VEC_OK) {
+        const int cc = col + VEC <= n_src ? col : n_src - VEC;
+        raw[q] = *reinterpret_cast<const uint4*>(row + cc);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int cc = col + e < n_src ? col + e : n_src - 1;
+          if constexpr (sizeof(SrcT) == 4) {
+            w[e] = __float_as_uint(reinterpret_cast<const float*>(row)[cc]);
+          } else {
+            const uint32_t bits = reinterpret_cast<const uint16_t*>(row)[cc];
+            w[e >> 1] |= bits << (16 * (e & 1));
+          }
+        }
+        raw[q] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(float* __restrict__ st, int64_t T, int n_src, int64_t t0,
+                                        int b, int h) const {
+    const int tt = threadIdx.x & (kRT - 1);
+    const int g = threadIdx.x / kRT;
+    const bool tok_ok = t0 + tt < T;
+#pragma unroll
+    for (int q = 0; q < NH; ++q) {
+      const int cl = g * 16 + h * 8 + q * VEC;
+      const int col = b * kRJB + cl;
+      const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float f;
+        if constexpr (sizeof(SrcT) == 4) f = __uint_as_float(w[e]);
+        else f = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+        const bool ok = tok_ok && (VEC_OK ? (col + VEC <= n_src) : (col + e < n_src));
+        st[(cl + e) * kRT + tt] = ok ? f : 0.f;
+      }
+    }
+  }
+};
+
+// 16 consecutive outputs at a 16-byte aligned address (+= when accumulate)
+__device__ __forceinline__ void store_row16(float* dst, const float (&v)[16], int accumulate) {
+  float4* d = reinterpret_cast<float4*>(dst);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float4 o = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+    if (accumulate) {
+      const float4 a = d[j];
+      o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+    }
+    d[j] = o;
+  }
+}
+
+__device__ __forceinline__ void store_row16(uint16_t* dst, const float (&v)[16], int accumulate) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = v[8 * j + e];
+    if (accumulate) {
+      const uint4 a = d[j];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] += bf16_to_f32(static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu)));
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = static_cast<uint32_t>(f32_to_bf16(f[2 * e])) |
+             (static_cast<uint32_t>(f32_to_bf16(f[2 * e + 1])) << 16);
+    d[j] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__device__ __forceinline__ void fma4(float (&a)[4], float v, const float4& z) {
+  a[0] = fmaf(v, z.x, a[0]);
+  a[1] = fmaf(v, z.y, a[1]);
+  a[2] = fmaf(v, z.z, a[2]);
+  a[3] = fmaf(v, z.w, a[3]);
+}
+
+// A group of up to four consecutive entries: ea = entries 0, 1 and eb =
+// entries 2, 3 as (LDS byte offset, value bits) pairs.
+__device__ __forceinline__ float4 lds4(const char* sb, int off) {
+  return *reinterpret_cast<const float4*>(sb + off);
+}
+
+template <int N>
+__device__ __forceinline__ void grp_read(float4 (&z)[4], const char* sb, const int4& ea,
+                                         const int4& eb) {
+  z[0] = lds4(sb, ea.x);
+  if constexpr (N > 1) z[1] = lds4(sb, ea.z);
+  if constexpr (N > 2) z[2] = lds4(sb, eb.x);
+  if constexpr (N > 3) z[3] = lds4(sb, eb.z);
+}
+
+template <int N>
+__device__ __forceinline__ void grp_fma(float (&a)[4], const float4 (&z)[4], const int4& ea,
+                                        const int4& eb) {
+  fma4(a, __int_as_float(ea.y), z[0]);
+  if constexpr (N > 1) fma4(a, __int_as_float(ea.w), z[1]);
+  if constexpr (N > 2) fma4(a, __int_as_float(eb.y), z[2]);
+  if constexpr (N > 3) fma4(a, __int_as_float(eb.w), z[3]);
+}
+
+// entries k .. k+3 (the stream is padded, so reading past a segment is safe)
+__device__ __forceinline__ void grp_load(const int2* __restrict__ stream, int k, int4& ea,
+                                         int4& eb) {
+  ea = *reinterpret_cast<const int4*>(stream + k);
+  eb = *reinterpret_cast<const int4*>(stream + k + 2);
+}
+
+// Marks the pair's four words as used here: the scalar load stays whole and
+// is waited for at this point, not earlier.
+__device__ __forceinline__ void pair_pin(int4& e) {
+  asm volatile("" : "+s"(e.x), "+s"(e.y), "+s"(e.z), "+s"(e.w));
+}
+
+// Marks all eight words as used here, so the compiler keeps the group's
+// scalar load whole and waits for it at this point, not earlier.
+__device__ __forceinline__ void grp_pin(int4& ea, int4& eb) {
+  asm volatile("" : "+s"(ea.x), "+s"(ea.y), "+s"(ea.z), "+s"(ea.w), "+s"(eb.x), "+s"(eb.y),
+               "+s"(eb.z), "+s"(eb.w));
+}
+
+// N entries of (ea, eb): LDS reads, then the load of the group at `nxt`
+// into (na, nb), then the FMAs.
+template <int N>
+__device__ __forceinline__ void grp_step(float (&a)[4], const char* sb, const int4& ea,
+                                         const int4& eb, const int2* __restrict__ stream, int nxt,
+                                         int4& na, int4& nb) {
+  float4 z[4];
+  grp_read<N>(z, sb, ea, eb);
+  grp_load(stream, nxt, na, nb);
+  grp_fma<N>(a, z, ea, eb);
+  grp_pin(na, nb);
+}
+
+// The wave's rows in one block: row r owns pairs [sg[r], sg[r+1]) of the
+// workgroup's run (segments are padded to even lengths), of which pairs
+// [c0, c0 + kEntCap / 2) are staged in pp as (offset0, offset1, value0,
+// value1). Rows r and r + kRR/2 advance together, one pair each per step,
+// so four LDS reads are in flight per wait; a step reads the next pairs'
+// offsets while its own reads are in flight and the next values after its
+// FMAs, so nothing is copied. mid() runs once, after half the rows.
+template <typename Mid>
+__device__ __forceinline__ void rows_pairs(float (&acc)[kRR][4], const int (&sg)[kRR + 1],
+                                           int c0, const char* sb, const int4* pp, Mid mid) {
+  constexpr int kH = kRR / 2;
+  const int c1 = c0 + kEntCap / 2;
+  const int* pw = reinterpret_cast<const int*>(pp) - 4 * c0;
+  auto off_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i); };
+  auto val_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i + 2); };
+  auto clampc = [&](int v) { return v < c0 ? c0 : (v > c1 ? c1 : v); };
+#pragma unroll
+  for (int r = 0; r < kH; ++r) {
+    float (&aa)[4] = acc[r];
+    float (&ab)[4] = acc[r + kH];
+    int ia = clampc(sg[r]);
+    const int ea = clampc(sg[r + 1]);
+    int ib = clampc(sg[r + kH]);
+    const int eb = clampc(sg[r + kH + 1]);
+    int2 offa = off_at(ia), vala = val_at(ia);
+    int2 offb = off_at(ib), valb = val_at(ib);
+    for (; ia < ea && ib < eb; ++ia, ++ib) {
+      const float4 za0 = lds4(sb, offa.x);
+      const float4 za1 = lds4(sb, offa.y);
+      const float4 zb0 = lds4(sb, offb.x);
+      const float4 zb1 = lds4(sb, offb.y);
+      offa = off_at(ia + 1);
+      offb = off_at(ib + 1);
+      asm volatile("" ::: "memory");
+      fma4(aa, __int_as_float(vala.x), za0);
+      fma4(aa, __int_as_float(vala.y), za1);
+      fma4(ab, __int_as_float(valb.x), zb0);
+      fma4(ab, __int_as_float(valb.y), zb1);
+      vala = val_at(ia + 1);
+      valb = val_at(ib + 1);
+      asm volatile("" ::: "memory");
+    }
+    for (; ia < ea; ++ia) {
+      const float4 za0 = lds4(sb, offa.x);
+      const float4 za1 = lds4(sb, offa.y);
+      offa = off_at(ia + 1);
+      asm volatile("" ::: "memory");
+      fma4(aa, __int_as_float(vala.x), za0);
+      fma4(aa, __int_as_float(vala.y), za1);
+      vala = val_at(ia + 1);
+      asm volatile("" ::: "memory");
+    }
+    for (; ib < eb; ++ib) {
+      const float4 zb0 = lds4(sb, offb.x);
+      const float4 zb1 = lds4(sb, offb.y);
+      offb = off_at(ib + 1);
+      asm volatile("" ::: "memory");
+      fma4(ab, __int_as_float(valb.x), zb0);
+      fma4(ab, __int_as_float(valb.y), zb1);
+      valb = val_at(ib + 1);
+      asm volatile("" ::: "memory");
+    }
+    if (r == kH / 2 - 1) mid();
+  }
+}
+
+// Per-block metadata of a workgroup: its rows' segment bounds relative to
+// the start k0 of its run of the stream, and the run's first kEntCap
+// entries as pairs. Entries past kEntCap are restaged in chunks.
+struct RowsMeta {
+  int seg;     // thread tid <= rows: bound of row tid
+  int4 pair;   // thread tid <= kEntCap / 2: pair tid of the run
+  int k0;      // uniform
+  __device__ __forceinline__ void load(const int2* __restrict__ stream,
+                                       const int32_t* __restrict__ ptr,
+                                       const int32_t* __restrict__ base, int ptr_stride, int rg0,
+                                       int b) {
+    const int32_t* pb = ptr + static_cast<int64_t>(b) * ptr_stride + rg0;
+    const int p0 = pb[0];
+    k0 = base[b] + p0;
+    const int cnt = pb[kRW * kRR] - p0;
+    const int tid = threadIdx.x;
+    seg = tid <= kRW * kRR ? pb[tid] - p0 : 0;
+    // the stream is padded past its end, so a pair may straddle the run's end
+    pair = 2 * tid < cnt && tid < kEntCap / 2
+               ? *reinterpret_cast<const int4*>(stream + k0 + 2 * tid)
+               : make_int4(0, 0, 0, 0);   // pair kEntCap / 2 (read, never used) is zero
+  }
+  __device__ __forceinline__ void store(int* segs, int4* pairs) const {
+    const int tid = threadIdx.x;
+    if (tid <= kRW * kRR) segs[tid] = seg;
+    if (tid < kEntCap / 2 + 1) pairs[tid] = make_int4(pair.x, pair.z, pair.y, pair.w);
+  }
+};
+
+template <typename SrcT, typename OutT, bool VEC_OK>
+__global__ __launch_bounds__(kRW * 64) void rows_kernel(
+    const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int n_out, int ptr_stride,
+    int nblk, float alpha, OutT* __restrict__ out, int accumulate) {
+  __shared__ float stage[2][kRJB * kRT];
+  __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + entries read past the end
+  __shared__ int segs[2][kRW * kRR + 1];
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
+  const int rg0 = static_cast<int>(blockIdx.y) * (kRW * kRR);
+  const int row0 = rg0 + w * kRR;
+
+  float acc[kRR][4];
+#pragma unroll
+  for (int r = 0; r < kRR; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+
+  StageRows<SrcT, VEC_OK> pf;
+  RowsMeta meta;
+  meta.load(stream, ptr, base, ptr_stride, rg0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pf.load(src, T, n_src, t0, 0, h);
+    pf.store(stage[0], T, n_src, t0, 0, h);
+  }
+  meta.store(segs[0], pairs[0]);
+  for (int b = 0; b < nblk; ++b) {
+    __syncthreads();
+    const int k0 = meta.k0;
+    const bool more = b + 1 < nblk;
+    const int nb = b + 1;
+    float* nst = stage[nb & 1];
+    if (more) {
+      pf.load(src, T, n_src, t0, nb, 0);
+      meta.load(stream, ptr, base, ptr_stride, rg0, nb);
+    }
+    const int buf = b & 1;
+    int sg[kRR + 1];
+#pragma unroll
+    for (int r = 0; r <= kRR; ++r) sg[r] = uniform(segs[buf][w * kRR + r]) >> 1;
+    const char* sb = reinterpret_cast<const char*>(stage[buf]) + lane * 16;
+    auto mid = [&]() {
+      if (more) {
+        pf.store(nst, T, n_src, t0, nb, 0);
+        pf.load(src, T, n_src, t0, nb, 1);
+      }
+    };
+    // Runs longer than the staged cap go in chunks of kEntCap / 2 pairs,
+    // restaged from the stream between barriers (all waves take part).
+    const int run = uniform(segs[buf][kRW * kRR]) >> 1;
+    rows_pairs(acc, sg, 0, sb, pairs[buf], mid);
+    for (int c0 = kEntCap / 2; c0 < run; c0 += kEntCap / 2) {
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < kEntCap / 2) {
+        const int4 e = c0 + t < run ? *reinterpret_cast<const int4*>(stream + k0 + 2 * (c0 + t))
+                                    : make_int4(0, 0, 0, 0);
+        pairs[buf][t] = make_int4(e.x, e.z, e.y, e.w);
+      }
+      __syncthreads();
+      rows_pairs(acc, sg, c0, sb, pairs[buf], [] {});
+    }
+    if (more) {
+      pf.store(nst, T, n_src, t0, nb, 1);
+      meta.store(segs[nb & 1], pairs[nb & 1]);
+    }
+  }
+
+  // epilogue: lane writes rows row0 .. row0+15 (contiguous) of its 4 tokens,
+  // as 16-byte stores when the rows are whole and aligned
+  constexpr int kVec = 16 / static_cast<int>(sizeof(OutT));
+  const bool vec = row0 + kRR <= n_out && n_out % kVec == 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * lane + q;
+    if (t >= T) continue;
+    OutT* dst = out + t * n_out;
+    if (vec) {
+      float v[kRR];
+#pragma unroll
+      for (int r = 0; r < kRR; ++r) v[r] = alpha * acc[r][q];
+      store_row16(dst + row0, v, accumulate);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kRR; ++r) {
+        const int o = row0 + r;
+        if (o < n_out) {
+          float val = alpha * acc[r][q];
+          if (accumulate) val += Elem<OutT>::ld(dst, o);
+          Elem<OutT>::st(dst, o, val);
+        }
+      }
+    }
+  }
+}
+
+template <typename SrcT, typename OutT>
+static hipError_t rows_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
+                         int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
+                         hipStream_t s) {
+  const int gy = (n_out + pl.rows_wg - 1) / pl.rows_wg;
+  void* pp = const_cast<void*>(prep);
+  const PrepLayout l = prep_layout(nnz, n_out, pl);
+  const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
+  constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
+  const bool vec_ok = (n_src % VEC) == 0 && n_src >= VEC;
+  if (vec_ok)
+    hipLaunchKernelGGL((rows_kernel<SrcT, OutT, true>), grid, dim3(kRW * 64), 0, s,
+                       static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
+                       at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), n_out, pl.ptr_stride,
+                       pl.nblk, alpha, static_cast<OutT*>(out), acc);
+  else
+    hipLaunchKernelGGL((rows_kernel<SrcT, OutT, false>), grid, dim3(kRW * 64), 0, s,
+                       static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
+                       at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), n_out, pl.ptr_stride,
+                       pl.nblk, alpha, static_cast<OutT*>(out), acc);
+  return hipGetLastError();
+}
+
 template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
 static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
@@ -525,16 +935,18 @@ static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep
   void* pp = const_cast<void*>(prep);
   const PrepLayout l = prep_layout(nnz, n_out, pl);
   const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
-  if (pl.pad4)
+  if (pl.seg_mult == 4)
     hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, !DC>), grid,
                        dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
                        at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
-                       nnz, n_out, pl.nblk, alpha, static_cast<OutT*>(out), acc, zsrc, partial);
+                       nnz, n_out, pl.ptr_stride, pl.nblk, alpha, static_cast<OutT*>(out), acc,
+                       zsrc, partial);
   else
     hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, false>), grid,
                        dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
                        at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
-                       nnz, n_out, pl.nblk, alpha, static_cast<OutT*>(out), acc, zsrc, partial);
+                       nnz, n_out, pl.ptr_stride, pl.nblk, alpha, static_cast<OutT*>(out), acc,
+                       zsrc, partial);
   return hipGetLastError();
 }
 
@@ -569,12 +981,22 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
                : spmm_jb<kWavesDc, kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha,
                                                       out, accumulate, zsrc, partial, s);
   }
+  if (pl.kind == 1) {
+    if (src_dt == Dt::F32 && out_dt == Dt::F32)
+      return rows_t<float, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate, s);
+    if (src_dt == Dt::F32 && out_dt == Dt::BF16)
+      return rows_t<float, uint16_t>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate,
+                                     s);
+    if (src_dt == Dt::BF16 && out_dt == Dt::F32)
+      return rows_t<uint16_t, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate,
+                                     s);
+    return hipErrorInvalidValue;
+  }
+  // 16-lane row groups without dc partials (the backward's dz when dc is
+  // not requested uses the dc plan)
   if (src_dt == Dt::F32 && out_dt == Dt::F32)
     return spmm_jb<kWavesFwd, kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                accumulate, nullptr, nullptr, s);
-  if (src_dt == Dt::F32 && out_dt == Dt::BF16)
-    return spmm_jb<kWavesFwd, kSfwd, float, uint16_t, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                  accumulate, nullptr, nullptr, s);
   if (src_dt == Dt::BF16 && out_dt == Dt::F32)
     return spmm_jb<kWavesFwd, kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
                                                   accumulate, nullptr, nullptr, s);
