@@ -120,15 +120,19 @@ struct BwdWs {
   size_t z, dz, prep, partial, total;
   SpmmPlan plan;
 };
-BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+// with_dc: the dz pass also forms the dc partials (one fp32 per nonzero and
+// token tile); without, it is the plain gather over entry pairs.
+BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p, bool with_dc) {
   BwdWs l;
-  l.plan = spmm_plan(T, d_out, d_in, p, true);
+  l.plan = spmm_plan(T, d_out, d_in, p, with_dc);
   const size_t zb = align256(static_cast<size_t>(T) * d_in * 4);
   l.z = 0;
   l.dz = zb;
   l.prep = 2 * zb;
   l.partial = l.prep + align256(spmm_prep_bytes(p, d_in, l.plan));
-  l.total = l.partial + align256(static_cast<size_t>(l.plan.ntiles) * static_cast<size_t>(p) * 4);
+  l.total = l.partial;
+  if (with_dc)
+    l.total += align256(static_cast<size_t>(l.plan.ntiles) * static_cast<size_t>(p) * 4);
   return l;
 }
 
@@ -284,7 +288,9 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
 // ------------------------------------------------------------------ backward
 size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
   if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
-  return bwd_ws(T, d_in, d_out, p).total;
+  const size_t a = bwd_ws(T, d_in, d_out, p, true).total;
+  const size_t b = bwd_ws(T, d_in, d_out, p, false).total;
+  return a > b ? a : b;
 }
 
 qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, int32_t d_in,
@@ -320,7 +326,7 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
   }
   QWHA_NEED(dy, 16);
   if (dc != nullptr) QWHA_NEED(x, 16);
-  const BwdWs l = bwd_ws(T, d_in, d_out, p);
+  const BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr);
   if (workspace == nullptr || workspace_bytes < l.total)
     return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", l.total);
   QWHA_NEED(workspace, 256);

@@ -62,6 +62,7 @@ constexpr int kRT = 256;          // tokens per tile: 64 lanes x 4
 constexpr int kRJB = 64;          // source columns per staged block (64 KiB fp32)
 constexpr int kRW = 16;           // waves per workgroup
 constexpr int kRR = 16;           // output rows per wave
+constexpr int kRRdc = 8;          // output rows per wave with dc partials
 constexpr int kEntCap = 1536;     // stream entries staged in LDS per block
 
 // Token (within the tile) held in accumulator q of lane gl of a group: lanes
@@ -74,26 +75,16 @@ __device__ __forceinline__ int lane_token(int gl, int q) {
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
+  (void)nnz;
   SpmmPlan pl;
-  if (!dc) {
-    // wave-uniform rows: 256-token tiles, 64-column blocks
-    pl.kind = 1;
-    pl.tt = kRT;
-    pl.jb = kRJB;
-    pl.rows_wg = kRW * kRR;
-    pl.seg_mult = 2;
-  } else {
-    pl.kind = 0;
-    pl.tt = kTT;
-    // Column block: 128 unless a (row, block) segment would average more
-    // than six entries; longer segments need extra 16-entry rounds.
-    const double per_row = n_out > 0 ? static_cast<double>(nnz) / n_out : 0.0;
-    int jb = 128;
-    if (n_src > 0 && per_row * 128.0 / n_src > 6.0) jb = 64;
-    pl.jb = jb;
-    pl.rows_wg = kWavesDc * kGroups * kSdc;
-    pl.seg_mult = 1;
-  }
+  // wave-uniform rows: 256-token tiles, 64-column blocks; the plain product
+  // walks entry pairs (segments padded to even lengths), the one with dc
+  // partials single entries (one partial per real entry)
+  pl.kind = dc ? 2 : 1;
+  pl.tt = kRT;
+  pl.jb = kRJB;
+  pl.rows_wg = dc ? kRW * kRRdc : kRW * kRR;
+  pl.seg_mult = dc ? 1 : 2;
   pl.nblk = (n_src + pl.jb - 1) / pl.jb;
   pl.ntiles = (T + pl.tt - 1) / pl.tt;
   const int n_out_pad = (n_out + pl.rows_wg - 1) / pl.rows_wg * pl.rows_wg;
@@ -109,9 +100,11 @@ struct PrepLayout {
 };
 
 // Every (row, block) segment is padded with zero entries (LDS offset 0,
-// value 0) to a multiple of seg_mult.
+// value 0) to a multiple of seg_mult: at most seg_mult - 1 per nonempty
+// segment, so at most (seg_mult - 1) * min(segments, nnz) in all.
 static int64_t stream_cap(int64_t nnz, int n_out, const SpmmPlan& pl) {
-  return nnz + static_cast<int64_t>(pl.seg_mult - 1) * n_out * pl.nblk;
+  const int64_t segs = static_cast<int64_t>(n_out) * pl.nblk;
+  return nnz + static_cast<int64_t>(pl.seg_mult - 1) * (segs < nnz ? segs : nnz);
 }
 static PrepLayout prep_layout(int64_t nnz, int n_out, const SpmmPlan& pl) {
   PrepLayout l;
@@ -712,74 +705,48 @@ __device__ __forceinline__ void grp_step(float (&a)[4], const char* sb, const in
 // The wave's rows in one block: row r owns pairs [sg[r], sg[r+1]) of the
 // workgroup's run (segments are padded to even lengths), of which pairs
 // [c0, c0 + kEntCap / 2) are staged in pp as (offset0, offset1, value0,
-// value1). Rows r and r + kRR/2 advance together, one pair each per step,
-// so four LDS reads are in flight per wait; a step reads the next pairs'
-// offsets while its own reads are in flight and the next values after its
-// FMAs, so nothing is copied. mid() runs once, after half the rows.
+// value1). The wave walks its pairs in order across its rows: a step reads
+// the next pair's offsets while its own z reads are in flight and the next
+// pair's values after its FMAs, so nothing is copied and a row's first pair
+// is already in registers when the row starts. mid() runs once, after half
+// the rows.
 template <typename Mid>
 __device__ __forceinline__ void rows_pairs(float (&acc)[kRR][4], const int (&sg)[kRR + 1],
                                            int c0, const char* sb, const int4* pp, Mid mid) {
-  constexpr int kH = kRR / 2;
   const int c1 = c0 + kEntCap / 2;
   const int* pw = reinterpret_cast<const int*>(pp) - 4 * c0;
   auto off_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i); };
   auto val_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i + 2); };
   auto clampc = [&](int v) { return v < c0 ? c0 : (v > c1 ? c1 : v); };
+  const int i0 = clampc(sg[0]);
+  int2 off = off_at(i0);
+  int2 val = val_at(i0);
+  asm volatile("" ::: "memory");
 #pragma unroll
-  for (int r = 0; r < kH; ++r) {
-    float (&aa)[4] = acc[r];
-    float (&ab)[4] = acc[r + kH];
-    int ia = clampc(sg[r]);
-    const int ea = clampc(sg[r + 1]);
-    int ib = clampc(sg[r + kH]);
-    const int eb = clampc(sg[r + kH + 1]);
-    int2 offa = off_at(ia), vala = val_at(ia);
-    int2 offb = off_at(ib), valb = val_at(ib);
-    for (; ia < ea && ib < eb; ++ia, ++ib) {
-      const float4 za0 = lds4(sb, offa.x);
-      const float4 za1 = lds4(sb, offa.y);
-      const float4 zb0 = lds4(sb, offb.x);
-      const float4 zb1 = lds4(sb, offb.y);
-      offa = off_at(ia + 1);
-      offb = off_at(ib + 1);
+  for (int r = 0; r < kRR; ++r) {
+    const int hi = clampc(sg[r + 1]);
+    for (int i = clampc(sg[r]); i < hi; ++i) {
+      const float4 z0 = lds4(sb, off.x);
+      const float4 z1 = lds4(sb, off.y);
+      off = off_at(i + 1);
       asm volatile("" ::: "memory");
-      fma4(aa, __int_as_float(vala.x), za0);
-      fma4(aa, __int_as_float(vala.y), za1);
-      fma4(ab, __int_as_float(valb.x), zb0);
-      fma4(ab, __int_as_float(valb.y), zb1);
-      vala = val_at(ia + 1);
-      valb = val_at(ib + 1);
+      fma4(acc[r], __int_as_float(val.x), z0);
+      fma4(acc[r], __int_as_float(val.y), z1);
+      val = val_at(i + 1);
       asm volatile("" ::: "memory");
     }
-    for (; ia < ea; ++ia) {
-      const float4 za0 = lds4(sb, offa.x);
-      const float4 za1 = lds4(sb, offa.y);
-      offa = off_at(ia + 1);
-      asm volatile("" ::: "memory");
-      fma4(aa, __int_as_float(vala.x), za0);
-      fma4(aa, __int_as_float(vala.y), za1);
-      vala = val_at(ia + 1);
-      asm volatile("" ::: "memory");
-    }
-    for (; ib < eb; ++ib) {
-      const float4 zb0 = lds4(sb, offb.x);
-      const float4 zb1 = lds4(sb, offb.y);
-      offb = off_at(ib + 1);
-      asm volatile("" ::: "memory");
-      fma4(ab, __int_as_float(valb.x), zb0);
-      fma4(ab, __int_as_float(valb.y), zb1);
-      valb = val_at(ib + 1);
-      asm volatile("" ::: "memory");
-    }
-    if (r == kH / 2 - 1) mid();
+    if (r == kRR / 2 - 1) mid();
   }
 }
 
-// Per-block metadata of a workgroup: its rows' segment bounds relative to
-// the start k0 of its run of the stream, and the run's first kEntCap
-// entries as pairs. Entries past kEntCap are restaged in chunks.
+// Per-block metadata of a workgroup of ROWS rows: the rows' segment bounds
+// relative to the start k0 of the workgroup's run of the stream, and the
+// run's first kEntCap entries. SPLIT = false: staged as pairs (offset0,
+// offset1, value0, value1); SPLIT = true: as an array of offsets followed by
+// an array of values (kEntCap + 2 each). Longer runs are restaged in chunks.
+template <int ROWS, bool SPLIT>
 struct RowsMeta {
-  int seg;     // thread tid <= rows: bound of row tid
+  int seg;     // thread tid <= ROWS: bound of row tid
   int4 pair;   // thread tid <= kEntCap / 2: pair tid of the run
   int k0;      // uniform
   __device__ __forceinline__ void load(const int2* __restrict__ stream,
@@ -789,18 +756,29 @@ struct RowsMeta {
     const int32_t* pb = ptr + static_cast<int64_t>(b) * ptr_stride + rg0;
     const int p0 = pb[0];
     k0 = base[b] + p0;
-    const int cnt = pb[kRW * kRR] - p0;
+    const int cnt = pb[ROWS] - p0;
     const int tid = threadIdx.x;
-    seg = tid <= kRW * kRR ? pb[tid] - p0 : 0;
-    // the stream is padded past its end, so a pair may straddle the run's end
+    seg = tid <= ROWS ? pb[tid] - p0 : 0;
+    // the stream is padded past its end, so a pair may straddle the run's
+    // end; pair kEntCap / 2 (read past the staged run, never used) is zero
     pair = 2 * tid < cnt && tid < kEntCap / 2
                ? *reinterpret_cast<const int4*>(stream + k0 + 2 * tid)
-               : make_int4(0, 0, 0, 0);   // pair kEntCap / 2 (read, never used) is zero
+               : make_int4(0, 0, 0, 0);
   }
   __device__ __forceinline__ void store(int* segs, int4* pairs) const {
     const int tid = threadIdx.x;
-    if (tid <= kRW * kRR) segs[tid] = seg;
-    if (tid < kEntCap / 2 + 1) pairs[tid] = make_int4(pair.x, pair.z, pair.y, pair.w);
+    if (tid <= ROWS) segs[tid] = seg;
+    if (tid < kEntCap / 2 + 1) store_pair(pairs, tid, pair);
+  }
+  static __device__ __forceinline__ void store_pair(int4* pairs, int t, const int4& e) {
+    if constexpr (SPLIT) {
+      int* offs = reinterpret_cast<int*>(pairs);
+      int* vals = offs + kEntCap + 2;
+      *reinterpret_cast<int2*>(offs + 2 * t) = make_int2(e.x, e.z);
+      *reinterpret_cast<int2*>(vals + 2 * t) = make_int2(e.y, e.w);
+    } else {
+      pairs[t] = make_int4(e.x, e.z, e.y, e.w);
+    }
   }
 };
 
@@ -825,7 +803,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
     for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
 
   StageRows<SrcT, VEC_OK> pf;
-  RowsMeta meta;
+  RowsMeta<kRW * kRR, false> meta;
   meta.load(stream, ptr, base, ptr_stride, rg0, 0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -864,7 +842,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
       if (t < kEntCap / 2) {
         const int4 e = c0 + t < run ? *reinterpret_cast<const int4*>(stream + k0 + 2 * (c0 + t))
                                     : make_int4(0, 0, 0, 0);
-        pairs[buf][t] = make_int4(e.x, e.z, e.y, e.w);
+        RowsMeta<kRW * kRR, false>::store_pair(pairs[buf], t, e);
       }
       __syncthreads();
       rows_pairs(acc, sg, c0, sb, pairs[buf], [] {});
@@ -901,6 +879,240 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
       }
     }
   }
+}
+
+// ------------------------------------------------------------ rows with dc
+// Backward through the columns of F with the dc partials. Rows are the
+// columns j of F (outputs dz[:, j]), the source is dy; a wave owns 8 rows and
+// also holds z[t, j] of its rows for its 4 tokens. Per entry (row i of F,
+// value c, column j): dz[t, j] += c * dy[t, i] (4 FMAs) and the entry's
+// partial of dc over the tile's 256 tokens, sum_t dy[t, i] z[t, j]: a 4-term
+// dot per lane, summed across the wave by DPP into lane 63, which stores it
+// at the entry's stream position. Entries go one at a time (no padding); the
+// next entry's offset is read while this entry's LDS read is in flight and
+// its value after this entry's FMAs.
+
+__device__ __forceinline__ float wave_total_lane63(float v) {
+  v += dpp_row_shr<1>(v);
+  v += dpp_row_shr<2>(v);
+  v += dpp_row_shr<4>(v);
+  v += dpp_row_shr<8>(v);   // lane 15 of each row of 16: the row's sum
+  // row_bcast:15 then row_bcast:31 on every row: lane 63 gathers rows 0-2
+  // (the other lanes end with partial sums that are not used)
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xF, 0xF, true));
+  return v;   // lane 63: the sum over all 64 lanes
+}
+
+// Entries are taken two at a time in stream order: a pair inside row RA, or
+// straddling from RA into the next row RB (RA's last entry and RB's first).
+// (off, val) hold the pair's offsets and values; the next pair's offsets are
+// read while this pair's LDS reads are in flight and its values after the
+// FMAs. Lane 63 stores the two dc partials.
+template <int RA, int RB>
+__device__ __forceinline__ void dc_pair(float (&acc)[kRRdc][4], const float (&zr)[kRRdc][4],
+                                        const char* sb, const int* offs, const int* vals, int j,
+                                        int2& off, int2& val, float* __restrict__ prow, int i,
+                                        int lane) {
+  const float4 z0 = lds4(sb, off.x);
+  const float4 z1 = lds4(sb, off.y);
+  off = make_int2(offs[j + 2], offs[j + 3]);
+  asm volatile("" ::: "memory");
+  fma4(acc[RA], __int_as_float(val.x), z0);
+  fma4(acc[RB], __int_as_float(val.y), z1);
+  val = make_int2(vals[j + 2], vals[j + 3]);
+  asm volatile("" ::: "memory");
+  float d0 = z0.x * zr[RA][0], d1 = z1.x * zr[RB][0];
+  d0 = fmaf(z0.y, zr[RA][1], d0);
+  d1 = fmaf(z1.y, zr[RB][1], d1);
+  d0 = fmaf(z0.z, zr[RA][2], d0);
+  d1 = fmaf(z1.z, zr[RB][2], d1);
+  d0 = fmaf(z0.w, zr[RA][3], d0);
+  d1 = fmaf(z1.w, zr[RB][3], d1);
+  d0 = wave_total_lane63(d0);
+  d1 = wave_total_lane63(d1);
+  if (lane == 63) {
+    prow[i] = d0;
+    prow[i + 1] = d1;
+  }
+}
+
+// One entry of row RA (its row's last, with no next row to pair with).
+template <int RA>
+__device__ __forceinline__ void dc_single(float (&acc)[kRRdc][4], const float (&zr)[kRRdc][4],
+                                          const char* sb, const int* offs, const int* vals, int j,
+                                          int2& off, int2& val, float* __restrict__ prow, int i,
+                                          int lane) {
+  const float4 z0 = lds4(sb, off.x);
+  off = make_int2(offs[j + 1], offs[j + 2]);
+  asm volatile("" ::: "memory");
+  fma4(acc[RA], __int_as_float(val.x), z0);
+  val = make_int2(vals[j + 1], vals[j + 2]);
+  asm volatile("" ::: "memory");
+  float d0 = z0.x * zr[RA][0];
+  d0 = fmaf(z0.y, zr[RA][1], d0);
+  d0 = fmaf(z0.z, zr[RA][2], d0);
+  d0 = fmaf(z0.w, zr[RA][3], d0);
+  d0 = wave_total_lane63(d0);
+  if (lane == 63) prow[i] = d0;
+}
+
+// The wave's rows in one block: row r owns entries [sg[r], sg[r+1]) of the
+// workgroup's run, of which [c0, c0 + kEntCap) are staged (offs, vals).
+template <typename Mid>
+__device__ __forceinline__ void rows_entries_dc(float (&acc)[kRRdc][4],
+                                                const float (&zr)[kRRdc][4],
+                                                const int (&sg)[kRRdc + 1], int c0,
+                                                const char* sb, const int4* staged,
+                                                float* __restrict__ prow, int lane, Mid mid) {
+  const int c1 = c0 + kEntCap;
+  const int* offs = reinterpret_cast<const int*>(staged) - c0;
+  const int* vals = reinterpret_cast<const int*>(staged) + kEntCap + 2 - c0;
+  auto clampc = [&](int v) { return v < c0 ? c0 : (v > c1 ? c1 : v); };
+  int i = clampc(sg[0]);
+  int2 off = make_int2(offs[i], offs[i + 1]);
+  int2 val = make_int2(vals[i], vals[i + 1]);
+  asm volatile("" ::: "memory");
+  static_for<0, kRRdc>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    const int hi = clampc(sg[r + 1]);
+    for (; i + 1 < hi; i += 2) dc_pair<r, r>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+    if (i < hi) {
+      bool paired = false;
+      if constexpr (r + 1 < kRRdc) {
+        if (i + 1 < clampc(sg[r + 2])) {   // row r+1 is not empty: pair across
+          dc_pair<r, r + 1>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+          i += 2;
+          paired = true;
+        }
+      }
+      if (!paired) {
+        dc_single<r>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+        i += 1;
+      }
+    }
+    if (r == kRRdc / 2 - 1) mid();
+  });
+}
+
+template <typename SrcT, bool VEC_OK>
+__global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
+    const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
+    int ptr_stride, int nblk, float* __restrict__ out, const float* __restrict__ zsrc,
+    float* __restrict__ partial) {
+  __shared__ float stage[2][kRJB * kRT];
+  __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + the entries read past the end
+  __shared__ int segs[2][kRW * kRRdc + 1];
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kRT;
+  const int rg0 = static_cast<int>(blockIdx.y) * (kRW * kRRdc);
+  const int row0 = rg0 + w * kRRdc;
+
+  float acc[kRRdc][4], zr[kRRdc][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * lane + q;
+#pragma unroll
+    for (int r = 0; r < kRRdc; ++r) {
+      acc[r][q] = 0.f;
+      zr[r][q] = (t < T && row0 + r < n_out) ? zsrc[t * n_out + row0 + r] : 0.f;
+    }
+  }
+
+  StageRows<SrcT, VEC_OK> pf;
+  RowsMeta<kRW * kRRdc, true> meta;
+  meta.load(stream, ptr, base, ptr_stride, rg0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pf.load(src, T, n_src, t0, 0, h);
+    pf.store(stage[0], T, n_src, t0, 0, h);
+  }
+  meta.store(segs[0], pairs[0]);
+  for (int b = 0; b < nblk; ++b) {
+    __syncthreads();
+    const int k0 = meta.k0;
+    const bool more = b + 1 < nblk;
+    const int nb = b + 1;
+    float* nst = stage[nb & 1];
+    if (more) {
+      pf.load(src, T, n_src, t0, nb, 0);
+      meta.load(stream, ptr, base, ptr_stride, rg0, nb);
+    }
+    const int buf = b & 1;
+    int sg[kRRdc + 1];
+#pragma unroll
+    for (int r = 0; r <= kRRdc; ++r) sg[r] = uniform(segs[buf][w * kRRdc + r]);
+    const char* sb = reinterpret_cast<const char*>(stage[buf]) + lane * 16;
+    float* prow = partial + tile * nnz + k0;
+    auto mid = [&]() {
+      if (more) {
+        pf.store(nst, T, n_src, t0, nb, 0);
+        pf.load(src, T, n_src, t0, nb, 1);
+      }
+    };
+    const int run = uniform(segs[buf][kRW * kRRdc]);
+    rows_entries_dc(acc, zr, sg, 0, sb, pairs[buf], prow, lane, mid);
+    for (int c0 = kEntCap; c0 < run; c0 += kEntCap) {
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < kEntCap / 2 + 1) {
+        const int4 e = t < kEntCap / 2 && c0 + 2 * t < run
+                           ? *reinterpret_cast<const int4*>(stream + k0 + c0 + 2 * t)
+                           : make_int4(0, 0, 0, 0);
+        RowsMeta<kRW * kRRdc, true>::store_pair(pairs[buf], t, e);
+      }
+      __syncthreads();
+      rows_entries_dc(acc, zr, sg, c0, sb, pairs[buf], prow, lane, [] {});
+    }
+    if (more) {
+      pf.store(nst, T, n_src, t0, nb, 1);
+      meta.store(segs[nb & 1], pairs[nb & 1]);
+    }
+  }
+
+  // epilogue: dz rows row0 .. row0+7 of the lane's 4 tokens
+  const bool vec = row0 + kRRdc <= n_out && n_out % 4 == 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * lane + q;
+    if (t >= T) continue;
+    float* dst = out + t * n_out;
+    if (vec) {
+      float4* d = reinterpret_cast<float4*>(dst + row0);
+      d[0] = make_float4(acc[0][q], acc[1][q], acc[2][q], acc[3][q]);
+      d[1] = make_float4(acc[4][q], acc[5][q], acc[6][q], acc[7][q]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kRRdc; ++r)
+        if (row0 + r < n_out) dst[row0 + r] = acc[r][q];
+    }
+  }
+}
+
+template <typename SrcT>
+static hipError_t rows_dc_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
+                            int n_out, const SpmmPlan& pl, void* out, const float* zsrc,
+                            float* partial, hipStream_t s) {
+  const int gy = (n_out + pl.rows_wg - 1) / pl.rows_wg;
+  void* pp = const_cast<void*>(prep);
+  const PrepLayout l = prep_layout(nnz, n_out, pl);
+  const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
+  constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
+  const bool vec_ok = (n_src % VEC) == 0 && n_src >= VEC;
+  if (vec_ok)
+    hipLaunchKernelGGL((rows_dc_kernel<SrcT, true>), grid, dim3(kRW * 64), 0, s,
+                       static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
+                       at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
+                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial);
+  else
+    hipLaunchKernelGGL((rows_dc_kernel<SrcT, false>), grid, dim3(kRW * 64), 0, s,
+                       static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
+                       at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
+                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial);
+  return hipGetLastError();
 }
 
 template <typename SrcT, typename OutT>
@@ -973,6 +1185,12 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
                        Dt out_dt, int accumulate, const float* zsrc, float* partial,
                        hipStream_t s) {
   if (pl.ntiles == 0) return hipSuccess;
+  if (pl.kind == 2) {
+    if (partial == nullptr || out_dt != Dt::F32) return hipErrorInvalidValue;
+    return src_dt == Dt::F32
+               ? rows_dc_t<float>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s)
+               : rows_dc_t<uint16_t>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s);
+  }
   if (partial != nullptr) {
     if (out_dt != Dt::F32) return hipErrorInvalidValue;
     return src_dt == Dt::F32
