@@ -26,6 +26,17 @@ __device__ __forceinline__ int block_sum_i32(int v, int* red, int parity) {
   return t;
 }
 
+// Sum over the block of a wave-uniform value (lane 0 of each wave posts it).
+__device__ __forceinline__ int block_total_i32(int v, int* red, int parity) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  if (lane == 0) red[parity * 16 + wid] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < nw; ++i) t += red[parity * 16 + i];
+  return t;
+}
+
 // Exclusive prefix over threads in threadIdx order; *total gets the sum.
 __device__ __forceinline__ int block_excl_scan_i32(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -325,30 +336,49 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     for (int r = 0; r < F::EPT; ++r) key[r] = 0;
   }
 
+  // tau = the k-th largest key: the largest t with count(key >= t) >= k,
+  // found by bisection, first on the top 32 bits of the keys (32-bit
+  // compares), then, only if the top bits leave more than k keys at the
+  // threshold, on the full keys within that 2^32-wide range. Counts go by
+  // wave ballots (one barrier per step); the search stops as soon as the
+  // keys >= lo are exactly k.
   unsigned long long tau = 0;
   int need = 0;      // how many |C| == tau are taken (lowest index first)
   bool all = (k >= F::N), none = (k <= 0);
   int parity = 0;
   if (!all && !none) {
-    unsigned long long lo = 0, hi = 1ull << 63;   // count(>=lo) >= k > count(>=hi)
-    while (hi - lo > 1) {
-      const unsigned long long mid = lo + ((hi - lo) >> 1);
+    auto count_ge32 = [&](unsigned m) {
       int cnt = 0;
-      if (active) {
 #pragma unroll
-        for (int r = 0; r < F::EPT; ++r) cnt += (key[r] >= mid) ? 1 : 0;
-      }
-      cnt = block_sum_i32(cnt, red, parity);
+      for (int r = 0; r < F::EPT; ++r)
+        cnt += __popcll(__ballot(static_cast<unsigned>(key[r] >> 32) >= m));
+      return block_total_i32(cnt, red, parity);
+    };
+    auto count_ge64 = [&](unsigned long long m) {
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) cnt += __popcll(__ballot(key[r] >= m));
+      return block_total_i32(cnt, red, parity);
+    };
+    // count(top32 >= lo32) >= k > count(top32 >= hi32); keys are < 2^63
+    unsigned lo32 = 0, hi32 = 1u << 31;
+    int cnt_lo = F::N;
+    while (hi32 - lo32 > 1 && cnt_lo != k) {
+      const unsigned mid = lo32 + ((hi32 - lo32) >> 1);
+      const int cnt = count_ge32(mid);
       parity ^= 1;
-      if (cnt >= k) lo = mid; else hi = mid;
+      if (cnt >= k) { lo32 = mid; cnt_lo = cnt; } else { hi32 = mid; }
+    }
+    unsigned long long lo = static_cast<unsigned long long>(lo32) << 32;
+    unsigned long long hi = static_cast<unsigned long long>(hi32) << 32;
+    while (hi - lo > 1 && cnt_lo != k) {
+      const unsigned long long mid = lo + ((hi - lo) >> 1);
+      const int cnt = count_ge64(mid);
+      parity ^= 1;
+      if (cnt >= k) { lo = mid; cnt_lo = cnt; } else { hi = mid; }
     }
     tau = lo;
-    int gt = 0;
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < F::EPT; ++r) gt += (key[r] > tau) ? 1 : 0;
-    }
-    gt = block_sum_i32(gt, red, parity);
+    const int gt = count_ge64(tau + 1);
     parity ^= 1;
     need = k - gt;
   }
