@@ -34,7 +34,7 @@ hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const fl
 
 // ---- adapter forward / backward (gather SpMM / SDDMM)
 struct SpmmPlan {
-  int kind;      // 0: 16-lane row groups (dc partials), 1: wave-uniform rows
+  int kind;      // 1: plain gather (entry pairs), 2: with dc partials (single entries)
   int tt;        // tokens per tile
   int jb;        // source columns per staged block
   int rows_wg;   // output rows per workgroup

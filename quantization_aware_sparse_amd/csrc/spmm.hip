@@ -8,28 +8,25 @@
 //                    product at E: only c is trainable, W_Q and H frozen,
 //                    papernotes.org, 损失函数 / 训练策略).
 //
-// One kernel serves both directions: out[t][o] = alpha * sum over the
-// nonzeros (o, col, val) of segment o of val * src[t][col], where the
-// segments are the rows of F (forward; src = z) or its columns (backward;
-// src = dy), optionally with the dc partials.
+// Both directions compute out[t][o] = alpha * sum over the nonzeros
+// (o, col, val) of segment o of val * src[t][col], where the segments are the
+// rows of F (forward; src = z) or its columns (backward; src = dy); the
+// backward kernel also forms the dc partials.
 //
-// Work decomposition (gfx950, wave64). A workgroup of W waves (16, or 8
-// with dc partials) owns a tile of TT = 128 tokens and W * 4 * S output rows. The source is staged through LDS in
-// blocks of JB columns, token-minor (row jj of the staged block holds the
-// 128 tokens of source column jj), double buffered. Each wave is four groups
-// of 16 lanes; a group owns S consecutive output rows and lane gl of a group
-// owns tokens 4gl..4gl+3 and 64+4gl..64+4gl+3, so the group covers the tile and every
-// output row's accumulators for the tile live in registers. A nonzero costs
-// the group's lanes two conflict-free ds_read_b128 (512 contiguous bytes)
-// and eight FMAs each.
+// Work decomposition (gfx950, wave64). A workgroup of 16 waves owns a tile of
+// 256 tokens and a group of output rows (16 per wave, or 8 with dc
+// partials); lane l owns tokens 4l .. 4l+3, so a row's accumulators for the
+// tile live in 4 registers per lane and every row is processed by the whole
+// wave: no divergence between rows. The source is staged through LDS in
+// blocks of 64 columns, token-minor (row jj of the staged block holds the
+// 256 tokens of source column jj), double buffered; a nonzero costs the wave
+// one conflict-free ds_read_b128 (1 KiB) and four FMAs per lane.
 //
 // The nonzeros are re-laid out per call "column-block major": for block b,
-// the segments of all output rows in row order. A group's row segment for a
-// block is then one coalesced 16-entry load (lane gl holds entry gl) and each
-// entry reaches all 16 lanes through a DPP row broadcast. All of a block's
-// entry loads are issued before the next block's staging loads, so waiting
-// for an entry never waits for the staging traffic (vector memory counters
-// drain in issue order).
+// the segments of all output rows in row order, so a workgroup's share of a
+// block is one contiguous run of the stream. It is staged in LDS with the
+// block, and waves read their entries from there (in-order LDS counters let
+// the next entry's read overlap the current one's).
 #include <type_traits>
 
 #include "common.h"
@@ -46,16 +43,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-constexpr int kTT = 128;          // tokens per tile
-constexpr int kWavesFwd = 16;     // waves per workgroup, plain SpMM
-constexpr int kWavesDc = 8;       // waves per workgroup with dc partials
-constexpr int kGroups = 4;        // 16-lane groups per wave
-constexpr int kTPL = 8;           // tokens per lane
-constexpr int kSfwd = 6;          // rows per group, plain SpMM
-constexpr int kSdc = 8;           // rows per group with dc partials
-constexpr int kChunk = 16;        // entries per group load
 constexpr int kPad = 16;          // padding entries after the stream
-constexpr int kHalfTile = kTT * 2;  // bytes of 64 fp32 tokens
 
 // wave-uniform rows (plain SpMM)
 constexpr int kRT = 256;          // tokens per tile: 64 lanes x 4
@@ -64,13 +52,6 @@ constexpr int kRW = 16;           // waves per workgroup
 constexpr int kRR = 16;           // output rows per wave
 constexpr int kRRdc = 8;          // output rows per wave with dc partials
 constexpr int kEntCap = 1536;     // stream entries staged in LDS per block
-
-// Token (within the tile) held in accumulator q of lane gl of a group: lanes
-// take 4 consecutive tokens in each half of the tile, so a wave's
-// ds_read_b128 touches consecutive 16-byte chunks (no bank conflicts).
-__device__ __forceinline__ int lane_token(int gl, int q) {
-  return (q < 4) ? 4 * gl + q : kTT / 2 + 4 * gl + (q - 4);
-}
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
@@ -294,240 +275,10 @@ hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* perm, const in
   return prep_common(col_ptr, E, c, perm, d_in, nnz, pl, prep, s);
 }
 
-// ------------------------------------------------------------ staging
-// Thread -> token tt = tid % 128, column group g = tid / 128; load q covers
-// local columns (q*kColGroups + g)*VEC .. +VEC-1 of the block. Loads are
-// unconditional (addresses clamped into the source) so the compiler can
-// count them; out-of-range elements are zeroed when stored to LDS.
-template <typename SrcT, int JB, bool VEC_OK, int THREADS>
-struct Stage {
-  static constexpr int kColGroups = THREADS / kTT;                  // column groups
-  static constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));   // elements per 16 bytes
-  static constexpr int NL = JB / (kColGroups * VEC);                 // 16-byte loads per thread
-  uint4 raw[NL];
-
-  __device__ __forceinline__ void load(const SrcT* __restrict__ src, int64_t T, int n_src,
-                                       int64_t t0, int b) {
-    const int tt = threadIdx.x & (kTT - 1);
-    const int g = threadIdx.x >> 7;
-    const int64_t t = t0 + tt < T ? t0 + tt : T - 1;
-    const SrcT* row = src + t * n_src;
-#pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int col = b * JB + (q * kColGroups + g) * VEC;
-      if constexpr (VEC_OK) {
-        const int cc = col + VEC <= n_src ? col : n_src - VEC;
-        raw[q] = *reinterpret_cast<const uint4*>(row + cc);
-      } else {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int cc = col + e < n_src ? col + e : n_src - 1;
-          if constexpr (sizeof(SrcT) == 4) {
-            w[e] = __float_as_uint(reinterpret_cast<const float*>(row)[cc]);
-          } else {
-            const uint32_t bits = reinterpret_cast<const uint16_t*>(row)[cc];
-            w[e >> 1] |= bits << (16 * (e & 1));
-          }
-        }
-        raw[q] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(float* __restrict__ st, int64_t T, int n_src, int64_t t0,
-                                        int b) const {
-    const int tt = threadIdx.x & (kTT - 1);
-    const int g = threadIdx.x >> 7;
-    const bool tok_ok = t0 + tt < T;
-#pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int cl = (q * kColGroups + g) * VEC;
-      const int col = b * JB + cl;
-      const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float f;
-        if constexpr (sizeof(SrcT) == 4) f = __uint_as_float(w[e]);
-        else f = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
-        // with VEC_OK a clamped load means the whole group is past the end
-        const bool ok = tok_ok && (VEC_OK ? (col + VEC <= n_src) : (col + e < n_src));
-        st[(cl + e) * kTT + tt] = ok ? f : 0.f;
-      }
-    }
-  }
-};
-
 // ------------------------------------------------------------ helpers
-template <int U>
-__device__ __forceinline__ int row_bcast(int v) {
-  return __builtin_amdgcn_mov_dpp(v, 0x150 + U, 0xF, 0xF, false);  // row_newbcast:U
-}
-
 template <int N>
 __device__ __forceinline__ float dpp_row_shr(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
-}
-
-// inclusive prefix over each 16-lane row: lane 15 ends with the row total
-__device__ __forceinline__ float row16_total(float v) {
-  v += dpp_row_shr<1>(v);
-  v += dpp_row_shr<2>(v);
-  v += dpp_row_shr<4>(v);
-  v += dpp_row_shr<8>(v);
-  return v;
-}
-
-template <int S, bool DC>
-struct Acc {
-  float a[S][kTPL];
-  float z[DC ? S : 1][kTPL];
-};
-
-// Entries u in [U0, U0+4) of a 16-entry chunk (lane gl of the group holds
-// entry gl); groups with fewer than u+1 entries are masked off.
-// PADDED: the segment length is a multiple of 4, so no entry is masked.
-template <int U0, int S, bool DC, bool PADDED>
-__device__ __forceinline__ void quad(Acc<S, DC>& A, int s, const int2& ent, int cnt,
-                                     const char* sb, float* __restrict__ prow, int gl) {
-  float4 v[4][2];
-  int off[4];
-  off[0] = row_bcast<U0 + 0>(ent.x);
-  off[1] = row_bcast<U0 + 1>(ent.x);
-  off[2] = row_bcast<U0 + 2>(ent.x);
-  off[3] = row_bcast<U0 + 3>(ent.x);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (PADDED || U0 + u < cnt) {
-      v[u][0] = *reinterpret_cast<const float4*>(sb + off[u]);
-      v[u][1] = *reinterpret_cast<const float4*>(sb + off[u] + kHalfTile);
-    }
-  }
-  float cv[4];
-  cv[0] = __int_as_float(row_bcast<U0 + 0>(ent.y));
-  cv[1] = __int_as_float(row_bcast<U0 + 1>(ent.y));
-  cv[2] = __int_as_float(row_bcast<U0 + 2>(ent.y));
-  cv[3] = __int_as_float(row_bcast<U0 + 3>(ent.y));
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (PADDED || U0 + u < cnt) {
-      const float x[kTPL] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
-                             v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
-#pragma unroll
-      for (int q = 0; q < kTPL; ++q) A.a[s][q] = fmaf(cv[u], x[q], A.a[s][q]);
-      if constexpr (DC) {
-        float d = x[0] * A.z[s][0];
-#pragma unroll
-        for (int q = 1; q < kTPL; ++q) d = fmaf(x[q], A.z[s][q], d);
-        d = row16_total(d);
-        if (gl == 15) prow[U0 + u] = d;
-      }
-    }
-  }
-}
-
-// One 16-entry chunk of slot s with cnt valid entries (cnt may be <= 0).
-template <int S, bool DC, bool PADDED>
-__device__ __forceinline__ void chunk16(Acc<S, DC>& A, int s, const int2& ent, int cnt,
-                                        const char* sb, float* __restrict__ prow, int gl) {
-  if (cnt > 0) quad<0, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 4) quad<4, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 8) quad<8, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
-  if (cnt > 12) quad<12, S, DC, PADDED>(A, s, ent, cnt, sb, prow, gl);
-}
-
-// ------------------------------------------------------------ main kernel
-template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC, bool PADDED>
-__global__ __launch_bounds__(WAVES * 64) void spmm_kernel(
-    const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
-    const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
-    int ptr_stride, int nblk, float alpha, OutT* __restrict__ out, int accumulate,
-    const float* __restrict__ zsrc, float* __restrict__ partial) {
-  __shared__ float stage[2][JB * kTT];
-  const int lane = threadIdx.x & 63;
-  const int gl = lane & 15;
-  const int g = lane >> 4;
-  const int w = uniform(threadIdx.x >> 6);
-  const int64_t tile = blockIdx.x;
-  const int64_t t0 = tile * kTT;
-  const int rows_wg = WAVES * kGroups * S;
-  const int orow = static_cast<int>(blockIdx.y) * rows_wg + (w * kGroups + g) * S;
-  const int lds_lane = gl * 16;      // lane's first 4 tokens; the other 4 are kHalfTile later
-
-  Acc<S, DC> A;
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int q = 0; q < kTPL; ++q) A.a[s][q] = 0.f;
-  if constexpr (DC) {
-#pragma unroll
-    for (int q = 0; q < kTPL; ++q) {
-      const int64_t t = t0 + lane_token(gl, q);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int o = orow + s;
-        A.z[s][q] = (t < T && o < n_out) ? zsrc[t * n_out + o] : 0.f;
-      }
-    }
-  }
-
-  // Lane gl (<= S) of a group holds the stream start of row orow + gl in
-  // the current block; rows past n_out read the block's end (empty segments).
-  const int rsel = orow + (gl <= S ? gl : S);
-  const int prow_idx = rsel < n_out ? rsel : n_out;
-  int pv = ptr[prow_idx] + base[0];
-
-  Stage<SrcT, JB, VEC_OK, WAVES * 64> pf;
-  pf.load(src, T, n_src, t0, 0);
-  for (int b = 0; b < nblk; ++b) {
-    float* st = stage[b & 1];
-    pf.store(st, T, n_src, t0, b);
-    __syncthreads();
-    // this block's segments: slot s spans [lane s's pv, lane s+1's pv)
-    int2 ent[S];
-    static_for<0, S>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      ent[s] = stream[row_bcast<s>(pv) + gl];
-    });
-    // next block's segment starts, then the next block's staging loads
-    // (issued after every entry load of this block)
-    const int pvb = pv;
-    const int bn = b + 1 < nblk ? b + 1 : b;
-    pv = ptr[static_cast<int64_t>(bn) * ptr_stride + prow_idx] + base[bn];
-    pf.load(src, T, n_src, t0, bn);
-
-    const char* sb = reinterpret_cast<const char*>(st) + lds_lane;
-    static_for<0, S>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      // slot s spans [lane s's start, lane s+1's start) of the block's stream
-      const int k0 = row_bcast<s>(pvb);
-      const int cnt = row_bcast<s + 1>(pvb) - k0;
-      float* prow = DC ? partial + tile * nnz + k0 : nullptr;
-      chunk16<S, DC, PADDED>(A, s, ent[s], cnt, sb, prow, gl);
-      // segments longer than one chunk: further 16-entry rounds
-      for (int kk = kChunk; kk < cnt; kk += kChunk) {
-        const int2 e2 = stream[k0 + kk + gl];
-        chunk16<S, DC, PADDED>(A, s, e2, cnt - kk, sb, DC ? prow + kk : nullptr, gl);
-      }
-    });
-  }
-
-  // epilogue: lane writes rows orow .. orow+S-1 (contiguous) of its 8 tokens
-#pragma unroll
-  for (int q = 0; q < kTPL; ++q) {
-    const int64_t t = t0 + lane_token(gl, q);
-    if (t >= T) continue;
-    OutT* dst = out + t * n_out;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int o = orow + s;
-      if (o < n_out) {
-        float val = alpha * A.a[s][q];
-        if (accumulate) val += Elem<OutT>::ld(dst, o);
-        Elem<OutT>::st(dst, o, val);
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------ wave-uniform rows
@@ -649,57 +400,6 @@ __device__ __forceinline__ void fma4(float (&a)[4], float v, const float4& z) {
 // entries 2, 3 as (LDS byte offset, value bits) pairs.
 __device__ __forceinline__ float4 lds4(const char* sb, int off) {
   return *reinterpret_cast<const float4*>(sb + off);
-}
-
-template <int N>
-__device__ __forceinline__ void grp_read(float4 (&z)[4], const char* sb, const int4& ea,
-                                         const int4& eb) {
-  z[0] = lds4(sb, ea.x);
-  if constexpr (N > 1) z[1] = lds4(sb, ea.z);
-  if constexpr (N > 2) z[2] = lds4(sb, eb.x);
-  if constexpr (N > 3) z[3] = lds4(sb, eb.z);
-}
-
-template <int N>
-__device__ __forceinline__ void grp_fma(float (&a)[4], const float4 (&z)[4], const int4& ea,
-                                        const int4& eb) {
-  fma4(a, __int_as_float(ea.y), z[0]);
-  if constexpr (N > 1) fma4(a, __int_as_float(ea.w), z[1]);
-  if constexpr (N > 2) fma4(a, __int_as_float(eb.y), z[2]);
-  if constexpr (N > 3) fma4(a, __int_as_float(eb.w), z[3]);
-}
-
-// entries k .. k+3 (the stream is padded, so reading past a segment is safe)
-__device__ __forceinline__ void grp_load(const int2* __restrict__ stream, int k, int4& ea,
-                                         int4& eb) {
-  ea = *reinterpret_cast<const int4*>(stream + k);
-  eb = *reinterpret_cast<const int4*>(stream + k + 2);
-}
-
-// Marks the pair's four words as used here: the scalar load stays whole and
-// is waited for at this point, not earlier.
-__device__ __forceinline__ void pair_pin(int4& e) {
-  asm volatile("" : "+s"(e.x), "+s"(e.y), "+s"(e.z), "+s"(e.w));
-}
-
-// Marks all eight words as used here, so the compiler keeps the group's
-// scalar load whole and waits for it at this point, not earlier.
-__device__ __forceinline__ void grp_pin(int4& ea, int4& eb) {
-  asm volatile("" : "+s"(ea.x), "+s"(ea.y), "+s"(ea.z), "+s"(ea.w), "+s"(eb.x), "+s"(eb.y),
-               "+s"(eb.z), "+s"(eb.w));
-}
-
-// N entries of (ea, eb): LDS reads, then the load of the group at `nxt`
-// into (na, nb), then the FMAs.
-template <int N>
-__device__ __forceinline__ void grp_step(float (&a)[4], const char* sb, const int4& ea,
-                                         const int4& eb, const int2* __restrict__ stream, int nxt,
-                                         int4& na, int4& nb) {
-  float4 z[4];
-  grp_read<N>(z, sb, ea, eb);
-  grp_load(stream, nxt, na, nb);
-  grp_fma<N>(a, z, ea, eb);
-  grp_pin(na, nb);
 }
 
 // The wave's rows in one block: row r owns pairs [sg[r], sg[r+1]) of the
@@ -1138,86 +838,27 @@ static hipError_t rows_t(const void* src, int64_t T, int n_src, const void* prep
   return hipGetLastError();
 }
 
-template <int WAVES, int S, int JB, bool VEC_OK, typename SrcT, typename OutT, bool DC>
-static hipError_t spmm_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
-                         int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
-                         const float* zsrc, float* partial, hipStream_t s) {
-  constexpr int rows_wg = WAVES * kGroups * S;
-  const int gy = (n_out + rows_wg - 1) / rows_wg;
-  void* pp = const_cast<void*>(prep);
-  const PrepLayout l = prep_layout(nnz, n_out, pl);
-  const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
-  if (pl.seg_mult == 4)
-    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, !DC>), grid,
-                       dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
-                       at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
-                       nnz, n_out, pl.ptr_stride, pl.nblk, alpha, static_cast<OutT*>(out), acc,
-                       zsrc, partial);
-  else
-    hipLaunchKernelGGL((spmm_kernel<WAVES, S, JB, VEC_OK, SrcT, OutT, DC, false>), grid,
-                       dim3(WAVES * 64), 0, s, static_cast<const SrcT*>(src), T, n_src,
-                       at<int2>(pp, l.stream), at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base),
-                       nnz, n_out, pl.ptr_stride, pl.nblk, alpha, static_cast<OutT*>(out), acc,
-                       zsrc, partial);
-  return hipGetLastError();
-}
-
-template <int WAVES, int S, typename SrcT, typename OutT, bool DC>
-static hipError_t spmm_jb(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
-                          int n_out, const SpmmPlan& pl, float alpha, void* out, int acc,
-                          const float* zsrc, float* partial, hipStream_t s) {
-  constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
-  const bool vec_ok = n_src % VEC == 0 && n_src >= VEC;
-  if (pl.jb == 128) {
-    return vec_ok ? spmm_t<WAVES, S, 128, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
-                                                         out, acc, zsrc, partial, s)
-                  : spmm_t<WAVES, S, 128, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl,
-                                                          alpha, out, acc, zsrc, partial, s);
-  }
-  return vec_ok ? spmm_t<WAVES, S, 64, true, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
-                                                      out, acc, zsrc, partial, s)
-                : spmm_t<WAVES, S, 64, false, SrcT, OutT, DC>(src, T, n_src, prep, nnz, n_out, pl, alpha,
-                                                       out, acc, zsrc, partial, s);
-}
-
 hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const void* prep,
                        int64_t nnz, int n_out, const SpmmPlan& pl, float alpha, void* out,
                        Dt out_dt, int accumulate, const float* zsrc, float* partial,
                        hipStream_t s) {
   if (pl.ntiles == 0) return hipSuccess;
   if (pl.kind == 2) {
-    if (partial == nullptr || out_dt != Dt::F32) return hipErrorInvalidValue;
+    // dz (unscaled, overwritten) and the dc partials
+    if (partial == nullptr || zsrc == nullptr || out_dt != Dt::F32 || accumulate ||
+        alpha != 1.0f)
+      return hipErrorInvalidValue;
     return src_dt == Dt::F32
                ? rows_dc_t<float>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s)
                : rows_dc_t<uint16_t>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s);
   }
-  if (partial != nullptr) {
-    if (out_dt != Dt::F32) return hipErrorInvalidValue;
-    return src_dt == Dt::F32
-               ? spmm_jb<kWavesDc, kSdc, float, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                   accumulate, zsrc, partial, s)
-               : spmm_jb<kWavesDc, kSdc, uint16_t, float, true>(src, T, n_src, prep, nnz, n_out, pl, alpha,
-                                                      out, accumulate, zsrc, partial, s);
-  }
-  if (pl.kind == 1) {
-    if (src_dt == Dt::F32 && out_dt == Dt::F32)
-      return rows_t<float, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate, s);
-    if (src_dt == Dt::F32 && out_dt == Dt::BF16)
-      return rows_t<float, uint16_t>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate,
-                                     s);
-    if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-      return rows_t<uint16_t, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate,
-                                     s);
-    return hipErrorInvalidValue;
-  }
-  // 16-lane row groups without dc partials (the backward's dz when dc is
-  // not requested uses the dc plan)
+  if (partial != nullptr) return hipErrorInvalidValue;
   if (src_dt == Dt::F32 && out_dt == Dt::F32)
-    return spmm_jb<kWavesFwd, kSfwd, float, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                               accumulate, nullptr, nullptr, s);
+    return rows_t<float, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate, s);
+  if (src_dt == Dt::F32 && out_dt == Dt::BF16)
+    return rows_t<float, uint16_t>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate, s);
   if (src_dt == Dt::BF16 && out_dt == Dt::F32)
-    return spmm_jb<kWavesFwd, kSfwd, uint16_t, float, false>(src, T, n_src, prep, nnz, n_out, pl, alpha, out,
-                                                  accumulate, nullptr, nullptr, s);
+    return rows_t<uint16_t, float>(src, T, n_src, prep, nnz, n_out, pl, alpha, out, accumulate, s);
   return hipErrorInvalidValue;
 }
 
