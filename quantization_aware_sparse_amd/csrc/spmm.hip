@@ -405,35 +405,27 @@ __device__ __forceinline__ float4 lds4(const char* sb, int off) {
 // The wave's rows in one block: row r owns pairs [sg[r], sg[r+1]) of the
 // workgroup's run (segments are padded to even lengths), of which pairs
 // [c0, c0 + kEntCap / 2) are staged in pp as (offset0, offset1, value0,
-// value1). The wave walks its pairs in order across its rows: a step reads
-// the next pair's offsets while its own z reads are in flight and the next
-// pair's values after its FMAs, so nothing is copied and a row's first pair
-// is already in registers when the row starts. mid() runs once, after half
-// the rows.
+// value1). The wave walks its pairs in order across its rows, reading the
+// next pair while the current pair's z reads are in flight, so a row's first
+// pair is already in registers when the row starts. mid() runs once, after
+// half the rows.
 template <typename Mid>
 __device__ __forceinline__ void rows_pairs(float (&acc)[kRR][4], const int (&sg)[kRR + 1],
                                            int c0, const char* sb, const int4* pp, Mid mid) {
   const int c1 = c0 + kEntCap / 2;
-  const int* pw = reinterpret_cast<const int*>(pp) - 4 * c0;
-  auto off_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i); };
-  auto val_at = [&](int i) { return *reinterpret_cast<const int2*>(pw + 4 * i + 2); };
+  const int4* pc = pp - c0;
   auto clampc = [&](int v) { return v < c0 ? c0 : (v > c1 ? c1 : v); };
-  const int i0 = clampc(sg[0]);
-  int2 off = off_at(i0);
-  int2 val = val_at(i0);
-  asm volatile("" ::: "memory");
+  int4 cur = pc[clampc(sg[0])];
 #pragma unroll
   for (int r = 0; r < kRR; ++r) {
     const int hi = clampc(sg[r + 1]);
     for (int i = clampc(sg[r]); i < hi; ++i) {
-      const float4 z0 = lds4(sb, off.x);
-      const float4 z1 = lds4(sb, off.y);
-      off = off_at(i + 1);
-      asm volatile("" ::: "memory");
-      fma4(acc[r], __int_as_float(val.x), z0);
-      fma4(acc[r], __int_as_float(val.y), z1);
-      val = val_at(i + 1);
-      asm volatile("" ::: "memory");
+      const int4 nx = pc[i + 1];
+      const float4 z0 = lds4(sb, cur.x);
+      const float4 z1 = lds4(sb, cur.y);
+      fma4(acc[r], __int_as_float(cur.z), z0);
+      fma4(acc[r], __int_as_float(cur.w), z1);
+      cur = nx;
     }
     if (r == kRR / 2 - 1) mid();
   }
