@@ -52,6 +52,7 @@ constexpr int kRW = 16;           // waves per workgroup
 constexpr int kRR = 16;           // output rows per wave
 constexpr int kRRdc = 8;          // output rows per wave with dc partials
 constexpr int kEntCap = 1536;     // stream entries staged in LDS per block
+constexpr int kMaxBlk = 256;      // blocks held in a workgroup's run table
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
@@ -441,14 +442,36 @@ struct RowsMeta {
   int seg;     // thread tid <= ROWS: bound of row tid
   int4 pair;   // thread tid <= kEntCap / 2: pair tid of the run
   int k0;      // uniform
+  // Run table of a workgroup, one int4 per block: (k0, the block-local
+  // start p0, the run length). Built once per workgroup so that a block's
+  // staging waits for one table read, not a chain of scalar loads.
+  static __device__ __forceinline__ void build_runs(int4* runs, const int32_t* __restrict__ ptr,
+                                                    const int32_t* __restrict__ base,
+                                                    int ptr_stride, int rg0, int nblk) {
+    for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
+      const int32_t* pb = ptr + static_cast<int64_t>(b) * ptr_stride + rg0;
+      const int p0 = pb[0];
+      runs[b] = make_int4(base[b] + p0, p0, pb[ROWS] - p0, 0);
+    }
+  }
+  // with_table: the run table holds every block (nblk <= kMaxBlk); else the
+  // run is read from ptr / base directly.
   __device__ __forceinline__ void load(const int2* __restrict__ stream,
                                        const int32_t* __restrict__ ptr,
-                                       const int32_t* __restrict__ base, int ptr_stride, int rg0,
-                                       int b) {
+                                       const int32_t* __restrict__ base, const int4* runs,
+                                       bool with_table, int ptr_stride, int rg0, int b) {
     const int32_t* pb = ptr + static_cast<int64_t>(b) * ptr_stride + rg0;
-    const int p0 = pb[0];
-    k0 = base[b] + p0;
-    const int cnt = pb[ROWS] - p0;
+    int p0, cnt;
+    if (with_table) {
+      const int4 rb = runs[b];
+      k0 = uniform(rb.x);
+      p0 = rb.y;
+      cnt = rb.z;
+    } else {
+      p0 = pb[0];
+      k0 = base[b] + p0;
+      cnt = pb[ROWS] - p0;
+    }
     const int tid = threadIdx.x;
     seg = tid <= ROWS ? pb[tid] - p0 : 0;
     // the stream is padded past its end, so a pair may straddle the run's
@@ -482,6 +505,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
   __shared__ float stage[2][kRJB * kRT];
   __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + entries read past the end
   __shared__ int segs[2][kRW * kRR + 1];
+  __shared__ int4 runs[kMaxBlk];
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
@@ -496,7 +520,10 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
 
   StageRows<SrcT, VEC_OK> pf;
   RowsMeta<kRW * kRR, false> meta;
-  meta.load(stream, ptr, base, ptr_stride, rg0, 0);
+  const bool tab = nblk <= kMaxBlk;
+  if (tab) RowsMeta<kRW * kRR, false>::build_runs(runs, ptr, base, ptr_stride, rg0, nblk);
+  __syncthreads();
+  meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     pf.load(src, T, n_src, t0, 0, h);
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
     float* nst = stage[nb & 1];
     if (more) {
       pf.load(src, T, n_src, t0, nb, 0);
-      meta.load(stream, ptr, base, ptr_stride, rg0, nb);
+      meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb);
     }
     const int buf = b & 1;
     int sg[kRR + 1];
@@ -696,6 +723,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
   __shared__ float stage[2][kRJB * kRT];
   __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + the entries read past the end
   __shared__ int segs[2][kRW * kRRdc + 1];
+  __shared__ int4 runs[kMaxBlk];
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int64_t tile = blockIdx.x;
@@ -716,7 +744,10 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
 
   StageRows<SrcT, VEC_OK> pf;
   RowsMeta<kRW * kRRdc, true> meta;
-  meta.load(stream, ptr, base, ptr_stride, rg0, 0);
+  const bool tab = nblk <= kMaxBlk;
+  if (tab) RowsMeta<kRW * kRRdc, true>::build_runs(runs, ptr, base, ptr_stride, rg0, nblk);
+  __syncthreads();
+  meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     pf.load(src, T, n_src, t0, 0, h);
@@ -731,7 +762,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     float* nst = stage[nb & 1];
     if (more) {
       pf.load(src, T, n_src, t0, nb, 0);
-      meta.load(stream, ptr, base, ptr_stride, rg0, nb);
+      meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb);
     }
     const int buf = b & 1;
     int sg[kRRdc + 1];

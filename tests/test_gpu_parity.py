@@ -203,7 +203,11 @@ def _dev_adapter(r):
 
 @pytest.mark.parametrize("d_out,d_in,p,T", [
     (256, 256, 2048, 64), (300, 64, 2500, 77), (37, 2, 74, 130), (513, 128, 4000, 129),
-    (64, 1024, 6000, 200), (40, 8192, 2000, 9), (3, 16384, 300, 5), (1100, 32, 3300, 1)])
+    (64, 1024, 6000, 200), (40, 8192, 2000, 9), (3, 16384, 300, 5), (1100, 32, 3300, 1),
+    # one block of 64 rows of F holding more nonzeros than a workgroup stages at once
+    (64, 128, 1920, 40),
+    # more than 256 blocks of 64 rows of F (the backward's per-workgroup run table)
+    (16500, 4, 49500, 70)])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_fwd_bwd_small(q, d_out, d_in, p, T, act):
     say("fwd/bwd small", d_out, d_in, p, T, act)
