@@ -301,11 +301,23 @@ struct StageRows {
   static constexpr int NH = NL / 2;                                  // loads per half
   uint4 raw[NH];
 
+  // Block b lies wholly inside the source and the tile wholly inside T:
+  // no clamping and no zeroing (uniform).
+  static __device__ __forceinline__ bool whole(int64_t T, int n_src, int64_t t0, int b) {
+    return VEC_OK && t0 + kRT <= T && (b + 1) * kRJB <= n_src;
+  }
+
   // half h covers the thread's columns g*16 + h*8 .. +7
   __device__ __forceinline__ void load(const SrcT* __restrict__ src, int64_t T, int n_src,
                                        int64_t t0, int b, int h) {
     const int tt = threadIdx.x & (kRT - 1);
     const int g = threadIdx.x / kRT;
+    if (whole(T, n_src, t0, b)) {
+      const SrcT* row = src + (t0 + tt) * n_src + b * kRJB + g * 16 + h * 8;
+#pragma unroll
+      for (int q = 0; q < NH; ++q) raw[q] = *reinterpret_cast<const uint4*>(row + q * VEC);
+      return;
+    }
     const int64_t t = t0 + tt < T ? t0 + tt : T - 1;
     const SrcT* row = src + t * n_src;
 #pragma unroll
@@ -331,10 +343,25 @@ struct StageRows {
     }
   }
 
+  static __device__ __forceinline__ float elem(const uint32_t (&w)[4], int e) {
+    if constexpr (sizeof(SrcT) == 4) return __uint_as_float(w[e]);
+    else return (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+  }
+
   __device__ __forceinline__ void store(float* __restrict__ st, int64_t T, int n_src, int64_t t0,
                                         int b, int h) const {
     const int tt = threadIdx.x & (kRT - 1);
     const int g = threadIdx.x / kRT;
+    if (whole(T, n_src, t0, b)) {
+#pragma unroll
+      for (int q = 0; q < NH; ++q) {
+        const int cl = g * 16 + h * 8 + q * VEC;
+        const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st[(cl + e) * kRT + tt] = elem(w, e);
+      }
+      return;
+    }
     const bool tok_ok = t0 + tt < T;
 #pragma unroll
     for (int q = 0; q < NH; ++q) {
@@ -343,11 +370,8 @@ struct StageRows {
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        float f;
-        if constexpr (sizeof(SrcT) == 4) f = __uint_as_float(w[e]);
-        else f = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
         const bool ok = tok_ok && (VEC_OK ? (col + VEC <= n_src) : (col + e < n_src));
-        st[(cl + e) * kRT + tt] = ok ? f : 0.f;
+        st[(cl + e) * kRT + tt] = ok ? elem(w, e) : 0.f;
       }
     }
   }
