@@ -123,6 +123,7 @@ __device__ __forceinline__ int seg_key(const int32_t* E, const int32_t* perm, in
 }
 
 // bptr[o][b] = first position of segment o whose column is >= b*JB
+// (b = 0 .. nblk; bptr[o][nblk] is the segment's end)
 __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ E,
                             const int32_t* __restrict__ perm, int n_out, int nblk, int jb,
                             int32_t* __restrict__ bptr) {
@@ -141,8 +142,9 @@ __global__ void bptr_kernel(const int32_t* __restrict__ seg_ptr, const int32_t* 
 }
 
 // Per block b: ptr[b][o] = entries of block b in rows before o (exclusive
-// scan over rows), ptr[b][n_out] and base[b] = the block's total.
-// Rows n_out .. stride-2 (padding up to a whole workgroup of rows) are empty.
+// scan over rows of the counts padded to a multiple of mult), ptr[b][n_rows]
+// and base[b] = the block's total. Rows n_out .. stride-2 (padding up to a
+// whole workgroup of rows) are empty.
 __global__ __launch_bounds__(1024) void blk_scan_kernel(const int32_t* __restrict__ bptr,
                                                         int n_out, int stride, int nblk, int mult,
                                                         int32_t* __restrict__ ptr,
@@ -215,37 +217,47 @@ __global__ __launch_bounds__(1024) void blk_base_kernel(int32_t* __restrict__ ba
 // Rows of F: position q = k, row o = E[2k], column E[2k+1], value c[k].
 // Columns of F: position q, row o = E[2 perm[q] + 1] (a column of F),
 // column E[2 perm[q]] (a row of F), value c[perm[q]].
-// korig[pos] keeps the nonzero's index k in E.
+// korig[pos] (if given) keeps the nonzero's index k in E. The last entry of
+// a segment whose padded length exceeds its count writes the zero padding
+// entries (offset 0, value 0, korig -1); thread 0 zeroes the kPad entries
+// past the stream's end.
 __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __restrict__ c,
-                               const int32_t* __restrict__ perm, int64_t nnz, int stride, int nblk,
-                               int jb, int tt, const int32_t* __restrict__ bptr,
+                               const int32_t* __restrict__ perm, int64_t nnz, int stride,
+                               int nblk, int jb, int tt, int mult, const int32_t* __restrict__ bptr,
                                const int32_t* __restrict__ ptr, const int32_t* __restrict__ base,
                                int2* __restrict__ stream, int32_t* __restrict__ korig) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q == 0) {
+    const int64_t end = base[nblk];
+    for (int i = 0; i < kPad; ++i) stream[end + i] = make_int2(0, 0);
+  }
   if (q >= nnz) return;
   const int64_t k = perm ? perm[q] : q;
   const int o = perm ? E[2 * k + 1] : E[2 * k];
   const int col = perm ? E[2 * k] : E[2 * k + 1];
   const int b = col / jb;
   const int64_t r = static_cast<int64_t>(o) * (nblk + 1) + b;
+  const int first = bptr[r];
   const int64_t pos = static_cast<int64_t>(base[b]) +
-                      ptr[static_cast<int64_t>(b) * stride + o] + (q - bptr[r]);
+                      ptr[static_cast<int64_t>(b) * stride + o] + (q - first);
   stream[pos] = make_int2((col - b * jb) * tt * 4, __float_as_int(c[k]));
-  korig[pos] = static_cast<int32_t>(k);
-}
-
-// zero entries everywhere (padding), korig = -1 for them
-__global__ void fill_stream_kernel(int2* __restrict__ stream, int32_t* __restrict__ korig,
-                                   int64_t cap, int64_t n) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (q >= n) return;
-  stream[q] = make_int2(0, 0);
-  if (q < cap) korig[q] = -1;
+  if (korig) korig[pos] = static_cast<int32_t>(k);
+  if (mult > 1) {
+    const int last = bptr[r + 1] - 1;
+    if (q == last) {
+      const int cnt = last + 1 - first;
+      const int pad = (cnt + mult - 1) / mult * mult - cnt;
+      for (int i = 1; i <= pad; ++i) {
+        stream[pos + i] = make_int2(0, 0);
+        if (korig) korig[pos + i] = -1;
+      }
+    }
+  }
 }
 
 static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const float* c,
                               const int32_t* perm, int n_out, int64_t nnz, const SpmmPlan& pl,
-                              void* prep, hipStream_t s) {
+                              bool with_korig, void* prep, hipStream_t s) {
   const PrepLayout l = prep_layout(nnz, n_out, pl);
   int32_t* bptr = at<int32_t>(prep, l.bptr);
   int32_t* ptr = at<int32_t>(prep, l.ptr);
@@ -256,24 +268,23 @@ static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const fl
   hipLaunchKernelGGL(blk_scan_kernel, dim3(pl.nblk), dim3(1024), 0, s, bptr, n_out,
                      pl.ptr_stride, pl.nblk, pl.seg_mult, ptr, base);
   hipLaunchKernelGGL(blk_base_kernel, dim3(1), dim3(1024), 0, s, base, pl.nblk);
-  const int64_t nf = l.cap + kPad;
-  hipLaunchKernelGGL(fill_stream_kernel, dim3(static_cast<unsigned>((nf + 255) / 256)), dim3(256), 0,
-                     s, at<int2>(prep, l.stream), at<int32_t>(prep, l.korig), l.cap, nf);
-  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((nnz + 255) / 256)), dim3(256), 0, s,
-                     E, c, perm, nnz, pl.ptr_stride, pl.nblk, pl.jb, pl.tt, bptr, ptr, base,
-                     at<int2>(prep, l.stream), at<int32_t>(prep, l.korig));
+  const int64_t nthreads = nnz > 0 ? nnz : 1;
+  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
+                     0, s, E, c, perm, nnz, pl.ptr_stride, pl.nblk, pl.jb, pl.tt,
+                     pl.seg_mult, bptr, ptr, base, at<int2>(prep, l.stream),
+                     with_korig ? at<int32_t>(prep, l.korig) : nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_prep_csr(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                            int64_t nnz, const SpmmPlan& pl, void* prep, hipStream_t s) {
-  return prep_common(row_ptr, E, c, nullptr, d_out, nnz, pl, prep, s);
+  return prep_common(row_ptr, E, c, nullptr, d_out, nnz, pl, false, prep, s);
 }
 
 hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* perm, const int32_t* E,
                            const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
                            hipStream_t s) {
-  return prep_common(col_ptr, E, c, perm, d_in, nnz, pl, prep, s);
+  return prep_common(col_ptr, E, c, perm, d_in, nnz, pl, true, prep, s);
 }
 
 // ------------------------------------------------------------ helpers
