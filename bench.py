@@ -256,16 +256,26 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def source_digest():
-    """sha256 over the HIP sources and headers of the library: a traffic
-    figure measured on other sources is stale."""
+# library sources that define each timed kernel (besides the shared headers
+# and the launch layer, which every kernel depends on)
+KERNEL_SOURCES = {
+    "FWD_FWHT": ["fwht.hip", "fwht_core.h"], "BWD_FWHT_X": ["fwht.hip", "fwht_core.h"],
+    "BWD_FWHT_DX": ["fwht.hip", "fwht_core.h"], "FWD_SPMM": ["spmm.hip"],
+    "BWD_SPMM": ["spmm.hip"], "BWD_DC_REDUCE": ["spmm.hip"],
+    "INIT_SELECT": ["init.hip", "fwht_core.h"], "MATERIALIZE": ["materialize.hip", "fwht_core.h"],
+}
+SHARED_SOURCES = ["common.h", "launch.h", "api.hip"]
+
+
+def source_digest(kernel):
+    """sha256 over the HIP sources a kernel is built from: a traffic figure
+    measured on other sources is stale."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantization_aware_sparse_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(set(KERNEL_SOURCES[kernel] + SHARED_SOURCES)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -276,7 +286,7 @@ def measured_traffic(kernel, config):
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.md")
     if not os.path.exists(path):
         return None
-    digest = source_digest()
+    digest = source_digest(kernel)
     with open(path) as f:
         for line in f:
             if line.startswith("traffic:"):

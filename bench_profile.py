@@ -91,7 +91,6 @@ def cmd_traffic(a):
     cname = max(calib, key=lambda n: fetch[n])
     f_fetch = known_kib / fetch[cname]
     f_write = known_kib / write[cname]
-    digest = bench.source_digest()
     lines = []
     table = []
     for name in sorted(set(fetch) & set(write)):
@@ -103,7 +102,8 @@ def cmd_traffic(a):
         table.append(("/".join(kids), short(name), fetch[name], write[name], fb, wb))
         for kid in kids:
             lines.append(f"traffic: kernel={kid} config={a.config} bytes={int(round(fb + wb))} "
-                         f"fetch={int(round(fb))} write={int(round(wb))} sources={digest}")
+                         f"fetch={int(round(fb))} write={int(round(wb))} "
+                         f"sources={bench.source_digest(kid)}")
     with open(a.out, "w") as f:
         f.write(f"# HBM traffic per launch, workload {a.config}\n\n")
         f.write("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc) in two runs, "
@@ -118,7 +118,7 @@ def cmd_traffic(a):
                 "write MB (scaled) |\n|---|---|---|---|---|---|\n")
         for kid, n, fk, wk, fb, wb in table:
             f.write(f"| {kid} | `{n}` | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |\n")
-        f.write("\nMachine-readable lines (sources = digest of the library's HIP sources when "
+        f.write("\nMachine-readable lines (sources = digest of the kernel's HIP sources when "
                 "the counters were taken; bench.py reports traffic only while it matches):\n\n")
         for ln in lines:
             f.write(ln + "\n")

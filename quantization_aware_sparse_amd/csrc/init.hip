@@ -65,12 +65,20 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const float* __restrict_
   const float* src = dWq + static_cast<int64_t>(row) * d_in;
   double acc = 0.0;
   if (d_in >= 4) {
-    for (int j = lane * 4; j < d_in; j += 256) {
-      const float4 f = *reinterpret_cast<const float4*>(src + j);
-      acc += static_cast<double>(f.x) * f.x;
-      acc += static_cast<double>(f.y) * f.y;
-      acc += static_cast<double>(f.z) * f.z;
-      acc += static_cast<double>(f.w) * f.w;
+    // eight 16-byte loads in flight per lane before they are summed
+    for (int j0 = lane * 4; j0 < d_in; j0 += 256 * 8) {
+      float4 f[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        f[u] = j0 + 256 * u < d_in ? *reinterpret_cast<const float4*>(src + j0 + 256 * u)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc += static_cast<double>(f[u].x) * f[u].x;
+        acc += static_cast<double>(f[u].y) * f[u].y;
+        acc += static_cast<double>(f[u].z) * f[u].z;
+        acc += static_cast<double>(f[u].w) * f[u].w;
+      }
     }
   } else {
     for (int j = lane; j < d_in; j += 64) acc += static_cast<double>(src[j]) * src[j];
@@ -449,7 +457,7 @@ hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int3
 // one row are distinct, so a row's entries are placed in parallel).
 constexpr int kCscThreads = 256;
 
-static int csc_chunks(int d_out) { return d_out < 64 ? d_out : 64; }
+static int csc_chunks(int d_out) { return d_out < 256 ? d_out : 256; }
 
 size_t csc_scratch_bytes(int d_out, int d_in) {
   return static_cast<size_t>(csc_chunks(d_out)) * d_in * 4 + 256;
@@ -473,17 +481,23 @@ __global__ __launch_bounds__(kCscThreads) void csc_hist_kernel(const int32_t* __
 }
 
 // Per column j (one thread each): hist[ch][j] -> number of entries of column
-// j in chunks before ch; the column's total goes to cnt[j].
+// j in chunks before ch; the column's total goes to cnt[j]. Chunks go in
+// batches of 16 whose loads are all issued before the running sum.
 __global__ __launch_bounds__(256) void csc_colsum_kernel(int32_t* __restrict__ hist, int d_in,
                                                          int nchunks, int32_t* __restrict__ cnt) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= d_in) return;
   int run = 0;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int64_t a = static_cast<int64_t>(ch) * d_in + j;
-    const int hv = hist[a];
-    hist[a] = run;
-    run += hv;
+  for (int c0 = 0; c0 < nchunks; c0 += 16) {
+    int hv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      hv[u] = c0 + u < nchunks ? hist[static_cast<int64_t>(c0 + u) * d_in + j] : 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (c0 + u < nchunks) hist[static_cast<int64_t>(c0 + u) * d_in + j] = run;
+      run += hv[u];
+    }
   }
   cnt[j] = run;
 }
