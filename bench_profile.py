@@ -41,8 +41,11 @@ def template_args(n: str):
 
 def kernel_ids(name: str):
     n = short(name)
-    if n.startswith("spmm_kernel<"):
-        return ["BWD_SPMM" if template_args(n)[6] == "true" else "FWD_SPMM"]
+    if n.startswith("rows_dc_kernel<"):
+        return ["BWD_SPMM"]
+    if n.startswith("rows_kernel<"):
+        # the plain gather: forward (source z, fp32); bench.py's backward always forms dc
+        return ["FWD_SPMM"] if template_args(n)[0] == "float" else []
     if n.startswith("fwht_rows_kernel<"):
         # FWHT(x) -> fp32 z in forward and backward; FWHT(dz) -> activations
         return ["FWD_FWHT", "BWD_FWHT_X"] if template_args(n)[2] == "float" else ["BWD_FWHT_DX"]
