@@ -831,7 +831,33 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     }
   }
 
-  // epilogue: dz rows row0 .. row0+7 of the lane's 4 tokens
+  // epilogue. A whole tile goes through LDS, 128 tokens at a time, laid out
+  // [token][row] (stride 129 floats), so that each token's 128 outputs leave
+  // as 512 contiguous bytes; otherwise each lane writes its own 8 rows.
+  if (t0 + kRT <= T && rg0 + kRW * kRRdc <= n_out && n_out % 4 == 0) {
+    constexpr int kEp = kRW * kRRdc + 1;
+    float* ep = &stage[0][0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // the staging buffers (or the previous half) are free
+      if ((lane >> 5) == h) {
+        const int lt = 4 * (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < kRRdc; ++r) ep[(lt + q) * kEp + w * kRRdc + r] = acc[r][q];
+      }
+      __syncthreads();
+      for (int task = threadIdx.x; task < (kRT / 2) * (kRW * kRRdc / 4); task += kRW * 64) {
+        const int tt = task / (kRW * kRRdc / 4);
+        const int c4 = task % (kRW * kRRdc / 4);
+        const float* e = ep + tt * kEp + 4 * c4;
+        *reinterpret_cast<float4*>(out + (t0 + (kRT / 2) * h + tt) * n_out + rg0 + 4 * c4) =
+            make_float4(e[0], e[1], e[2], e[3]);
+      }
+    }
+    return;
+  }
   const bool vec = row0 + kRRdc <= n_out && n_out % 4 == 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
