@@ -34,6 +34,10 @@ Readings of points the pages leave open (all listed in the design notes):
     column; +0.0 and -0.0 are equal magnitudes. E is listed by (i, j).
   * Value Refinement with an identity Hessian (R = I) is exactly the identity
     on the dense solution, so c = fp32_RNE(C[i, E_i]) (see ``refine_ls``).
+  * The ablation's selection variants: "magnitude" takes the global top-p of
+    |C| (equal magnitudes in row-major order); "random" takes the p positions
+    with the smallest SplitMix64 draws, the draw of position (i, j) being
+    output i*d_in + j of the generator seeded with the caller's seed.
 
 Parity pins: every public function here is pinned by tests under ``tests/``
 against closed forms, library routines or brute force, except the parts of
@@ -51,7 +55,8 @@ import numpy as np
 
 __all__ = [
     "sylvester", "transform", "row_norms", "adaalloc", "adaalloc_margins",
-    "select", "values", "refine_ls", "csc", "init_select", "scatter_dense",
+    "select", "values", "refine_ls", "csc", "init_select", "splitmix64", "magnitude_keys",
+    "random_keys", "global_select", "init_select_global", "scatter_dense",
     "materialize", "forward", "backward", "backward_dc_rows", "sign_update",
     "rel_err",
 ]
@@ -275,6 +280,82 @@ def init_select(dwq: np.ndarray, p: int, m: int = 3, t: float = 1.0,
         out["budget_margin"] = adaalloc_margins(w, p, d_in, m, t)
         out["C"] = C
     return out
+
+
+# --------------------------------------------------------------------------
+# Selection variants of the ablation: the global top-p of the dense solution
+# by magnitude, and p positions drawn at random ([PN] 关键设计 2 describes
+# the global magnitude pick that AdaAlloc improves on; 实验关键数据 ›
+# 消融实验 (Table 4) compares both with AdaAlloc; [GS] §2.2). Values and
+# refinement are as for AdaAlloc: c = fp32(C[E]) under R = I.
+# --------------------------------------------------------------------------
+
+_GAMMA = 0x9E3779B97F4A7C15
+_U64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: np.ndarray) -> np.ndarray:
+    """Output n (n = 0, 1, ...) of the SplitMix64 generator seeded with
+    `seed` (Steele, Lea & Flood, "Fast splittable pseudorandom number
+    generators", OOPSLA 2014): the state after n+1 steps is
+    seed + (n+1)*gamma mod 2^64 with gamma = 0x9E3779B97F4A7C15, and the
+    output is that state through the mix: z ^= z >> 30; z *= 0xBF58476D1CE4E5B9;
+    z ^= z >> 27; z *= 0x94D049BB133111EB; z ^= z >> 31 (all mod 2^64).
+    The state is a function of n alone, so any draw is computed directly."""
+    n = np.asarray(n, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & _U64) + (n + np.uint64(1)) * np.uint64(_GAMMA)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def magnitude_keys(C: np.ndarray) -> np.ndarray:
+    """|C| as fp64 bit patterns (uint64): ordered like |C|; -0.0 == +0.0."""
+    return np.ascontiguousarray(np.abs(C)).view(np.uint64)
+
+
+def random_keys(d_out: int, d_in: int, seed: int) -> np.ndarray:
+    """The complement of the SplitMix64 draw of each position (flat index
+    i*d_in + j): larger keys are smaller draws, so taking the largest keys
+    takes the positions with the smallest draws."""
+    n = np.arange(d_out * d_in, dtype=np.uint64)
+    return (~splitmix64(seed, n)).reshape(d_out, d_in)
+
+
+def global_select(keys: np.ndarray, p: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The p positions with the largest keys over the whole matrix, equal
+    keys taken in row-major order; E listed by (i, j), row_ptr per row."""
+    d_out, d_in = keys.shape
+    flat = keys.ravel()
+    if not 0 <= p <= flat.size:
+        raise ValueError("p out of range")
+    order = np.lexsort((np.arange(flat.size), ~flat))   # key descending, index ascending
+    sel = np.sort(order[:p])
+    E = np.stack([sel // d_in, sel % d_in], axis=1).astype(np.int32)
+    counts = np.bincount(E[:, 0], minlength=d_out)
+    row_ptr = np.zeros(d_out + 1, dtype=np.int32)
+    np.cumsum(counts, out=row_ptr[1:])
+    return row_ptr, E
+
+
+def init_select_global(dwq: np.ndarray, p: int, strategy: str,
+                       seed: int = 0) -> Dict[str, np.ndarray]:
+    """Global selection variant ('magnitude' or 'random') of the init:
+    E from global_select on the variant's keys, c = fp32(C[E])."""
+    d_out, d_in = dwq.shape
+    C = transform(dwq)
+    if strategy == "magnitude":
+        keys = magnitude_keys(C)
+    elif strategy == "random":
+        keys = random_keys(d_out, d_in, seed)
+    else:
+        raise ValueError(strategy)
+    row_ptr, E = global_select(keys, p)
+    c = values(C, E)
+    col_ptr, perm = csc(E, d_in)
+    return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm, C=C, keys=keys)
 
 
 # --------------------------------------------------------------------------

@@ -483,3 +483,108 @@ def test_rank_of_small_config_adapter():
     F[r["E"][:, 0], r["E"][:, 1]] = rng.integers(1, 1000, size=len(r["E"]))
     assert _rank_mod_p(F) == 256
     assert np.diff(r["row_ptr"]).min() >= 3
+
+
+# ------------------------------------------------------------------ selection variants
+# ([PN] 关键设计 2, 实验关键数据 › 消融实验 Table 4; [GS] §2.2)
+
+def test_splitmix64_published_outputs():
+    # first outputs of SplitMix64 from state 0 (Steele, Lea & Flood 2014; the
+    # reference generator's well-known test values)
+    got = [int(v) for v in O.splitmix64(0, np.arange(3))]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_splitmix64_counter_form_continues_a_stream():
+    # draw n of seed s is draw 0 of the generator advanced by n steps
+    n = np.arange(50, dtype=np.uint64)
+    seed = 12345
+    stepped = [int(O.splitmix64((seed + int(k) * 0x9E3779B97F4A7C15) & ((1 << 64) - 1), 0))
+               for k in range(50)]
+    assert [int(v) for v in O.splitmix64(seed, n)] == stepped
+
+
+def test_splitmix64_bits_are_balanced():
+    z = O.splitmix64(99, np.arange(200000))
+    for b in (0, 17, 40, 63):
+        frac = float(np.mean((z >> np.uint64(b)) & np.uint64(1)))
+        assert abs(frac - 0.5) < 0.01
+
+
+def _rand_dwq(d_out, d_in, seed):
+    return np.random.default_rng(seed).standard_normal((d_out, d_in)).astype(np.float32)
+
+
+@pytest.mark.parametrize("p", [0, 1, 7, 40, 128])
+def test_magnitude_selection_is_a_threshold(p):
+    dwq = _rand_dwq(8, 16, 3)
+    r = O.init_select_global(dwq, p, "magnitude")
+    C = O.transform(dwq)
+    mask = np.zeros(C.shape, bool)
+    mask[r["E"][:, 0], r["E"][:, 1]] = True
+    assert mask.sum() == p
+    if 0 < p < C.size:
+        assert np.abs(C[mask]).min() >= np.abs(C[~mask]).max()
+    assert np.array_equal(r["c"], C[mask].astype(np.float32))   # row-major = E order
+
+
+def test_magnitude_captures_at_least_the_adaalloc_energy():
+    dwq = _rand_dwq(32, 64, 5)
+    p = 300
+    C = O.transform(dwq)
+    g = O.init_select_global(dwq, p, "magnitude")
+    a = O.init_select(dwq, p)
+    eg = np.sum(C[g["E"][:, 0], g["E"][:, 1]] ** 2)
+    ea = np.sum(C[a["E"][:, 0], a["E"][:, 1]] ** 2)
+    assert eg >= ea
+
+
+def test_magnitude_bruteforce_tiny():
+    # every p-subset of a 2x4 matrix: the selection has the largest sum of |C|
+    dwq = np.array([[0.3, -1.0, 0.25, 0.5], [2.0, 0.1, -0.4, 0.05]], np.float32)
+    C = np.abs(O.transform(dwq)).ravel()
+    for p in range(9):
+        r = O.init_select_global(dwq, p, "magnitude")
+        got = sorted((r["E"][:, 0] * 4 + r["E"][:, 1]).tolist())
+        best = max(itertools.combinations(range(8), p), key=lambda s: (sum(C[list(s)]), [-i for i in s]))
+        assert np.isclose(sum(C[got]), sum(C[list(best)]), rtol=0, atol=1e-12)
+
+
+def test_magnitude_ties_go_in_row_major_order():
+    # one spike per row: every |C| of a row is equal; rows 1 and 2 share a value
+    dwq = np.zeros((3, 8), np.float32)
+    dwq[0, 5], dwq[1, 2], dwq[2, 7] = 0.5, 2.0, -2.0
+    r = O.init_select_global(dwq, 11, "magnitude")
+    flat = (r["E"][:, 0] * 8 + r["E"][:, 1]).tolist()
+    assert flat == list(range(8, 19))     # all of row 1, then the first 3 of row 2
+    assert r["row_ptr"].tolist() == [0, 0, 8, 11]
+
+
+def test_random_selection_ignores_the_data_and_follows_the_draws():
+    a = O.init_select_global(_rand_dwq(8, 16, 1), 30, "random", seed=11)
+    b = O.init_select_global(_rand_dwq(8, 16, 2), 30, "random", seed=11)
+    assert np.array_equal(a["E"], b["E"])
+    c = O.init_select_global(_rand_dwq(8, 16, 1), 30, "random", seed=12)
+    assert not np.array_equal(a["E"], c["E"])
+    draws = O.splitmix64(11, np.arange(128)).reshape(8, 16)
+    mask = np.zeros((8, 16), bool)
+    mask[a["E"][:, 0], a["E"][:, 1]] = True
+    assert draws[mask].max() < draws[~mask].min()     # the 30 smallest draws
+
+
+def test_random_selection_is_uniform():
+    counts = np.zeros(64)
+    for seed in range(400):
+        r = O.init_select_global(np.zeros((8, 8), np.float32), 16, "random", seed=seed)
+        counts[r["E"][:, 0] * 8 + r["E"][:, 1]] += 1
+    freq = counts / 400
+    assert np.all(np.abs(freq - 0.25) < 0.1)
+
+
+def test_global_selection_full_and_empty_budgets():
+    dwq = _rand_dwq(4, 8, 9)
+    for strategy in ("magnitude", "random"):
+        full = O.init_select_global(dwq, 32, strategy, seed=1)
+        assert full["E"].shape == (32, 2) and full["row_ptr"].tolist() == [0, 8, 16, 24, 32]
+        empty = O.init_select_global(dwq, 0, strategy, seed=1)
+        assert empty["E"].shape == (0, 2) and empty["col_ptr"].tolist() == [0] * 9
