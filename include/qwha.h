@@ -152,6 +152,34 @@ qwha_status qwha_sign_update(float* c, const float* dc, int64_t p, float step,
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Global selection variants of the init: the baselines AdaAlloc is compared
+ * with (papernotes.org, 关键设计 2 (global top-p of the dense solution) and
+ * 实验关键数据 › 消融实验, Table 4; gist.science §2.2).
+ *   QWHA_SELECT_MAGNITUDE: the p positions of the whole matrix with the
+ *     largest |C| (C = dWq H, fp64 as in qwha_init_select).
+ *   QWHA_SELECT_RANDOM: p positions uniformly at random without
+ *     replacement: the p smallest draws u[i][j] = SplitMix64 output
+ *     i*d_in + j of the generator seeded with `seed` (Steele, Lea & Flood,
+ *     OOPSLA 2014; output n is mix64(seed + (n+1) * 0x9E3779B97F4A7C15)).
+ * Equal keys are taken in row-major order (lower row, then lower column).
+ * The budgets p_i follow from the selection; E ascending per row and
+ * c = fp32_RNE(C[i,j]) as in qwha_init_select (the values are the dense
+ * solution for both strategies). Outputs as qwha_init_select. Requires
+ * 0 <= p <= d_in * d_out (QWHA_ERR_BUDGET), a known strategy
+ * (QWHA_ERR_INVALID_ARG) and a workspace of at least
+ * qwha_init_global_workspace_bytes(d_out, d_in, strategy) bytes (0 for an
+ * unknown strategy); the magnitude strategy keeps one 64-bit key per
+ * position there (8 * d_out * d_in bytes).
+ * --------------------------------------------------------------------------- */
+enum { QWHA_SELECT_MAGNITUDE = 1, QWHA_SELECT_RANDOM = 2 };
+size_t qwha_init_global_workspace_bytes(int32_t d_out, int32_t d_in, int32_t strategy);
+qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_in, int64_t p,
+                                    int32_t strategy, uint64_t seed, int32_t* row_ptr,
+                                    int32_t* E, float* c, int32_t* col_ptr, int32_t* csc_perm,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Profiling aid: the next launch of kernel `kernel` made by this thread
  * (inside any entry point above) is bracketed by hipEventRecord(start) and
  * hipEventRecord(stop) on that launch's stream; the request is then
@@ -169,7 +197,8 @@ typedef enum qwha_kernel {
   QWHA_KERNEL_BWD_DC_REDUCE = 6,
   QWHA_KERNEL_INIT_SELECT = 7,  /* fp64 transform + top-k inside qwha_init_select */
   QWHA_KERNEL_MATERIALIZE = 8,
-  QWHA_KERNEL_FWHT = 9          /* qwha_fwht */
+  QWHA_KERNEL_FWHT = 9,         /* qwha_fwht */
+  QWHA_KERNEL_GLOBAL_THRESHOLD = 10 /* keys, radix select and budgets in qwha_init_select_global */
 } qwha_kernel;
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 

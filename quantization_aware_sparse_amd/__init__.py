@@ -19,12 +19,16 @@ from ._lib import QwhaError, check, lib  # noqa: F401
 
 __all__ = [
     "QWHA_F32", "QWHA_BF16", "QwhaError", "lib",
-    "qwha_init_select", "qwha_materialize", "qwha_fwd", "qwha_bwd",
+    "QWHA_SELECT_MAGNITUDE", "QWHA_SELECT_RANDOM",
+    "qwha_init_select", "qwha_init_select_global", "qwha_materialize", "qwha_fwd", "qwha_bwd",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
 QWHA_F32 = 0
 QWHA_BF16 = 1
+QWHA_SELECT_MAGNITUDE = 1
+QWHA_SELECT_RANDOM = 2
+_STRATEGY = {"magnitude": QWHA_SELECT_MAGNITUDE, "random": QWHA_SELECT_RANDOM}
 
 _DT = {torch.float32: QWHA_F32, torch.bfloat16: QWHA_BF16}
 
@@ -73,6 +77,33 @@ def qwha_init_select(dWq: torch.Tensor, p: int, min_per_row: int = 3,
                                _ptr(row_ptr), E.data_ptr(), c.data_ptr(), _ptr(col_ptr),
                                perm.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
           "qwha_init_select")
+    return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm)
+
+
+def qwha_init_select_global(dWq: torch.Tensor, p: int, strategy: str = "magnitude",
+                            seed: int = 0,
+                            ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Global top-p selection by |C| ("magnitude") or uniformly at random
+    ("random", SplitMix64 draws seeded with `seed`); outputs as
+    qwha_init_select."""
+    if strategy not in _STRATEGY:
+        raise ValueError(f"strategy must be one of {sorted(_STRATEGY)}")
+    st = _STRATEGY[strategy]
+    d_out, d_in = dWq.shape
+    dev = dWq.device
+    row_ptr = torch.empty(d_out + 1, dtype=torch.int32, device=dev)
+    E = torch.empty((max(p, 1), 2), dtype=torch.int32, device=dev)[:p]
+    c = torch.empty(max(p, 1), dtype=torch.float32, device=dev)[:p]
+    col_ptr = torch.empty(d_in + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(p, 1), dtype=torch.int32, device=dev)[:p]
+    need = lib.qwha_init_global_workspace_bytes(d_out, d_in, st)
+    if ws is None:
+        ws = workspace(need, dev)
+    check(lib.qwha_init_select_global(_ptr(dWq), d_out, d_in, p, st,
+                                      int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(row_ptr),
+                                      E.data_ptr(), c.data_ptr(), _ptr(col_ptr),
+                                      perm.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+          "qwha_init_select_global")
     return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm)
 
 

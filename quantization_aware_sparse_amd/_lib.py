@@ -31,6 +31,10 @@ SIGNATURES = {
     "qwha_init_select": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int32, c_double,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]),
+    "qwha_init_global_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "qwha_init_select_global": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int32,
+                                          ctypes.c_uint64, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "qwha_materialize": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
                                    c_float, c_int32, c_void_p, c_int32, c_void_p]),
     "qwha_fwd_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),

@@ -32,7 +32,7 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 struct Hook {
   hipEvent_t start, stop;
 };
-constexpr int kNumKernelIds = 10;
+constexpr int kNumKernelIds = 11;
 thread_local Hook g_hook[kNumKernelIds] = {};
 
 // Runs `launch` (a callable returning hipError_t) for kernel id `k`, with the
@@ -200,10 +200,65 @@ qwha_status qwha_init_select(const float* dWq, int32_t d_out, int32_t d_in, int6
                                      at(workspace, l.alloc), stream),
                      "adaalloc"));
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_INIT_SELECT, stream,
-                           [&] { return launch_init_select(dWq, d_out, log_n, row_ptr, E, c, stream); }),
+                           [&] {
+                             return launch_init_select(dWq, d_out, log_n, row_ptr, E, c, 0,
+                                                       nullptr, 0, stream);
+                           }),
                      "init_select"));
   QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
                                       at(workspace, l.csc), stream),
+                     "csc_build"));
+  return QWHA_OK;
+}
+
+size_t qwha_init_global_workspace_bytes(int32_t d_out, int32_t d_in, int32_t strategy) {
+  if (d_out < 1 || d_in < 1) return 0;
+  if (strategy != QWHA_SELECT_MAGNITUDE && strategy != QWHA_SELECT_RANDOM) return 0;
+  return align256(global_select_scratch_bytes(d_out, d_in, strategy)) +
+         align256(csc_scratch_bytes(d_out, d_in));
+}
+
+qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_in, int64_t p,
+                                    int32_t strategy, uint64_t seed, int32_t* row_ptr,
+                                    int32_t* E, float* c, int32_t* col_ptr, int32_t* csc_perm,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  if (strategy != QWHA_SELECT_MAGNITUDE && strategy != QWHA_SELECT_RANDOM)
+    return fail(QWHA_ERR_INVALID_ARG, "strategy=%d is neither QWHA_SELECT_MAGNITUDE nor "
+                "QWHA_SELECT_RANDOM", strategy);
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_NEED(dWq, 16);
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(col_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+    QWHA_NEED(csc_perm, 4);
+  }
+  const size_t sel_bytes = align256(global_select_scratch_bytes(d_out, d_in, strategy));
+  const size_t total = sel_bytes + align256(csc_scratch_bytes(d_out, d_in));
+  if (workspace == nullptr || workspace_bytes < total)
+    return fail(QWHA_ERR_WORKSPACE, "global init workspace needs %zu bytes", total);
+  QWHA_NEED(workspace, 256);
+
+  const unsigned long long* gtau = nullptr;
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_GLOBAL_THRESHOLD, stream,
+                           [&] {
+                             return launch_global_budgets(dWq, d_out, log_n, p, strategy, seed,
+                                                          row_ptr, workspace, &gtau, stream);
+                           }),
+                     "global_threshold"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_INIT_SELECT, stream,
+                           [&] {
+                             return launch_init_select(dWq, d_out, log_n, row_ptr, E, c,
+                                                       strategy, gtau, seed, stream);
+                           }),
+                     "init_select"));
+  QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
+                                      at(workspace, sel_bytes), stream),
                      "csc_build"));
   return QWHA_OK;
 }
@@ -407,7 +462,8 @@ qwha_status qwha_fwht(const void* in, qwha_dtype in_dtype, void* out, qwha_dtype
 
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
   g_err[0] = 0;
-  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_FWHT || kernel >= kNumKernelIds)
+  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_GLOBAL_THRESHOLD ||
+      kernel >= kNumKernelIds)
     return fail(QWHA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
   if (kernel == QWHA_KERNEL_NONE) {
     for (int i = 0; i < kNumKernelIds; ++i) g_hook[i] = Hook{nullptr, nullptr};

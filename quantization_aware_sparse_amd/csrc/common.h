@@ -88,4 +88,18 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// ------------------------------------------------------- random draws
+// Output n (n = 0, 1, ...) of the SplitMix64 generator seeded with `seed`
+// (Steele, Lea & Flood, "Fast splittable pseudorandom number generators",
+// OOPSLA 2014): the state after n+1 steps is seed + (n+1) * 0x9E3779B97F4A7C15
+// (mod 2^64), passed through the generator's 64-bit mix. Counter-based: any
+// draw is computed directly from n.
+__device__ __forceinline__ unsigned long long splitmix64(unsigned long long seed,
+                                                         unsigned long long n) {
+  unsigned long long z = seed + (n + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 }  // namespace qwha

@@ -21,8 +21,19 @@ hipError_t launch_row_norms(const float* dWq, int d_out, int d_in, double* w, hi
 hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int m, double t,
                            int32_t* row_ptr, void* scratch, hipStream_t s);
 size_t adaalloc_scratch_bytes(int d_out);
+// mode 0: AdaAlloc budgets in row_ptr, per-row threshold; mode 1 / 2: the
+// global threshold *gtau on |C| / random keys (see select_global.hip)
 hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
-                              int32_t* E, float* c, hipStream_t s);
+                              int32_t* E, float* c, int mode, const unsigned long long* gtau,
+                              unsigned long long seed, hipStream_t s);
+
+// ---- global selection variants (magnitude / random)
+size_t global_select_scratch_bytes(int d_out, int d_in, int mode);
+// keys (mode 1), the global threshold by radix select and the row budgets:
+// writes row_ptr and the threshold at *gtau (inside the scratch)
+hipError_t launch_global_budgets(const float* dWq, int d_out, int log_n, int64_t p, int mode,
+                                 unsigned long long seed, int32_t* row_ptr, void* scratch,
+                                 const unsigned long long** gtau, hipStream_t s);
 size_t csc_scratch_bytes(int d_out, int d_in);
 hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
                             int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s);

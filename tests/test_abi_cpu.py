@@ -55,6 +55,12 @@ def test_workspace_queries(q):
     assert b >= 2 * 8192 * 4096 * 4 + 524288 * 8
     assert q.qwha_init_workspace_bytes(4096, 4096) >= 4096 * 8
     assert q.qwha_fwd_workspace_bytes(-1, 4096, 4096, 1) == 0
+    # magnitude keeps one 64-bit key per position; random draws them on the fly
+    mag = q.qwha_init_global_workspace_bytes(4096, 4096, 1)
+    rnd = q.qwha_init_global_workspace_bytes(4096, 4096, 2)
+    assert mag >= 4096 * 4096 * 8 > rnd > 0
+    assert q.qwha_init_global_workspace_bytes(4096, 4096, 3) == 0
+    assert q.qwha_init_global_workspace_bytes(0, 4096, 1) == 0
 
 
 FAKE = 0x10000          # aligned, never dereferenced (validation fails first)
@@ -105,6 +111,29 @@ def test_init_validation(q):
     assert call(dWq=FAKE + 8) == ALIGN
     assert call(E=None) == INVALID
     assert call() == WORKSPACE                      # everything else fine, no workspace
+
+
+def test_init_global_validation(q):
+    def call(**kw):
+        a = dict(dWq=FAKE, d_out=256, d_in=256, p=2048, st=1, seed=7, row_ptr=FAKE, E=FAKE,
+                 c=FAKE, col_ptr=FAKE, perm=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_init_select_global(a["dWq"], a["d_out"], a["d_in"], a["p"], a["st"],
+                                         a["seed"], a["row_ptr"], a["E"], a["c"], a["col_ptr"],
+                                         a["perm"], a["ws"], a["wsb"], None)
+    assert call(p=256 * 256 + 1) == BUDGET
+    assert call(p=-1) == BUDGET
+    assert call(st=0) == INVALID
+    assert call(st=3) == INVALID
+    assert call(d_in=100) == SHAPE
+    assert call(d_out=0) == SHAPE
+    assert call(dWq=FAKE + 8) == ALIGN
+    assert call(E=None) == INVALID
+    assert call(row_ptr=None) == INVALID
+    assert call() == WORKSPACE                      # everything else fine, no workspace
+    assert call(st=2, wsb=q.qwha_init_global_workspace_bytes(256, 256, 2) - 1) == WORKSPACE
+    assert call(st=2, ws=FAKE + 16, wsb=1 << 30) == ALIGN
+    assert call(seed=(1 << 64) - 1, ws=None) == WORKSPACE     # full 64-bit seeds accepted
 
 
 def test_bwd_materialize_fwht_validation(q):

@@ -152,6 +152,99 @@ def test_init_select_configs(q, cfg):
         assert_init_equal(ref, got)
 
 
+# ------------------------------------------------------------------ global selection
+def global_both(q, dwq, p, strategy, seed=0):
+    ref = O.init_select_global(dwq, p, strategy, seed)
+    got = q.qwha_init_select_global(to_dev(dwq), p, strategy, seed)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def magnitude_boundary_ambiguous(ref, p):
+    """True when the p-th and (p+1)-th largest |C| differ by less than the
+    rounding of an fp64 transform (different summation orders could swap
+    them); exact ties (gap 0) are decided by position on both sides."""
+    a = np.sort(np.abs(ref["C"]).ravel())[::-1]
+    if p == 0 or p >= a.size:
+        return False
+    gap = a[p - 1] - a[p]
+    return 0 < gap <= 1e-12 * max(a[0], 1e-300)
+
+
+@pytest.mark.parametrize("strategy", ["magnitude", "random"])
+@pytest.mark.parametrize("d_out,d_in,p", [
+    (37, 2, 40), (5, 4, 0), (5, 4, 20), (5, 4, 1), (64, 16, 300), (300, 64, 2500),
+    (129, 128, 9000), (17, 1024, 2000), (3, 8192, 900), (2, 16384, 1000), (1, 16384, 16383),
+    (64, 256, 64 * 256), (50, 512, 150), (1000, 32, 7)])
+def test_init_global_edges(q, strategy, d_out, d_in, p):
+    say("init global", strategy, d_out, d_in, p)
+    dwq = _edge_dwq(d_out, d_in, 5 * d_out + d_in)
+    ref, got = global_both(q, dwq, p, strategy, seed=d_out * 31 + p)
+    if strategy == "magnitude":
+        assert not magnitude_boundary_ambiguous(ref, p)
+    assert_init_equal(ref, got)
+
+
+def test_init_global_magnitude_ties_across_rows(q):
+    # rows that are one spike each have |C| equal to the spike everywhere:
+    # the boundary falls inside a run of equal keys spanning several rows,
+    # which go in row-major order; an all-zero matrix is one tie of all keys
+    d_out, d_in = 24, 64
+    dwq = _edge_dwq(d_out, d_in, 11) * 1e-3
+    for i, col in ((2, 5), (3, 0), (7, 63), (8, 9), (15, 1)):
+        dwq[i] = 0.0
+        dwq[i, col] = 0.125 if i % 2 else -0.125
+    for p in (40, 64 + 10, 5 * 64 - 1, 5 * 64 + 3):
+        say("init global ties", p)
+        ref, got = global_both(q, dwq, p, "magnitude")
+        assert_init_equal(ref, got)
+    zero = np.zeros((9, 32), dtype=np.float32)
+    for p in (0, 1, 33, 9 * 32 - 1, 9 * 32):
+        say("init global zeros", p)
+        ref, got = global_both(q, zero, p, "magnitude")
+        assert_init_equal(ref, got)
+        assert np.array_equal(got["E"].cpu().numpy()[:, 0] * 32 + got["E"].cpu().numpy()[:, 1],
+                              np.arange(p))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 0x9E3779B97F4A7C15, (1 << 64) - 1])
+def test_init_global_random_seeds(q, seed):
+    dwq = _edge_dwq(200, 128, 3)
+    say("init global random seed", seed)
+    ref, got = global_both(q, dwq, 3000, "random", seed)
+    assert_init_equal(ref, got)
+    # the draw ignores the data: another matrix, same positions
+    got2 = q.qwha_init_select_global(to_dev(_edge_dwq(200, 128, 4)), 3000, "random", seed)
+    assert torch.equal(got2["E"], got["E"])
+
+
+@pytest.mark.parametrize("strategy", ["magnitude", "random"])
+def test_init_global_workspace_reuse(q, strategy):
+    # one workspace for two calls, the second smaller: nothing carries over
+    big = _edge_dwq(300, 256, 1)
+    small = _edge_dwq(40, 64, 2)
+    ws = q.workspace(q.lib.qwha_init_global_workspace_bytes(300, 256, 1 if strategy ==
+                                                            "magnitude" else 2), DEV)
+    for dwq, p in ((big, 9000), (small, 500), (big, 1)):
+        say("init global reuse", strategy, dwq.shape, p)
+        ref = O.init_select_global(dwq, p, strategy, 9)
+        got = q.qwha_init_select_global(to_dev(dwq), p, strategy, 9, ws=ws)
+        torch.cuda.synchronize()
+        assert_init_equal(ref, got)
+
+
+@pytest.mark.parametrize("strategy", ["magnitude", "random"])
+@pytest.mark.parametrize("cfg", ["c2", "c4"])
+def test_init_global_configs(q, strategy, cfg):
+    for spec in synth.config_specs(cfg):
+        say("init global config", strategy, spec.name)
+        layer = synth.make_layer(spec, seed=0)
+        ref, got = global_both(q, layer.dwq, spec.p, strategy, seed=17)
+        if strategy == "magnitude":
+            assert not magnitude_boundary_ambiguous(ref, spec.p), "ambiguous at this seed"
+        assert_init_equal(ref, got)
+
+
 # ------------------------------------------------------------------ materialize
 @pytest.mark.parametrize("d_out,d_in,p", [(37, 2, 40), (300, 64, 2500), (17, 1024, 2000),
                                           (3, 8192, 900), (2, 16384, 1000), (256, 256, 2048)])
