@@ -33,6 +33,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X vector fp32 (packed FMA)
 
 K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_FWHT_X=3, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC_REDUCE=6,
          INIT_SELECT=7, MATERIALIZE=8)
+GLOBAL_THRESHOLD = 10
 
 
 def parse():
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--sets", type=int, default=4, help="rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant-reps", type=int, default=10,
+                    help="timed calls of each init selection strategy (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: all of the workload's)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -60,6 +63,10 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
 
     def create(self):
         e = ctypes.c_void_p()
@@ -251,9 +258,80 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
 
+    if args.variant_reps > 0:
+        out["init_variants"] = init_variants(args.variant_reps, sets, (d_out, d_in, p),
+                                             (row_ptr, E, c, col_ptr, perm), ws_i, stream, hip)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens or T)
     print(json.dumps(out), flush=True)
+
+
+def init_variants(reps, sets, dims, outs, ws_i, stream, hip):
+    """Time the init under each selection strategy on the same layer and
+    budget: AdaAlloc (qwha_init_select) and the global magnitude / random
+    selections (qwha_init_select_global), whole call and, for the global
+    ones, the threshold stage (keys, radix select, budgets) and the per-row
+    select kernel. Achieved rates use the stage's own traffic by design:
+    magnitude reads dW_Q once and writes its 8-byte keys once, then reads
+    them in 8 radix passes and one tie count (84 B per position); random
+    draws SplitMix64 in 9 passes over all positions and keeps nothing."""
+    import numpy as np
+    import torch
+    from quantization_aware_sparse_amd import check, lib
+    d_out, d_in, p = dims
+    row_ptr, E, c, col_ptr, perm = (t.data_ptr() for t in outs)
+    n = d_out * d_in
+    ev = [hip.create() for _ in range(6)]
+    res = {}
+    for name, strat in (("adaalloc", 0), ("magnitude", 1), ("random", 2)):
+        if strat:
+            ws = torch.empty(lib.qwha_init_global_workspace_bytes(d_out, d_in, strat),
+                             dtype=torch.uint8, device="cuda:0")
+        else:
+            ws = ws_i
+
+        def call(s):
+            dwq = sets[s % len(sets)][0].data_ptr()
+            if strat:
+                return lib.qwha_init_select_global(dwq, d_out, d_in, p, strat, 17 + s, row_ptr,
+                                                   E, c, col_ptr, perm, ws.data_ptr(),
+                                                   ws.numel(), stream)
+            return lib.qwha_init_select(dwq, d_out, d_in, p, 3, 1.0, row_ptr, E, c, col_ptr,
+                                        perm, ws.data_ptr(), ws.numel(), stream)
+        for s in range(2):
+            check(call(s), name)
+        torch.cuda.synchronize()
+        whole, thr, sel = [], [], []
+        for s in range(reps):
+            check(lib.qwha_profile_next(K["INIT_SELECT"], ev[2], ev[3]), "profile")
+            if strat:
+                check(lib.qwha_profile_next(GLOBAL_THRESHOLD, ev[4], ev[5]), "profile")
+            hip.record(ev[0], stream)
+            check(call(s), name)
+            hip.record(ev[1], stream)
+            torch.cuda.synchronize()
+            whole.append(hip.elapsed_ms(ev[0], ev[1]))
+            sel.append(hip.elapsed_ms(ev[2], ev[3]))
+            if strat:
+                thr.append(hip.elapsed_ms(ev[4], ev[5]))
+        r = {"init_us": round(1e3 * float(np.mean(whole)), 2),
+             "select_us": round(1e3 * float(np.mean(sel)), 2)}
+        if strat:
+            t_us = 1e3 * float(np.mean(thr))
+            r["threshold_us"] = round(t_us, 2)
+            if strat == 1:
+                a = 84.0 * n / (t_us * 1e-6) / 1e9
+                r["threshold_roofline"] = dict(bound="hbm", achieved=round(a, 1), unit="GB/s",
+                                               peak=HBM_PEAK_GBS, frac=round(a / HBM_PEAK_GBS, 4),
+                                               bytes_per_position=84)
+            else:
+                r["threshold_gdraws_per_s"] = round(9.0 * n / (t_us * 1e-6) / 1e9, 1)
+        res[name] = r
+        del ws
+    res["calls"] = reps
+    res["layer"] = f"{d_out}x{d_in}, p={p}"
+    return res
 
 
 # library sources that define each timed kernel (besides the shared headers
@@ -263,6 +341,7 @@ KERNEL_SOURCES = {
     "BWD_FWHT_DX": ["fwht.hip", "fwht_core.h"], "FWD_SPMM": ["spmm.hip"],
     "BWD_SPMM": ["spmm.hip"], "BWD_DC_REDUCE": ["spmm.hip"],
     "INIT_SELECT": ["init.hip", "fwht_core.h"], "MATERIALIZE": ["materialize.hip", "fwht_core.h"],
+    "GLOBAL_THRESHOLD": ["select_global.hip", "fwht_core.h"],
 }
 SHARED_SOURCES = ["common.h", "launch.h", "api.hip"]
 

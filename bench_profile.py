@@ -22,11 +22,22 @@ import re
 
 import bench
 
+# ids timed over several kernels: listed in the table, no per-launch traffic line
+MULTI_KERNEL_IDS = {"GLOBAL_THRESHOLD"}
+# ids with no bench.py event of their own: listed in the table only
+TABLE_ONLY_IDS = {"INIT_SELECT_GLOBAL"}
+
 # kernel symbol prefix -> profiling ids (spmm and fwht resolved by template arguments)
 KERNEL_IDS = {
-    "init_select_kernel": ["INIT_SELECT"],
     "materialize_kernel": ["MATERIALIZE"],
     "dc_reduce_kernel": ["BWD_DC_REDUCE"],
+    # global selection: the threshold stage
+    "mag_keys_kernel": ["GLOBAL_THRESHOLD"],
+    "radix_hist_kernel": ["GLOBAL_THRESHOLD"],
+    "radix_pick_kernel": ["GLOBAL_THRESHOLD"],
+    "row_ties_kernel": ["GLOBAL_THRESHOLD"],
+    "global_budget_kernel": ["GLOBAL_THRESHOLD"],
+    "gsel_init_kernel": ["GLOBAL_THRESHOLD"],
 }
 
 
@@ -46,6 +57,9 @@ def kernel_ids(name: str):
     if n.startswith("rows_kernel<"):
         # the plain gather: forward (source z, fp32); bench.py's backward always forms dc
         return ["FWD_SPMM"] if template_args(n)[0] == "float" else []
+    if n.startswith("init_select_kernel<"):
+        # the AdaAlloc instance (selection mode 0) is the one of the step
+        return ["INIT_SELECT"] if template_args(n)[1] == "0" else ["INIT_SELECT_GLOBAL"]
     if n.startswith("fwht_rows_kernel<"):
         # FWHT(x) -> fp32 z in forward and backward; FWHT(dz) -> activations
         return ["FWD_FWHT", "BWD_FWHT_X"] if template_args(n)[2] == "float" else ["BWD_FWHT_DX"]
@@ -104,6 +118,8 @@ def cmd_traffic(a):
         wb = write[name] * f_write * 1024.0
         table.append(("/".join(kids), short(name), fetch[name], write[name], fb, wb))
         for kid in kids:
+            if kid in MULTI_KERNEL_IDS or kid in TABLE_ONLY_IDS:
+                continue
             lines.append(f"traffic: kernel={kid} config={a.config} bytes={int(round(fb + wb))} "
                          f"fetch={int(round(fb))} write={int(round(wb))} "
                          f"sources={bench.source_digest(kid)}")

@@ -297,16 +297,16 @@ struct SelCfg {
   static constexpr int BLOCK = F::TPR < 64 ? 64 : F::TPR;
 };
 
-// mode 0 (AdaAlloc): the row's budget picks its own threshold by bisection
+// MODE 0 (AdaAlloc): the row's budget picks its own threshold by bisection
 // on the |C| keys. Modes 1 / 2 (global selection): the threshold *gtau over
 // the whole matrix is given and the row takes its keys above it plus, of the
 // keys equal to it, as many as its budget leaves (lowest column first); the
 // keys are |C| (mode 1) or the complement of the position's SplitMix64 draw
 // (mode 2, output row*N + col of the generator seeded with `seed`).
-template <int LOG_N>
+template <int LOG_N, int MODE>
 __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     const float* __restrict__ dWq, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ E,
-    float* __restrict__ c, int mode, const unsigned long long* __restrict__ gtau,
+    float* __restrict__ c, const unsigned long long* __restrict__ gtau,
     unsigned long long seed) {
   using F = Fwht<LOG_N>;
   __shared__ double lds[F::LDS];
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) {
       v[r] = lds[F::pad(u * F::EPT + r)];
-      key[r] = mode == 2
+      key[r] = MODE == 2
                    ? ~splitmix64(seed, static_cast<unsigned long long>(row) * F::N + u * F::EPT + r)
                    : static_cast<unsigned long long>(__double_as_longlong(v[r])) &
                          0x7FFFFFFFFFFFFFFFull;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
   int need = 0;      // how many |C| == tau are taken (lowest index first)
   bool all = (k >= F::N), none = (k <= 0);
   int parity = 0;
-  if (!all && !none && mode != 0) {
+  if (!all && !none && MODE != 0) {
     tau = *gtau;
     int gt = 0;
 #pragma unroll
@@ -450,15 +450,31 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
   }
 }
 
+template <int L>
+hipError_t launch_select_mode(const float* dWq, int d_out, const int32_t* row_ptr, int32_t* E,
+                              float* c, int mode, const unsigned long long* gtau,
+                              unsigned long long seed, hipStream_t s) {
+  const dim3 grid(d_out), block(SelCfg<L>::BLOCK);
+  if (mode == 0)
+    hipLaunchKernelGGL((init_select_kernel<L, 0>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
+                       seed);
+  else if (mode == 1)
+    hipLaunchKernelGGL((init_select_kernel<L, 1>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
+                       seed);
+  else
+    hipLaunchKernelGGL((init_select_kernel<L, 2>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
+                       seed);
+  return hipGetLastError();
+}
+
 hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
                               int32_t* E, float* c, int mode, const unsigned long long* gtau,
                               unsigned long long seed, hipStream_t s) {
+  if (mode < 0 || mode > 2) return hipErrorInvalidValue;
   switch (log_n) {
-#define QWHA_CASE(L)                                                                        \
-  case L:                                                                                   \
-    hipLaunchKernelGGL(init_select_kernel<L>, dim3(d_out), dim3(SelCfg<L>::BLOCK), 0, s, dWq, \
-                       row_ptr, E, c, mode, gtau, seed);                                    \
-    return hipGetLastError();
+#define QWHA_CASE(L)                                                                       \
+  case L:                                                                                  \
+    return launch_select_mode<L>(dWq, d_out, row_ptr, E, c, mode, gtau, seed, s);
     QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
     QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
     QWHA_CASE(14)
