@@ -34,6 +34,13 @@ Readings of points the pages leave open (all listed in the design notes):
     column; +0.0 and -0.0 are equal magnitudes. E is listed by (i, j).
   * Value Refinement with an identity Hessian (R = I) is exactly the identity
     on the dense solution, so c = fp32_RNE(C[i, E_i]) (see ``refine_ls``).
+  * With calibration activations X the refinement is the normal equations of
+    the pages' per-channel least squares, x G[S,S] = Q[i,S] with
+    G = H Hs H / n^2, Q = dW_Q Hs H / n, Hs = X^T X (X token-major), solved by
+    Cholesky; a pivot at or below 1e-10 times its diagonal entry marks G[S,S]
+    as not positive definite and the row keeps the dense solution. AdaAlloc
+    then allocates by sqrt(dW_Q[i] Hs dW_Q[i]^T). Optional damping adds
+    damp * mean(diag Hs) to the diagonal (0 by default: the pages add none).
   * The ablation's selection variants: "magnitude" takes the global top-p of
     |C| (equal magnitudes in row-major order); "random" takes the p positions
     with the smallest SplitMix64 draws, the draw of position (i, j) being
@@ -56,7 +63,9 @@ import numpy as np
 __all__ = [
     "sylvester", "transform", "row_norms", "adaalloc", "adaalloc_margins",
     "select", "values", "refine_ls", "csc", "init_select", "splitmix64", "magnitude_keys",
-    "random_keys", "global_select", "init_select_global", "scatter_dense",
+    "random_keys", "global_select", "init_select_global", "hessian", "damped",
+    "activation_error_norms", "refine_system", "cholesky_lower", "refine_values",
+    "init_select_calibrated", "layer_output_error", "scatter_dense",
     "materialize", "forward", "backward", "backward_dc_rows", "sign_update",
     "rel_err",
 ]
@@ -356,6 +365,138 @@ def init_select_global(dwq: np.ndarray, p: int, strategy: str,
     c = values(C, E)
     col_ptr, perm = csc(E, d_in)
     return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm, C=C, keys=keys)
+
+
+# --------------------------------------------------------------------------
+# O11-O14: Value Refinement with a calibration Hessian   ([PN] 关键设计 2, 3;
+# 损失函数 / 训练策略; [GS] §2.2)
+#
+# The init's objective is the layer-output error ||dW_Q X - F H^-1 X||_F^2
+# over calibration activations; with the Hessian XX^T = U S U^T and
+# R = U S^(1/2) it becomes ||dW_Q R - F H^-1 R||_F^2, solved channel by
+# channel: positions by AdaAlloc (budgets from the activation error
+# magnitude ||dW_Q[i,:] R||, then the in-row top |C|), values by least
+# squares min_x ||v - x B'||^2 with v = dW_Q[i,:] R and B' the rows of
+# B = H^-1 R at the chosen positions. The closed form did not survive
+# extraction; it is read as the normal equations of that problem,
+#   x (B' B'^T) = v B'^T,  B' B'^T = G[S,S],  v B'^T = Q[i,S],
+#   G = H Hs H / n^2,  Q = dW_Q Hs H / n,  Hs = XX^T,
+# since R R^T = Hs and H^-1 = H/n is symmetric: no SVD is needed.
+# Activations are stored token-major here (X is [N][d_in]), so Hs = X^T X.
+# --------------------------------------------------------------------------
+
+def hessian(X: np.ndarray) -> np.ndarray:
+    """Hs = sum over calibration tokens of x^T x (fp64 [d_in][d_in]): the
+    pages' XX^T with one column per token."""
+    a = np.asarray(X, dtype=np.float64)
+    return a.T @ a
+
+
+def damped(Hs: np.ndarray, damp: float) -> np.ndarray:
+    """Hs + damp * mean(diag Hs) * I. The pages add no damping (damp = 0 is
+    the plain reading); a relative diagonal load is offered for calibration
+    sets too small to make Hs definite."""
+    Hs = np.asarray(Hs, dtype=np.float64)
+    if damp == 0.0:
+        return Hs.copy()
+    return Hs + damp * float(np.mean(np.diag(Hs))) * np.eye(Hs.shape[0])
+
+
+def activation_error_norms(dwq: np.ndarray, Hs: np.ndarray) -> np.ndarray:
+    """w_i = ||dW_Q[i,:] R||_2 = sqrt(dW_Q[i,:] Hs dW_Q[i,:]^T): the
+    activation error magnitude AdaAlloc allocates by ([PN] 关键设计 2)."""
+    a = np.asarray(dwq, dtype=np.float64)
+    q = np.einsum("ij,ij->i", a @ np.asarray(Hs, dtype=np.float64), a)
+    return np.sqrt(np.maximum(q, 0.0))
+
+
+def refine_system(dwq: np.ndarray, Hs: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """G = H Hs H / n^2 (the Gram matrix of the rows of B = H^-1 R) and
+    Q = dW_Q Hs H / n (row i holds v B^T), both fp64 dense."""
+    d_in = dwq.shape[1]
+    H = sylvester(d_in)
+    Hs = np.asarray(Hs, dtype=np.float64)
+    G = (H @ Hs @ H) / float(d_in) ** 2
+    Q = (np.asarray(dwq, dtype=np.float64) @ Hs @ H) / float(d_in)
+    return G, Q
+
+
+def cholesky_lower(A: np.ndarray, pivot_tol: float = 1e-10) -> Tuple[np.ndarray, bool]:
+    """Textbook Cholesky A = L L^T, column by column (outer-product form).
+    A pivot (the diagonal before its square root) at or below pivot_tol times
+    that diagonal entry of A marks A as not positive definite, returning
+    (partial L, False)."""
+    A = np.array(A, dtype=np.float64)
+    n = A.shape[0]
+    d0 = A.diagonal().copy()
+    L = np.zeros_like(A)
+    for k in range(n):
+        piv = A[k, k]
+        if not piv > pivot_tol * d0[k]:
+            return L, False
+        L[k, k] = np.sqrt(piv)
+        L[k + 1:, k] = A[k + 1:, k] / L[k, k]
+        A[k + 1:, k + 1:] -= np.outer(L[k + 1:, k], L[k + 1:, k])
+    return L, True
+
+
+def refine_values(G: np.ndarray, Q: np.ndarray, row_ptr: np.ndarray, E: np.ndarray,
+                  pivot_tol: float = 1e-10) -> Tuple[np.ndarray, np.ndarray]:
+    """Per row i with positions S = E_i: solve x G[S,S] = Q[i,S] by Cholesky
+    of G[S,S] and two triangular solves ([PN] 关键设计 3). Returns x (fp64 [p];
+    NaN on rows whose G[S,S] is not positive definite) and ok [d_out]."""
+    import scipy.linalg as sla
+    d_out = len(row_ptr) - 1
+    x = np.full(len(E), np.nan)
+    ok = np.ones(d_out, dtype=bool)
+    for i in range(d_out):
+        a, b = int(row_ptr[i]), int(row_ptr[i + 1])
+        if a == b:
+            continue
+        S = np.asarray(E[a:b, 1], dtype=np.int64)
+        A = G[np.ix_(S, S)]
+        L, good = cholesky_lower(A, pivot_tol)
+        if not good:
+            ok[i] = False
+            continue
+        y = sla.solve_triangular(L, Q[i, S], lower=True)
+        x[a:b] = sla.solve_triangular(L.T, y, lower=False)
+    return x, ok
+
+
+def init_select_calibrated(dwq: np.ndarray, Hs: np.ndarray, p: int, m: int = 3,
+                           t: float = 1.0, damp: float = 0.0,
+                           pivot_tol: float = 1e-10) -> Dict[str, np.ndarray]:
+    """The init with calibration data ([PN] 方法详解 › 整体框架, 关键设计 2, 3):
+    Hs' = damped(Hs), w = activation error norms under Hs', AdaAlloc budgets,
+    in-row top |C| positions (C = dW_Q H does not depend on Hs), then refined
+    values c = fp32(x); a row whose G[S,S] is not positive definite keeps the
+    dense solution fp32(C[E])."""
+    d_out, d_in = dwq.shape
+    Hd = damped(Hs, damp)
+    C = transform(dwq)
+    w = activation_error_norms(dwq, Hd)
+    budgets = adaalloc(w, p, d_in, m, t)
+    row_ptr, E = select(C, budgets)
+    c0 = values(C, E)
+    G, Q = refine_system(dwq, Hd)
+    x, ok = refine_values(G, Q, row_ptr, E, pivot_tol)
+    bad = np.repeat(~ok, np.diff(row_ptr))
+    c = np.where(bad, c0, x.astype(np.float32)).astype(np.float32)
+    rhs = Q[E[:, 0], E[:, 1]] if len(E) else np.zeros(0)
+    col_ptr, perm = csc(E, d_in)
+    return dict(row_ptr=row_ptr, E=E, c=c, c_dense=c0, x=x, ok=ok, col_ptr=col_ptr,
+                csc_perm=perm, budgets=budgets, w=w, G=G, rhs=rhs, C=C, Hs=Hd)
+
+
+def layer_output_error(dwq: np.ndarray, X: np.ndarray, E: np.ndarray, c: np.ndarray) -> float:
+    """||(dW_Q - F H^-1) X^T||_F^2 over calibration tokens X [N][d_in]: the
+    init's objective ([PN] 损失函数 / 训练策略)."""
+    d_out, d_in = dwq.shape
+    F = scatter_dense(E, np.asarray(c, dtype=np.float64), d_out, d_in)
+    resid = np.asarray(dwq, dtype=np.float64) - F @ sylvester(d_in) / float(d_in)
+    r = resid @ np.asarray(X, dtype=np.float64).T
+    return float(np.sum(r * r))
 
 
 # --------------------------------------------------------------------------

@@ -588,3 +588,144 @@ def test_global_selection_full_and_empty_budgets():
         assert full["E"].shape == (32, 2) and full["row_ptr"].tolist() == [0, 8, 16, 24, 32]
         empty = O.init_select_global(dwq, 0, strategy, seed=1)
         assert empty["E"].shape == (0, 2) and empty["col_ptr"].tolist() == [0] * 9
+
+
+# ---------------------------------------------- refinement with a Hessian (O11-O14)
+
+def _calib(N, d_in, seed, spread=1.0):
+    """Calibration tokens with per-channel scales spread over e^(+-spread)."""
+    rng = np.random.default_rng(seed)
+    scale = np.exp(spread * rng.standard_normal(d_in))
+    return rng.standard_normal((N, d_in)) * scale
+
+
+def test_refine_golden():
+    g = read_golden("refine_hand_2x2.txt")
+    p, m = (int(v) for v in g["p m"][0])
+    r = O.init_select_calibrated(g["dWq"].astype(np.float32), g["Hs"], p, m=m)
+    assert np.allclose(r["w"] ** 2, g["w squared"][0], rtol=1e-14)
+    assert r["budgets"].tolist() == g["budgets"][0].astype(int).tolist()
+    assert np.array_equal(r["E"], g["E"].astype(np.int32))
+    assert np.array_equal(r["c_dense"], g["c dense"][0].astype(np.float32))
+    x = g["x numerator"][0] / g["x denominator"][0]
+    assert np.allclose(r["x"], x, rtol=1e-14, atol=0)
+    assert np.array_equal(r["c"], x.astype(np.float32))
+
+
+def test_hessian_is_the_sum_of_token_outer_products():
+    X = _calib(7, 8, 1)
+    Hs = np.zeros((8, 8))
+    for t in range(7):
+        Hs += np.outer(X[t], X[t])
+    assert np.allclose(O.hessian(X), Hs, rtol=1e-13, atol=1e-13)
+
+
+def test_activation_error_norms_are_output_error_norms():
+    dwq = _rand_dwq(9, 16, 2)
+    X = _calib(40, 16, 3)
+    direct = np.linalg.norm(dwq.astype(np.float64) @ X.T, axis=1)    # ||dW_Q[i] X||
+    assert np.allclose(O.activation_error_norms(dwq, O.hessian(X)), direct, rtol=1e-12)
+    # identity Hessian: the plain row norms
+    assert np.allclose(O.activation_error_norms(dwq, np.eye(16)), O.row_norms(dwq), rtol=1e-14)
+
+
+@pytest.mark.parametrize("s", [1.0, 4.0, 0.37])
+def test_refine_with_isotropic_hessian_is_the_dense_solution(s):
+    dwq = _rand_dwq(12, 32, 5)
+    r = O.init_select_calibrated(dwq, s * np.eye(32), 120, m=3)
+    base = O.init_select(dwq, 120, m=3)
+    for key in ("row_ptr", "E", "col_ptr", "csc_perm"):
+        assert np.array_equal(r[key], base[key]), key
+    C = O.transform(dwq)
+    assert np.allclose(r["x"], C[r["E"][:, 0], r["E"][:, 1]], rtol=1e-12, atol=1e-15)
+
+
+def test_refine_matches_lstsq_on_the_unreduced_problem():
+    # min_x ||(dW_Q[i] - x (H/n)[S,:]) X^T||: no Hessian, no normal equations
+    d_out, d_in = 10, 32
+    dwq = _rand_dwq(d_out, d_in, 6)
+    X = _calib(96, d_in, 7, spread=1.5)
+    r = O.init_select_calibrated(dwq, O.hessian(X), 130, m=3)
+    H = O.sylvester(d_in)
+    assert r["ok"].all()
+    for i in range(d_out):
+        a, b = r["row_ptr"][i], r["row_ptr"][i + 1]
+        S = r["E"][a:b, 1]
+        D = (H / d_in)[S, :] @ X.T
+        target = dwq[i].astype(np.float64) @ X.T
+        sol, *_ = np.linalg.lstsq(D.T, target, rcond=None)
+        assert np.allclose(r["x"][a:b], sol, rtol=1e-9, atol=1e-12 * np.abs(sol).max())
+
+
+def test_refine_never_raises_the_layer_error_and_usually_lowers_it():
+    d_out, d_in = 16, 64
+    dwq = _rand_dwq(d_out, d_in, 8)
+    X = _calib(200, d_in, 9, spread=1.0)
+    r = O.init_select_calibrated(dwq, O.hessian(X), 400, m=3)
+    H = O.sylvester(d_in)
+    lower = 0
+    for i in range(d_out):     # per channel: refined x is optimal over its support
+        a, b = r["row_ptr"][i], r["row_ptr"][i + 1]
+        rows = slice(a, b)
+        def err(vals):
+            resid = dwq[i].astype(np.float64) - vals @ (H / d_in)[r["E"][rows, 1], :]
+            return float(np.sum((resid @ X.T) ** 2))
+        e_ref, e_dense = err(r["x"][rows]), err(r["c_dense"][rows].astype(np.float64))
+        assert e_ref <= e_dense * (1 + 1e-12)
+        lower += e_ref < 0.99 * e_dense
+    assert lower >= d_out // 2
+    assert O.layer_output_error(dwq, X, r["E"], r["c"]) < \
+        O.layer_output_error(dwq, X, r["E"], r["c_dense"])
+
+
+def test_refine_full_budget_reconstructs_for_any_hessian():
+    d_out, d_in = 4, 16
+    dwq = _rand_dwq(d_out, d_in, 10)
+    X = _calib(50, d_in, 11, spread=2.0)
+    r = O.init_select_calibrated(dwq, O.hessian(X), d_out * d_in, m=3)
+    C = O.transform(dwq)
+    assert np.allclose(r["x"], C.ravel(), rtol=1e-8, atol=1e-10 * np.abs(C).max())
+    assert O.layer_output_error(dwq, X, r["E"], r["x"]) < 1e-14 * np.sum((dwq @ X.T) ** 2)
+
+
+def test_refine_is_scale_invariant_in_the_calibration_set():
+    dwq = _rand_dwq(8, 32, 12)
+    X = _calib(80, 32, 13)
+    a = O.init_select_calibrated(dwq, O.hessian(X), 90, m=3)
+    b = O.init_select_calibrated(dwq, O.hessian(4.0 * X), 90, m=3)
+    assert np.array_equal(a["E"], b["E"])
+    assert np.allclose(b["w"], 4.0 * a["w"], rtol=1e-13)
+    assert np.allclose(a["x"], b["x"], rtol=1e-10)
+
+
+def test_cholesky_matches_numpy_and_flags_indefinite():
+    rng = np.random.default_rng(14)
+    B = rng.standard_normal((30, 12))
+    A = B.T @ B
+    L, ok = O.cholesky_lower(A)
+    assert ok and np.allclose(L, np.linalg.cholesky(A), rtol=1e-12, atol=1e-13)
+    low_rank = B[:5].T @ B[:5]             # rank 5 < 12: a pivot collapses to rounding
+    assert not O.cholesky_lower(low_rank)[1]
+    indef = A.copy()
+    indef[3, 3] = -1.0
+    assert not O.cholesky_lower(indef)[1]
+
+
+def test_refine_rows_without_a_definite_system_keep_the_dense_solution():
+    # 6 calibration tokens: rank(Hs) = 6, so rows with more than 6 positions
+    # have a singular G[S,S]
+    d_out, d_in = 6, 32
+    dwq = _rand_dwq(d_out, d_in, 15)
+    X = _calib(6, d_in, 16)
+    r = O.init_select_calibrated(dwq, O.hessian(X), 40, m=3)
+    big = r["budgets"] > 6
+    assert big.any() and (~big).any()
+    assert np.array_equal(r["ok"], ~big)
+    rows = np.repeat(np.arange(d_out), r["budgets"])
+    assert np.array_equal(r["c"][big[rows]], r["c_dense"][big[rows]])
+    # damping makes every system definite
+    d = O.init_select_calibrated(dwq, O.hessian(X), 40, m=3, damp=0.01)
+    assert d["ok"].all()
+    Hd = O.damped(O.hessian(X), 0.01)
+    assert np.allclose(np.diag(Hd) - np.diag(O.hessian(X)),
+                       0.01 * np.mean(np.diag(O.hessian(X))), rtol=1e-12)
