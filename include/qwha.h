@@ -180,6 +180,60 @@ qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_i
                                     hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Value Refinement with calibration data (papernotes.org, 关键设计 2 and 3,
+ * 损失函数 / 训练策略; gist.science §2.2).
+ *
+ * The init's objective is the layer-output error ||dW_Q X - F H^-1 X||_F^2
+ * on calibration activations; with the Hessian Hs = XX^T it splits into
+ * channels. Activations are token-major here ([N][d_in]), so Hs = X^T X.
+ *
+ * qwha_hessian: Hs (+)= X^T X in fp64 (X [N][d_in] fp32 or bf16, Hs
+ *   [d_in][d_in] fp64, both triangles written). accumulate = 1 adds to Hs,
+ *   which must then be symmetric (as this call leaves it): calibration
+ *   batches can be summed call by call. N = 0 leaves Hs (or zeros it).
+ *
+ * qwha_init_select_calibrated: the init of qwha_init_select with
+ *   Hs' = Hs + damp * mean(diag Hs) * I in place of the identity:
+ *   w_i = sqrt(dW_Q[i] Hs' dW_Q[i]^T) (the activation error magnitude) for
+ *   AdaAlloc; positions by the in-row top |C| (C = dW_Q H does not depend
+ *   on Hs); c = fp32(C[E]) (the dense solution, refined by the next call);
+ *   and the refinement system
+ *     G   [d_in][d_in] fp64 = H Hs' H / d_in^2,
+ *     rhs [p] fp64,  rhs_k = (dW_Q Hs' H / d_in)[i_k, j_k].
+ *   damp >= 0 (0 = no damping, the plain reading). Other requirements as
+ *   qwha_init_select, with a workspace of at least
+ *   qwha_init_calibrated_workspace_bytes(d_out, d_in) bytes (it holds
+ *   dW_Q Hs' and one d_in x d_in temporary, fp64).
+ *
+ * qwha_refine_values: for each row i with positions S = E_i, solves
+ *   x G[S,S] = rhs[S] (the normal equations of min_x ||v - x B'||^2,
+ *   v = dW_Q[i] R, B' the rows of H^-1 R at S) by Cholesky in fp64 and
+ *   writes c[S] = fp32(x). A row whose pivot falls to or below 1e-10 times
+ *   its diagonal entry of G (G[S,S] not positive definite) keeps its c
+ *   and counts in status[0]; a row whose system does not fit the workspace
+ *   keeps its c and counts in status[1] (status: device int32 [2], set by
+ *   the call). Needs qwha_refine_workspace_bytes(row_ptr_host, d_out)
+ *   bytes for every row to be solved, where row_ptr_host is a host copy of
+ *   row_ptr (0 when it is not a valid row_ptr); at least
+ *   8 * (d_out + 1) rounded up to 256 (QWHA_ERR_WORKSPACE otherwise).
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_hessian(const void* X, qwha_dtype x_dtype, int64_t N, int32_t d_in,
+                         double* Hs, int32_t accumulate, hipStream_t stream);
+size_t qwha_init_calibrated_workspace_bytes(int32_t d_out, int32_t d_in);
+qwha_status qwha_init_select_calibrated(const float* dWq, int32_t d_out, int32_t d_in,
+                                        const double* Hs, double damp, int64_t p,
+                                        int32_t min_per_row, double temperature,
+                                        int32_t* row_ptr, int32_t* E, float* c,
+                                        int32_t* col_ptr, int32_t* csc_perm, double* G,
+                                        double* rhs, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+size_t qwha_refine_workspace_bytes(const int32_t* row_ptr_host, int32_t d_out);
+qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const double* G,
+                               const double* rhs, int32_t d_out, int32_t d_in, int64_t p,
+                               float* c, int32_t* status, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Profiling aid: the next launch of kernel `kernel` made by this thread
  * (inside any entry point above) is bracketed by hipEventRecord(start) and
  * hipEventRecord(stop) on that launch's stream; the request is then
@@ -198,7 +252,11 @@ typedef enum qwha_kernel {
   QWHA_KERNEL_INIT_SELECT = 7,  /* fp64 transform + top-k inside qwha_init_select */
   QWHA_KERNEL_MATERIALIZE = 8,
   QWHA_KERNEL_FWHT = 9,         /* qwha_fwht */
-  QWHA_KERNEL_GLOBAL_THRESHOLD = 10 /* keys, radix select and budgets in qwha_init_select_global */
+  QWHA_KERNEL_GLOBAL_THRESHOLD = 10, /* keys, radix select and budgets in qwha_init_select_global */
+  QWHA_KERNEL_HESSIAN = 11,     /* qwha_hessian */
+  QWHA_KERNEL_CALIB_PREPARE = 12, /* dW_Q Hs, norms and Q inside qwha_init_select_calibrated */
+  QWHA_KERNEL_CALIB_SYSTEM = 13,  /* rhs gather and G inside qwha_init_select_calibrated */
+  QWHA_KERNEL_REFINE = 14       /* the per-row solves of qwha_refine_values */
 } qwha_kernel;
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 

@@ -20,7 +20,8 @@ from ._lib import QwhaError, check, lib  # noqa: F401
 __all__ = [
     "QWHA_F32", "QWHA_BF16", "QwhaError", "lib",
     "QWHA_SELECT_MAGNITUDE", "QWHA_SELECT_RANDOM",
-    "qwha_init_select", "qwha_init_select_global", "qwha_materialize", "qwha_fwd", "qwha_bwd",
+    "qwha_init_select", "qwha_init_select_global", "qwha_hessian",
+    "qwha_init_select_calibrated", "qwha_refine_values", "qwha_materialize", "qwha_fwd", "qwha_bwd",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
@@ -105,6 +106,69 @@ def qwha_init_select_global(dWq: torch.Tensor, p: int, strategy: str = "magnitud
                                       perm.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
           "qwha_init_select_global")
     return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm)
+
+
+# ---------------------------------------------------------------- calibration
+def qwha_hessian(X: torch.Tensor, Hs: Optional[torch.Tensor] = None,
+                 accumulate: bool = False) -> torch.Tensor:
+    """Hs (+)= X^T X in fp64 for calibration tokens X [N][d_in] (fp32/bf16)."""
+    N, d_in = X.shape
+    if Hs is None:
+        Hs = torch.empty((d_in, d_in), dtype=torch.float64, device=X.device)
+        accumulate = False
+    check(lib.qwha_hessian(_ptr(X) if N else None, _dt(X), N, d_in, _ptr(Hs), int(accumulate),
+                           _stream()), "qwha_hessian")
+    return Hs
+
+
+def qwha_init_select_calibrated(dWq: torch.Tensor, Hs: torch.Tensor, p: int,
+                                min_per_row: int = 3, temperature: float = 1.0,
+                                damp: float = 0.0,
+                                ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """The init with a calibration Hessian: positions and dense-solution
+    values as qwha_init_select (allocation by activation error norms), plus
+    the refinement system G [d_in][d_in] and rhs [p] (fp64)."""
+    d_out, d_in = dWq.shape
+    dev = dWq.device
+    row_ptr = torch.empty(d_out + 1, dtype=torch.int32, device=dev)
+    E = torch.empty((max(p, 1), 2), dtype=torch.int32, device=dev)[:p]
+    c = torch.empty(max(p, 1), dtype=torch.float32, device=dev)[:p]
+    col_ptr = torch.empty(d_in + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(p, 1), dtype=torch.int32, device=dev)[:p]
+    G = torch.empty((d_in, d_in), dtype=torch.float64, device=dev)
+    rhs = torch.empty(max(p, 1), dtype=torch.float64, device=dev)[:p]
+    need = lib.qwha_init_calibrated_workspace_bytes(d_out, d_in)
+    if ws is None:
+        ws = workspace(need, dev)
+    check(lib.qwha_init_select_calibrated(_ptr(dWq), d_out, d_in, _ptr(Hs), float(damp), p,
+                                          min_per_row, float(temperature), _ptr(row_ptr),
+                                          E.data_ptr(), c.data_ptr(), _ptr(col_ptr),
+                                          perm.data_ptr(), _ptr(G), rhs.data_ptr(),
+                                          ws.data_ptr(), ws.numel(), _stream()),
+          "qwha_init_select_calibrated")
+    return dict(row_ptr=row_ptr, E=E, c=c, col_ptr=col_ptr, csc_perm=perm, G=G, rhs=rhs)
+
+
+def refine_workspace_bytes(row_ptr: torch.Tensor) -> int:
+    host = row_ptr.detach().to("cpu", torch.int32).contiguous()
+    return lib.qwha_refine_workspace_bytes(host.data_ptr(), host.numel() - 1)
+
+
+def qwha_refine_values(row_ptr, E, G, rhs, c: torch.Tensor,
+                       ws: Optional[torch.Tensor] = None):
+    """Refined values in place of c (rows whose system is not definite, or
+    does not fit ws, keep theirs). Returns (c, status[2]) with status =
+    (rows not positive definite, rows skipped for workspace)."""
+    d_out = row_ptr.numel() - 1
+    d_in = G.shape[0]
+    p = c.numel()
+    status = torch.empty(2, dtype=torch.int32, device=c.device)
+    if ws is None:
+        ws = workspace(refine_workspace_bytes(row_ptr), c.device)
+    check(lib.qwha_refine_values(_ptr(row_ptr), E.data_ptr(), _ptr(G), rhs.data_ptr(), d_out,
+                                 d_in, p, c.data_ptr(), _ptr(status), ws.data_ptr(), ws.numel(),
+                                 _stream()), "qwha_refine_values")
+    return c, status
 
 
 # ---------------------------------------------------------------- materialize

@@ -35,6 +35,15 @@ SIGNATURES = {
     "qwha_init_select_global": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int32,
                                           ctypes.c_uint64, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qwha_hessian": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p]),
+    "qwha_init_calibrated_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+    "qwha_init_select_calibrated": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_double,
+                                              c_int64, c_int32, c_double, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_size_t, c_void_p]),
+    "qwha_refine_workspace_bytes": (c_size_t, [c_void_p, c_int32]),
+    "qwha_refine_values": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                     c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "qwha_materialize": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
                                    c_float, c_int32, c_void_p, c_int32, c_void_p]),
     "qwha_fwd_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),

@@ -19,8 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqwha.so")
 
-SOURCES = ["api.hip", "fwht.hip", "init.hip", "materialize.hip", "select_global.hip",
-           "spmm.hip"]
+SOURCES = ["api.hip", "fwht.hip", "init.hip", "materialize.hip", "refine.hip",
+           "select_global.hip", "spmm.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 ops stay off on gfx950 (the compiler would otherwise emit

@@ -32,7 +32,7 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 struct Hook {
   hipEvent_t start, stop;
 };
-constexpr int kNumKernelIds = 11;
+constexpr int kNumKernelIds = 15;
 thread_local Hook g_hook[kNumKernelIds] = {};
 
 // Runs `launch` (a callable returning hipError_t) for kernel id `k`, with the
@@ -263,6 +263,134 @@ qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_i
   return QWHA_OK;
 }
 
+// ------------------------------------------------------------------ calibration
+qwha_status qwha_hessian(const void* X, qwha_dtype x_dtype, int64_t N, int32_t d_in, double* Hs,
+                         int32_t accumulate, hipStream_t stream) {
+  g_err[0] = 0;
+  if (log2_pow2(d_in) < 0)
+    return fail(QWHA_ERR_SHAPE, "d_in=%d is not a power of two in [2, 16384]", d_in);
+  if (N < 0 || N > (static_cast<int64_t>(1) << 40))
+    return fail(QWHA_ERR_SHAPE, "N=%lld out of [0, 2^40]", static_cast<long long>(N));
+  QWHA_TRY(check_dt(x_dtype, "x_dtype"));
+  if (accumulate != 0 && accumulate != 1)
+    return fail(QWHA_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  QWHA_NEED(Hs, 16);
+  if (N > 0) QWHA_NEED(X, 16);
+  return hip_check(timed(QWHA_KERNEL_HESSIAN, stream,
+                         [&] {
+                           return launch_hessian(X, static_cast<Dt>(x_dtype), N, d_in, Hs,
+                                                 accumulate, stream);
+                         }),
+                   "hessian");
+}
+
+size_t qwha_init_calibrated_workspace_bytes(int32_t d_out, int32_t d_in) {
+  if (d_out < 1 || d_in < 1) return 0;
+  return align256(calibrated_scratch_bytes(d_out, d_in)) +
+         align256(adaalloc_scratch_bytes(d_out)) + align256(csc_scratch_bytes(d_out, d_in));
+}
+
+qwha_status qwha_init_select_calibrated(const float* dWq, int32_t d_out, int32_t d_in,
+                                        const double* Hs, double damp, int64_t p,
+                                        int32_t min_per_row, double temperature,
+                                        int32_t* row_ptr, int32_t* E, float* c,
+                                        int32_t* col_ptr, int32_t* csc_perm, double* G,
+                                        double* rhs, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  if (min_per_row < 0 || min_per_row > d_in)
+    return fail(QWHA_ERR_INVALID_ARG, "min_per_row=%d outside [0, d_in]", min_per_row);
+  if (!(temperature > 0.0) || !isfinite(temperature))
+    return fail(QWHA_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (!(damp >= 0.0) || !isfinite(damp))
+    return fail(QWHA_ERR_INVALID_ARG, "damp must be finite and >= 0");
+  QWHA_TRY(check_p(p, d_out, d_in));
+  if (p < static_cast<int64_t>(min_per_row) * d_out)
+    return fail(QWHA_ERR_BUDGET, "p=%lld < min_per_row*d_out=%lld", static_cast<long long>(p),
+                static_cast<long long>(min_per_row) * d_out);
+  QWHA_NEED(dWq, 16);
+  QWHA_NEED(Hs, 16);
+  QWHA_NEED(G, 16);
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(col_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+    QWHA_NEED(csc_perm, 4);
+    QWHA_NEED(rhs, 8);
+  }
+  const size_t cal = align256(calibrated_scratch_bytes(d_out, d_in));
+  const size_t alloc = align256(adaalloc_scratch_bytes(d_out));
+  const size_t total = cal + alloc + align256(csc_scratch_bytes(d_out, d_in));
+  if (workspace == nullptr || workspace_bytes < total)
+    return fail(QWHA_ERR_WORKSPACE, "calibrated init workspace needs %zu bytes", total);
+  QWHA_NEED(workspace, 256);
+
+  double* w = nullptr;
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_CALIB_PREPARE, stream,
+                           [&] {
+                             return launch_calib_prepare(dWq, d_out, log_n, Hs, damp, workspace,
+                                                         &w, stream);
+                           }),
+                     "calib_prepare"));
+  QWHA_TRY(hip_check(launch_adaalloc(w, d_out, d_in, p, min_per_row, temperature, row_ptr,
+                                     at(workspace, cal), stream),
+                     "adaalloc"));
+  QWHA_TRY(hip_check(launch_init_select(dWq, d_out, log_n, row_ptr, E, c, 0, nullptr, 0, stream),
+                     "init_select"));
+  QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
+                                      at(workspace, cal + alloc), stream),
+                     "csc_build"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_CALIB_SYSTEM, stream,
+                           [&] {
+                             return launch_calib_finish(E, p, d_out, log_n, Hs, workspace, G, rhs,
+                                                        stream);
+                           }),
+                     "calib_system"));
+  return QWHA_OK;
+}
+
+size_t qwha_refine_workspace_bytes(const int32_t* row_ptr_host, int32_t d_out) {
+  if (row_ptr_host == nullptr || d_out < 1 || row_ptr_host[0] != 0) return 0;
+  size_t n = 0;
+  for (int32_t i = 0; i < d_out; ++i) {
+    const int64_t pi = static_cast<int64_t>(row_ptr_host[i + 1]) - row_ptr_host[i];
+    if (pi < 0) return 0;
+    n += static_cast<size_t>((pi + 1) * (pi + 2) / 2);
+  }
+  return refine_header_bytes(d_out) + 8 * n;
+}
+
+qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const double* G,
+                               const double* rhs, int32_t d_out, int32_t d_in, int64_t p,
+                               float* c, int32_t* status, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(G, 8);
+  QWHA_NEED(status, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(rhs, 8);
+    QWHA_NEED(c, 4);
+  }
+  const size_t hb = refine_header_bytes(d_out);
+  if (workspace == nullptr || workspace_bytes < hb)
+    return fail(QWHA_ERR_WORKSPACE, "refine workspace needs at least %zu bytes", hb);
+  QWHA_NEED(workspace, 256);
+  return hip_check(timed(QWHA_KERNEL_REFINE, stream,
+                         [&] {
+                           return launch_refine(row_ptr, E, G, d_in, rhs, d_out, c, status,
+                                                workspace, workspace_bytes, 1e-10, stream);
+                         }),
+                   "refine");
+}
+
 // ------------------------------------------------------------------ materialize
 qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const float* c,
                              int32_t d_out, int32_t d_in, int64_t p, float alpha,
@@ -462,7 +590,7 @@ qwha_status qwha_fwht(const void* in, qwha_dtype in_dtype, void* out, qwha_dtype
 
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
   g_err[0] = 0;
-  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_GLOBAL_THRESHOLD ||
+  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_REFINE ||
       kernel >= kNumKernelIds)
     return fail(QWHA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
   if (kernel == QWHA_KERNEL_NONE) {

@@ -38,6 +38,24 @@ size_t csc_scratch_bytes(int d_out, int d_in);
 hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
                             int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s);
 
+// ---- refinement with a calibration Hessian (refine.hip)
+// Hs (+)= X^T X, fp64 [d_in][d_in], X [N][d_in] in x_dt
+hipError_t launch_hessian(const void* X, Dt x_dt, int64_t N, int d_in, double* Hs,
+                          int accumulate, hipStream_t s);
+size_t calibrated_scratch_bytes(int d_out, int d_in);
+// delta = damp * mean(diag Hs); M = dW_Q Hs; per row w_i (activation error
+// norm, returned in *w_out, inside the scratch) and Q = (M + delta dW_Q) H / n
+hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const double* Hs,
+                                double damp, void* scratch, double** w_out, hipStream_t s);
+// rhs[k] = Q[E_k]; G = H Hs H / n^2 + (delta / n) I
+hipError_t launch_calib_finish(const int32_t* E, int64_t p, int d_out, int log_n,
+                               const double* Hs, void* scratch, double* G, double* rhs,
+                               hipStream_t s);
+size_t refine_header_bytes(int d_out);
+hipError_t launch_refine(const int32_t* row_ptr, const int32_t* E, const double* G, int d_in,
+                         const double* rhs, int d_out, float* c, int32_t* status, void* ws,
+                         size_t ws_bytes, double pivot_tol, hipStream_t s);
+
 // ---- materialize
 hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                               int log_n, float alpha, Dt out_dt, void* dW, int accumulate,

@@ -28,6 +28,7 @@ __all__ = [
     "config_specs",
     "make_layer",
     "make_activations",
+    "make_calibration",
     "rtn_quantize",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -205,6 +206,25 @@ def make_activations(spec: LayerSpec, seed: int = 0, T: Optional[int] = None,
     x = _draw(ss_x, (T, spec.d_in), spec.act)
     dy = _draw(ss_dy, (T, spec.d_out), spec.act)
     return x, dy
+
+
+def make_calibration(d_in: int, N: int, seed: int = 0, act: str = "bf16",
+                     outlier_channels: float = 0.005, outlier_mult: float = 10.0,
+                     channel_spread: float = 0.5) -> np.ndarray:
+    """Calibration activations X [N][d_in], the stand-in for the WikiText-2
+    tokens the init is calibrated on: N(0,1) entries times a per-channel
+    scale exp(channel_spread * N(0,1)), with a seeded `outlier_channels`
+    fraction of channels (at least one) scaled by `outlier_mult` -- the
+    channel-wise outliers of LLM activations. bf16 as uint16 bit patterns
+    (round-to-nearest-even) or float32."""
+    ss_s, ss_o, ss_x = np.random.SeedSequence([int(seed), 2000, int(d_in)]).spawn(3)
+    scale = np.exp(channel_spread * np.random.default_rng(ss_s).standard_normal(d_in))
+    n_out = max(1, int(round(outlier_channels * d_in)))
+    idx = np.random.default_rng(ss_o).choice(d_in, size=min(n_out, d_in), replace=False)
+    scale[idx] *= outlier_mult
+    x = np.random.default_rng(ss_x).standard_normal((N, d_in)) * scale
+    x = x.astype(np.float32)
+    return f32_to_bf16_bits(x) if act == "bf16" else x
 
 
 def act_to_f64(a: np.ndarray) -> np.ndarray:

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from tests.conftest import ROOT
@@ -134,6 +135,64 @@ def test_init_global_validation(q):
     assert call(st=2, wsb=q.qwha_init_global_workspace_bytes(256, 256, 2) - 1) == WORKSPACE
     assert call(st=2, ws=FAKE + 16, wsb=1 << 30) == ALIGN
     assert call(seed=(1 << 64) - 1, ws=None) == WORKSPACE     # full 64-bit seeds accepted
+
+
+def test_calibration_validation(q):
+    # qwha_hessian(X, dtype, N, d_in, Hs, accumulate, stream)
+    assert q.qwha_hessian(FAKE, 0, 10, 24, FAKE, 0, None) == SHAPE
+    assert q.qwha_hessian(FAKE, 0, -1, 64, FAKE, 0, None) == SHAPE
+    assert q.qwha_hessian(FAKE, 3, 10, 64, FAKE, 0, None) == DTYPE
+    assert q.qwha_hessian(FAKE, 0, 10, 64, FAKE, 2, None) == INVALID
+    assert q.qwha_hessian(FAKE, 0, 10, 64, None, 0, None) == INVALID
+    assert q.qwha_hessian(FAKE + 4, 1, 10, 64, FAKE, 0, None) == ALIGN
+    assert q.qwha_hessian(None, 0, 10, 64, FAKE, 0, None) == INVALID
+
+    def init(**kw):
+        a = dict(dWq=FAKE, d_out=256, d_in=256, Hs=FAKE, damp=0.0, p=2048, m=3, t=1.0,
+                 row_ptr=FAKE, E=FAKE, c=FAKE, col_ptr=FAKE, perm=FAKE, G=FAKE, rhs=FAKE,
+                 ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_init_select_calibrated(
+            a["dWq"], a["d_out"], a["d_in"], a["Hs"], a["damp"], a["p"], a["m"], a["t"],
+            a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["perm"], a["G"], a["rhs"], a["ws"],
+            a["wsb"], None)
+    assert init(damp=-0.1) == INVALID
+    assert init(damp=float("inf")) == INVALID
+    assert init(p=3 * 256 - 1) == BUDGET
+    assert init(Hs=None) == INVALID
+    assert init(G=FAKE + 8) == ALIGN
+    assert init(rhs=None) == INVALID
+    assert init(d_in=96) == SHAPE
+    assert init() == WORKSPACE
+    need = q.qwha_init_calibrated_workspace_bytes(256, 256)
+    assert need >= 256 * 256 * 8 * 2       # dW_Q Hs and one d_in x d_in temporary
+    assert init(wsb=need - 1) == WORKSPACE
+
+    def refine(**kw):
+        a = dict(row_ptr=FAKE, E=FAKE, G=FAKE, rhs=FAKE, d_out=4, d_in=64, p=20, c=FAKE,
+                 status=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_refine_values(a["row_ptr"], a["E"], a["G"], a["rhs"], a["d_out"],
+                                    a["d_in"], a["p"], a["c"], a["status"], a["ws"], a["wsb"],
+                                    None)
+    assert refine(d_in=63) == SHAPE
+    assert refine(p=4 * 64 + 1) == BUDGET
+    assert refine(status=None) == INVALID
+    assert refine(rhs=None) == INVALID
+    assert refine() == WORKSPACE
+    assert refine(ws=FAKE + 16, wsb=1 << 20) == ALIGN
+
+
+def test_refine_workspace_query_on_host_row_ptr(q):
+    rp = np.array([0, 3, 3, 10, 11], dtype=np.int32)
+    got = q.qwha_refine_workspace_bytes(rp.ctypes.data, 4)
+    tri = sum((k + 1) * (k + 2) // 2 for k in np.diff(rp))     # augmented triangles
+    header = ((5 * 8 + 255) // 256) * 256
+    assert got == header + 8 * tri
+    assert q.qwha_refine_workspace_bytes(None, 4) == 0
+    bad = np.array([0, 3, 2, 4, 5], dtype=np.int32)
+    assert q.qwha_refine_workspace_bytes(bad.ctypes.data, 4) == 0
+    assert q.qwha_refine_workspace_bytes(np.array([1, 2], np.int32).ctypes.data, 1) == 0
 
 
 def test_bwd_materialize_fwht_validation(q):
