@@ -34,6 +34,9 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X vector fp32 (packed FMA)
 K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_FWHT_X=3, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC_REDUCE=6,
          INIT_SELECT=7, MATERIALIZE=8)
 GLOBAL_THRESHOLD = 10
+KR = dict(HESSIAN=11, CALIB_PREPARE=12, CALIB_SYSTEM=13, REFINE=14)
+FP64_MFMA_PEAK_TFLOPS = 78.6     # MI355X dense fp64 matrix
+FP64_VECTOR_PEAK_TFLOPS = 78.6   # MI355X fp64 vector
 
 
 def parse():
@@ -44,6 +47,9 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--sets", type=int, default=4, help="rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--refine-tokens", type=int, default=32768,
+                    help="calibration tokens for the refinement measurement (0: skip)")
+    ap.add_argument("--refine-reps", type=int, default=3)
     ap.add_argument("--variant-reps", type=int, default=10,
                     help="timed calls of each init selection strategy (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -262,6 +268,10 @@ def main():
         out["init_variants"] = init_variants(args.variant_reps, sets, (d_out, d_in, p),
                                              (row_ptr, E, c, col_ptr, perm), ws_i, stream, hip)
 
+    if args.refine_tokens > 0 and args.refine_reps > 0:
+        out["refine"] = refine_measure(args.refine_tokens, args.refine_reps, spec, sets[0][0],
+                                       stream, hip)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens or T)
     print(json.dumps(out), flush=True)
@@ -334,6 +344,83 @@ def init_variants(reps, sets, dims, outs, ws_i, stream, hip):
     return res
 
 
+def refine_measure(N, reps, spec, dwq, stream, hip):
+    """Time the init with a calibration Hessian on the layer: Hs = X^T X over
+    N synthetic bf16 calibration tokens (qwha_hessian), the calibrated init
+    (qwha_init_select_calibrated: dW_Q Hs, norms, AdaAlloc, selection, G and
+    rhs) and the per-row solves (qwha_refine_values). Rates: the Hessian's
+    N d_in (d_in + 1) flops (a symmetric rank-N update) against the fp64
+    matrix-core peak; dW_Q Hs's 2 d_out d_in^2 flops inside the preparation
+    step; the solves' sum over rows of (p_i + 1)^3 / 3 flops (Cholesky of the
+    augmented system) + p_i^2 (back substitution) against the fp64 vector peak."""
+    import numpy as np
+    import torch
+    import synth
+    import quantization_aware_sparse_amd as q
+    from quantization_aware_sparse_amd import check, lib
+    d_out, d_in, p = spec.d_out, spec.d_in, spec.p
+    X = synth.make_calibration(d_in, N, seed=1, act="bf16")
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    del X
+    Hs = torch.empty((d_in, d_in), dtype=torch.float64, device="cuda:0")
+    got = None
+    ev = {k: (hip.create(), hip.create()) for k in list(KR) + ["WHOLE"]}
+    times = {k: [] for k in ev}
+    ws_c = q.workspace(lib.qwha_init_calibrated_workspace_bytes(d_out, d_in), "cuda:0")
+    ws_r = None
+    status = torch.empty(2, dtype=torch.int32, device="cuda:0")
+    for r in range(reps + 1):
+        timed_rep = r > 0
+        if timed_rep:
+            for k, kid in KR.items():
+                check(lib.qwha_profile_next(kid, ev[k][0], ev[k][1]), "profile")
+            hip.record(ev["WHOLE"][0], stream)
+        check(lib.qwha_hessian(Xd.data_ptr(), q.QWHA_BF16, N, d_in, Hs.data_ptr(), 0, stream),
+              "hessian")
+        got = q.qwha_init_select_calibrated(dwq, Hs, p, 3, ws=ws_c)
+        if ws_r is None:
+            ws_r = q.workspace(q.refine_workspace_bytes(got["row_ptr"]), "cuda:0")
+        check(lib.qwha_refine_values(got["row_ptr"].data_ptr(), got["E"].data_ptr(),
+                                     got["G"].data_ptr(), got["rhs"].data_ptr(), d_out, d_in, p,
+                                     got["c"].data_ptr(), status.data_ptr(), ws_r.data_ptr(),
+                                     ws_r.numel(), stream), "refine")
+        if timed_rep:
+            hip.record(ev["WHOLE"][1], stream)
+        torch.cuda.synchronize()
+        if timed_rep:
+            for k in ev:
+                times[k].append(hip.elapsed_ms(*ev[k]))
+    us = {k: 1e3 * float(np.mean(v)) for k, v in times.items()}
+    budgets = np.diff(got["row_ptr"].cpu().numpy().astype(np.int64))
+    refine_flops = float(np.sum((budgets + 1.0) ** 3 / 3.0 + budgets.astype(np.float64) ** 2))
+    hess_flops = float(N) * d_in * (d_in + 1)
+    gemm_flops = 2.0 * d_out * d_in * d_in
+    a_h = hess_flops / (us["HESSIAN"] * 1e-6) / 1e12
+    a_g = gemm_flops / (us["CALIB_PREPARE"] * 1e-6) / 1e12
+    a_r = refine_flops / (us["REFINE"] * 1e-6) / 1e12
+    return {
+        "calibration": f"{N} synthetic bf16 tokens (per-channel scales, 0.5% x10 outlier "
+                       "channels)",
+        "reps": reps,
+        "status": status.cpu().tolist(),
+        "whole_us": round(us["WHOLE"], 1),
+        "hessian_us": round(us["HESSIAN"], 1),
+        "calib_prepare_us": round(us["CALIB_PREPARE"], 1),
+        "calib_system_us": round(us["CALIB_SYSTEM"], 1),
+        "refine_us": round(us["REFINE"], 1),
+        "hessian_roofline": dict(bound="mfma", achieved=round(a_h, 2), unit="TFLOP/s",
+                                 peak=FP64_MFMA_PEAK_TFLOPS,
+                                 frac=round(a_h / FP64_MFMA_PEAK_TFLOPS, 4), dtype="f64"),
+        "calib_gemm_roofline": dict(bound="mfma", achieved=round(a_g, 2), unit="TFLOP/s",
+                                    peak=FP64_MFMA_PEAK_TFLOPS,
+                                    frac=round(a_g / FP64_MFMA_PEAK_TFLOPS, 4), dtype="f64",
+                                    note="time of the whole preparation step"),
+        "refine_rate": dict(bound="alu", achieved=round(a_r, 3), unit="TFLOP/s",
+                            peak=FP64_VECTOR_PEAK_TFLOPS,
+                            frac=round(a_r / FP64_VECTOR_PEAK_TFLOPS, 4), dtype="f64"),
+    }
+
+
 # library sources that define each timed kernel (besides the shared headers
 # and the launch layer, which every kernel depends on)
 KERNEL_SOURCES = {
@@ -342,6 +429,8 @@ KERNEL_SOURCES = {
     "BWD_SPMM": ["spmm.hip"], "BWD_DC_REDUCE": ["spmm.hip"],
     "INIT_SELECT": ["init.hip", "fwht_core.h"], "MATERIALIZE": ["materialize.hip", "fwht_core.h"],
     "GLOBAL_THRESHOLD": ["select_global.hip", "fwht_core.h"],
+    "HESSIAN": ["refine.hip", "fwht_core.h"], "CALIB_PREPARE": ["refine.hip", "fwht_core.h"],
+    "CALIB_SYSTEM": ["refine.hip", "fwht_core.h"], "REFINE": ["refine.hip", "fwht_core.h"],
 }
 SHARED_SOURCES = ["common.h", "launch.h", "api.hip"]
 

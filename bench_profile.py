@@ -23,7 +23,7 @@ import re
 import bench
 
 # ids timed over several kernels: listed in the table, no per-launch traffic line
-MULTI_KERNEL_IDS = {"GLOBAL_THRESHOLD"}
+MULTI_KERNEL_IDS = {"GLOBAL_THRESHOLD", "CALIB_PREPARE", "CALIB_SYSTEM", "REFINE"}
 # ids with no bench.py event of their own: listed in the table only
 TABLE_ONLY_IDS = {"INIT_SELECT_GLOBAL"}
 
@@ -38,11 +38,21 @@ KERNEL_IDS = {
     "row_ties_kernel": ["GLOBAL_THRESHOLD"],
     "global_budget_kernel": ["GLOBAL_THRESHOLD"],
     "gsel_init_kernel": ["GLOBAL_THRESHOLD"],
+    # calibrated init and refinement
+    "delta_kernel": ["CALIB_PREPARE"],
+    "calib_rows_kernel": ["CALIB_PREPARE"],
+    "fwht64_rows_kernel": ["CALIB_SYSTEM"],
+    "transpose64_kernel": ["CALIB_SYSTEM"],
+    "rhs_gather_kernel": ["CALIB_SYSTEM"],
+    "refine_offsets_kernel": ["REFINE"],
+    "refine_kernel": ["REFINE"],
+    "fill_i32_kernel": ["REFINE"],
 }
 
 
 def short(name: str) -> str:
-    n = re.sub(r"\(.*", "", name)
+    n = name.replace("(anonymous namespace)::", "")
+    n = re.sub(r"\(.*", "", n)
     return n.replace("qwha::", "").replace("void ", "")
 
 
@@ -57,6 +67,9 @@ def kernel_ids(name: str):
     if n.startswith("rows_kernel<"):
         # the plain gather: forward (source z, fp32); bench.py's backward always forms dc
         return ["FWD_SPMM"] if template_args(n)[0] == "float" else []
+    if n.startswith("gemm64_kernel<"):
+        # A read k-major (calibration tokens): the Hessian; else dW_Q Hs
+        return ["HESSIAN"] if template_args(n)[1] == "true" else ["CALIB_PREPARE"]
     if n.startswith("init_select_kernel<"):
         # the AdaAlloc instance (selection mode 0) is the one of the step
         return ["INIT_SELECT"] if template_args(n)[1] == "0" else ["INIT_SELECT_GLOBAL"]
