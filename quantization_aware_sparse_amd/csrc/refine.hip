@@ -11,8 +11,9 @@
 //
 // Kernels (all fp64):
 //   gemm64_kernel      dense products on the fp64 matrix cores
-//                      (v_mfma_f64_16x16x4): Hs = X^T X (symmetric: lower
-//                      tiles only, mirrored) and M = dW_Q Hs;
+//                      (v_mfma_f64_16x16x4): Hs = X^T X (symmetric: 64x64
+//                      tiles on and below the diagonal, mirrored) and
+//                      M = dW_Q Hs (128x128 tiles);
 //   calib_rows_kernel  per row of M: w_i and Q[i,:] = (M + delta dW_Q)[i,:] H/n;
 //   fwht64_rows_kernel + transpose64_kernel: G = H (H Hs)^T / n^2 (Hs is
 //                      symmetric), plus delta/n on the diagonal;
@@ -30,63 +31,82 @@ namespace {
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ GEMM
-constexpr int kGT = 128;   // workgroup tile, M and N
 constexpr int kGK = 16;    // K per staged chunk
-constexpr int kGLd = kGT + 4;   // LDS row stride (doubles)
 
 __device__ __forceinline__ double to_f64(float v) { return static_cast<double>(v); }
 __device__ __forceinline__ double to_f64(uint16_t v) { return static_cast<double>(bf16_to_f32(v)); }
 __device__ __forceinline__ double to_f64(double v) { return v; }
 
-// 8 consecutive elements starting at p; `valid` of them in range (<= 0: none).
-// VEC: p is 16-byte aligned whenever valid >= 8.
-template <typename T, bool VEC>
-__device__ __forceinline__ void load8(const T* p, int valid, double* v) {
-  if (VEC && valid >= 8) {
-    if constexpr (sizeof(T) == 4) {
-      const float4* q = reinterpret_cast<const float4*>(p);
-      const float4 f0 = q[0], f1 = q[1];
-      v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
-      v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
-    } else if constexpr (sizeof(T) == 2) {
+// EPT (4 or 8) consecutive elements at p, 16-byte vector loads (p aligned
+// to EPT elements), times `mask` (0 or 1).
+template <typename T, int EPT>
+__device__ __forceinline__ void load_vec(const T* p, double mask, double* v) {
+  if constexpr (sizeof(T) == 4) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < EPT / 4; ++i) {
+      const float4 f = q[i];
+      v[4 * i] = f.x * mask;
+      v[4 * i + 1] = f.y * mask;
+      v[4 * i + 2] = f.z * mask;
+      v[4 * i + 3] = f.w * mask;
+    }
+  } else if constexpr (sizeof(T) == 2) {
+    uint32_t w[EPT / 2];
+    if constexpr (EPT == 8) {
       const uint4 u = *reinterpret_cast<const uint4*>(p);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = static_cast<double>(__uint_as_float(w[i] << 16));
-        v[2 * i + 1] = static_cast<double>(__uint_as_float(w[i] & 0xFFFF0000u));
-      }
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
     } else {
-      const double2* q = reinterpret_cast<const double2*>(p);
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double2 d = q[i];
-        v[2 * i] = d.x;
-        v[2 * i + 1] = d.y;
-      }
+    for (int i = 0; i < EPT / 2; ++i) {
+      v[2 * i] = static_cast<double>(__uint_as_float(w[i] << 16)) * mask;
+      v[2 * i + 1] = static_cast<double>(__uint_as_float(w[i] & 0xFFFF0000u)) * mask;
     }
   } else {
+    const double2* q = reinterpret_cast<const double2*>(p);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = r < valid ? to_f64(p[r]) : 0.0;
+    for (int i = 0; i < EPT / 2; ++i) {
+      const double2 d = q[i];
+      v[2 * i] = d.x * mask;
+      v[2 * i + 1] = d.y * mask;
+    }
   }
+}
+
+// EPT consecutive elements at p, `valid` of them in range (<= 0: none).
+template <typename T, int EPT>
+__device__ __forceinline__ void load_guarded(const T* p, int valid, double* v) {
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) v[r] = r < valid ? to_f64(p[r]) : 0.0;
 }
 
 // C[m][n] = (accumulate ? C[m][n] : 0) + sum_k A(m,k) B(k,n), fp64, with
 //   A(m,k) = A_KM ? a[k*lda + m] : a[m*lda + k],   B(k,n) = b[k*ldb + n].
-// 256 threads, a 128x128 tile per workgroup, 64x64 per wave as 4x4 blocks of
-// v_mfma_f64_16x16x4 (operand lane l: row/column l%16, k l/16; result lane l
-// register r: row l/16 + 4r, column l%16). K is staged 16 at a time through
-// LDS, the next chunk's global loads in flight during the current MFMAs.
+// 256 threads; a TT x TT tile per workgroup (TT = 32 WB), a quarter of it per
+// wave as WB x WB blocks of v_mfma_f64_16x16x4 (operand lane l: row/column
+// l%16, k l/16; result lane l register r: row l/16 + 4r, column l%16). K is
+// staged 16 at a time through LDS, the next chunk's global loads in flight
+// during the current MFMAs.
+// VEC: 16-byte loads with no per-element tests: requires N % TT == 0,
+// M % TT == 0 when A is k-major, lda % 8 == 0 and K % 16 == 0 when A is
+// m-major, ldb % 8 == 0 and 16-byte aligned a, b; rows past M or K are read
+// at a clamped row and multiplied by 0. Otherwise every element is tested.
 // SYM (A and B the same matrix, M == N): only tiles on or below the
 // diagonal are computed, each stored at (m,n) and (n,m); with accumulate the
 // old C must be symmetric.
-template <typename TA, bool A_KM, typename TB, bool VEC, bool SYM>
-__global__ __launch_bounds__(256) void gemm64_kernel(const TA* __restrict__ a, int64_t lda,
+template <typename TA, bool A_KM, typename TB, bool VEC, bool SYM, int WB>
+__global__ __launch_bounds__(256, 2) void gemm64_kernel(const TA* __restrict__ a, int64_t lda,
                                                      const TB* __restrict__ b, int64_t ldb,
                                                      double* __restrict__ c, int64_t ldc, int M,
                                                      int N, int64_t K, int accumulate) {
-  __shared__ double As[kGK][kGLd];
-  __shared__ double Bs[kGK][kGLd];
+  constexpr int TT = 32 * WB;          // workgroup tile
+  constexpr int EPT = TT / 16;         // staged elements per thread and operand
+  constexpr int LDW = TT + 4;          // LDS row stride (doubles)
+  __shared__ double As[kGK][LDW];
+  __shared__ double Bs[kGK][LDW];
   int tm, tn;
   if (SYM) {
     const int q = blockIdx.x;
@@ -99,48 +119,62 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const TA* __restrict__ a, i
     tm = blockIdx.y;
     tn = blockIdx.x;
   }
-  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int m0 = tm * TT, n0 = tn * TT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (TT / 2), wn = (w & 1) * (TT / 2);
 
-  v4d acc[4][4];
+  v4d acc[WB][WB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < WB; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
 
-  double ra[8], rb[8];
+  // staging coordinates: k-major operands take row kk = tid / 16 and
+  // columns (tid % 16) * EPT; the m-major A takes row tid / (16 / EPT)
+  // and k offset (tid % (16 / EPT)) * EPT
+  const int kk_km = tid >> 4, col_km = (tid & 15) * EPT;
+  constexpr int TPR = 16 / EPT;
+  const int mm_mk = tid / TPR, kk_mk = (tid % TPR) * EPT;
+  double ra[EPT], rb[EPT];
   auto fetch = [&](int64_t k0) {
     if (A_KM) {
-      const int kk = tid >> 4, mm = (tid & 15) * 8;
-      const int64_t k = k0 + kk;
-      const int valid = k < K ? M - (m0 + mm) : 0;
-      load8<TA, VEC>(a + k * lda + m0 + mm, valid, ra);
+      const int64_t k = k0 + kk_km;
+      if (VEC) {
+        const int64_t kc = k < K ? k : K - 1;
+        load_vec<TA, EPT>(a + kc * lda + m0 + col_km, k < K ? 1.0 : 0.0, ra);
+      } else {
+        load_guarded<TA, EPT>(a + k * lda + m0 + col_km, k < K ? M - (m0 + col_km) : 0, ra);
+      }
     } else {
-      const int mm = tid >> 1, kk = (tid & 1) * 8;
-      const int m = m0 + mm;
-      const int64_t left = K - (k0 + kk);
-      const int valid = m < M ? static_cast<int>(left < 8 ? left : 8) : 0;
-      load8<TA, VEC>(a + static_cast<int64_t>(m) * lda + k0 + kk, valid, ra);
+      const int m = m0 + mm_mk;
+      if (VEC) {
+        const int mc = m < M ? m : M - 1;
+        load_vec<TA, EPT>(a + static_cast<int64_t>(mc) * lda + k0 + kk_mk, m < M ? 1.0 : 0.0,
+                          ra);
+      } else {
+        const int64_t left = K - (k0 + kk_mk);
+        const int valid = m < M ? static_cast<int>(left < EPT ? left : EPT) : 0;
+        load_guarded<TA, EPT>(a + static_cast<int64_t>(m) * lda + k0 + kk_mk, valid, ra);
+      }
     }
-    const int kk = tid >> 4, nn = (tid & 15) * 8;
-    const int64_t k = k0 + kk;
-    const int valid = k < K ? N - (n0 + nn) : 0;
-    load8<TB, VEC>(b + k * ldb + n0 + nn, valid, rb);
+    const int64_t k = k0 + kk_km;
+    if (VEC) {
+      const int64_t kc = k < K ? k : K - 1;
+      load_vec<TB, EPT>(b + kc * ldb + n0 + col_km, k < K ? 1.0 : 0.0, rb);
+    } else {
+      load_guarded<TB, EPT>(b + k * ldb + n0 + col_km, k < K ? N - (n0 + col_km) : 0, rb);
+    }
   };
   auto stage = [&]() {
     if (A_KM) {
-      const int kk = tid >> 4, mm = (tid & 15) * 8;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) As[kk][mm + r] = ra[r];
+      for (int r = 0; r < EPT; ++r) As[kk_km][col_km + r] = ra[r];
     } else {
-      const int mm = tid >> 1, kk = (tid & 1) * 8;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) As[kk + r][mm] = ra[r];
+      for (int r = 0; r < EPT; ++r) As[kk_mk + r][mm_mk] = ra[r];
     }
-    const int kk = tid >> 4, nn = (tid & 15) * 8;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) Bs[kk][nn + r] = rb[r];
+    for (int r = 0; r < EPT; ++r) Bs[kk_km][col_km + r] = rb[r];
   };
 
   if (K > 0) fetch(0);
@@ -152,23 +186,23 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const TA* __restrict__ a, i
 #pragma unroll
     for (int ks = 0; ks < kGK; ks += 4) {
       const int kr = ks + (lane >> 4);
-      double af[4], bf[4];
+      double af[WB], bf[WB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = As[kr][wm + i * 16 + (lane & 15)];
+      for (int i = 0; i < WB; ++i) af[i] = As[kr][wm + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = Bs[kr][wn + j * 16 + (lane & 15)];
+      for (int j = 0; j < WB; ++j) bf[j] = Bs[kr][wn + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm + i * 16 + (lane >> 4) + 4 * r;
@@ -183,20 +217,22 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const TA* __restrict__ a, i
       }
 }
 
-template <typename TA, bool A_KM, typename TB, bool SYM>
+template <typename TA, bool A_KM, typename TB, bool SYM, int WB>
 hipError_t gemm64_t(const TA* a, int64_t lda, const TB* b, int64_t ldb, double* c, int64_t ldc,
                     int M, int N, int64_t K, int accumulate, hipStream_t s) {
-  const bool vec = (lda % 8 == 0) && (ldb % 8 == 0) &&
+  constexpr int TT = 32 * WB;
+  const bool vec = (lda % 8 == 0) && (ldb % 8 == 0) && (N % TT == 0) &&
+                   (!A_KM || M % TT == 0) && (A_KM || K % kGK == 0) &&
                    (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(b) % 16 == 0);
-  const int tm = (M + kGT - 1) / kGT, tn = (N + kGT - 1) / kGT;
+  const int tm = (M + TT - 1) / TT, tn = (N + TT - 1) / TT;
   const dim3 grid = SYM ? dim3(tm * (tm + 1) / 2) : dim3(tn, tm);
   if (vec)
-    hipLaunchKernelGGL((gemm64_kernel<TA, A_KM, TB, true, SYM>), grid, dim3(256), 0, s, a, lda,
-                       b, ldb, c, ldc, M, N, K, accumulate);
+    hipLaunchKernelGGL((gemm64_kernel<TA, A_KM, TB, true, SYM, WB>), grid, dim3(256), 0, s, a,
+                       lda, b, ldb, c, ldc, M, N, K, accumulate);
   else
-    hipLaunchKernelGGL((gemm64_kernel<TA, A_KM, TB, false, SYM>), grid, dim3(256), 0, s, a, lda,
-                       b, ldb, c, ldc, M, N, K, accumulate);
+    hipLaunchKernelGGL((gemm64_kernel<TA, A_KM, TB, false, SYM, WB>), grid, dim3(256), 0, s, a,
+                       lda, b, ldb, c, ldc, M, N, K, accumulate);
   return hipGetLastError();
 }
 
@@ -326,6 +362,15 @@ constexpr int kST = 64;   // trailing-update tile
 
 __device__ __forceinline__ int64_t tri(int64_t a) { return a * (a + 1) / 2; }
 
+// v (fp64) of lane `lane` (wave-uniform index), broadcast to the wave
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
 // off[i] = sum over rows i' < i of tri(p_i' + 1): start (in doubles) of row
 // i's packed augmented triangle; off[d_out] = total. One workgroup.
 __global__ __launch_bounds__(1024) void refine_offsets_kernel(const int32_t* __restrict__ row_ptr,
@@ -426,29 +471,48 @@ __global__ __launch_bounds__(256) void refine_kernel(const int32_t* __restrict__
       const int r = e / kNB, cc = e % kNB;
       Ld[r][cc] = (r < nb && cc <= r) ? T[tri(k0 + r) + k0 + cc] : 0.0;
     }
-    if (tid == 0) bad = 0;
     __syncthreads();
-    for (int k = 0; k < nb; ++k) {
-      if (tid == 0) {
-        const double piv = Ld[k][k];
-        const int sk = S[2 * (k0 + k)];
-        const double d0 = G[static_cast<int64_t>(sk) * ld + sk];
-        if (piv > pivot_tol * d0)
-          Ld[k][k] = sqrt(piv);
-        else
-          bad = 1;
+    // factor the diagonal block in wave 0, lane r holding row r in
+    // registers; pivots and column entries are broadcast by readlane. A
+    // pivot at or below pivot_tol times the entry's original value
+    // G[S_k][S_k] stops the row.
+    if (tid < 64) {
+      const int r = tid;
+      double arow[kNB];
+#pragma unroll
+      for (int cc = 0; cc < kNB; ++cc) arow[cc] = (r < nb && cc <= r) ? Ld[r][cc] : 0.0;
+      double dg = 0.0;
+      if (r < nb) {
+        const int sr = S[2 * (k0 + r)];
+        dg = G[static_cast<int64_t>(sr) * ld + sr];
       }
-      __syncthreads();
-      if (bad) break;
-      const double dk = Ld[k][k];
-      for (int r = k + 1 + tid; r < nb; r += 256) Ld[r][k] /= dk;
-      __syncthreads();
-      for (int e = tid; e < kNB * kNB; e += 256) {
-        const int r = e / kNB, cc = e % kNB;
-        if (cc > k && cc <= r && r < nb) Ld[r][cc] -= Ld[r][k] * Ld[cc][k];
+      int ok = 1;
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        if (k < nb && ok) {
+          const double piv = readlane_f64(arow[k], k);
+          if (!(piv > pivot_tol * readlane_f64(dg, k))) {
+            ok = 0;
+          } else {
+            const double dk = sqrt(piv);
+            if (r == k) arow[k] = dk;
+            else if (r > k) arow[k] = arow[k] / dk;
+#pragma unroll
+            for (int cc = k + 1; cc < kNB; ++cc) {
+              if (cc < nb) {
+                const double lck = readlane_f64(arow[k], cc);
+                if (r >= cc) arow[cc] -= arow[k] * lck;
+              }
+            }
+          }
+        }
       }
-      __syncthreads();
+#pragma unroll
+      for (int cc = 0; cc < kNB; ++cc)
+        if (r < nb && cc <= r) Ld[r][cc] = arow[cc];
+      if (tid == 0) bad = ok ? 0 : 1;
     }
+    __syncthreads();
     if (bad) {
       if (tid == 0) atomicAdd(&status[0], 1);
       return;
@@ -458,15 +522,26 @@ __global__ __launch_bounds__(256) void refine_kernel(const int32_t* __restrict__
       if (r < nb && cc <= r) T[tri(k0 + r) + k0 + cc] = Ld[r][cc];
     }
     // rows below the block, the right-hand side row included:
-    // L21 = A21 L11^-T, with L11^-1 formed by one wave (lane cc solves for
-    // column cc; each lane reads back only its own column)
+    // L21 = A21 L11^-T, with L11^-1 formed in wave 0: lane cc solves for
+    // column cc, reading L11 uniformly and its own earlier entries from LDS
     if (tid < kNB) {
       const int cc = tid;
-      for (int r = 0; r < kNB; ++r) {
+      for (int r = 0; r < nb; ++r) {
         double s = r == cc ? 1.0 : 0.0;
-        for (int c2 = cc; c2 < r; ++c2) s -= Ld[r][c2] * Li[c2][cc];
-        Li[r][cc] = (r >= cc && r < nb) ? s / Ld[r][r] : 0.0;
+        int c2 = 0;
+        for (; c2 + 4 <= r; c2 += 4) {
+          const double l0 = Ld[r][c2], l1 = Ld[r][c2 + 1], l2 = Ld[r][c2 + 2], l3 = Ld[r][c2 + 3];
+          const double x0 = Li[c2][cc], x1 = Li[c2 + 1][cc], x2 = Li[c2 + 2][cc],
+                       x3 = Li[c2 + 3][cc];
+          s -= l0 * x0;
+          s -= l1 * x1;
+          s -= l2 * x2;
+          s -= l3 * x3;
+        }
+        for (; c2 < r; ++c2) s -= Ld[r][c2] * Li[c2][cc];
+        Li[r][cc] = cc < nb ? s / Ld[r][r] : 0.0;
       }
+      for (int r = nb; r < kNB; ++r) Li[r][cc] = 0.0;
     }
     __syncthreads();
     for (int a0 = k0 + nb; a0 <= p; a0 += kST) {
@@ -625,12 +700,12 @@ hipError_t calib_rows_t(const double* M, const float* dWq, const double* delta, 
 hipError_t launch_hessian(const void* X, Dt x_dt, int64_t N, int d_in, double* Hs,
                           int accumulate, hipStream_t s) {
   if (x_dt == Dt::F32)
-    return gemm64_t<float, true, float, true>(static_cast<const float*>(X), d_in,
-                                              static_cast<const float*>(X), d_in, Hs, d_in, d_in,
-                                              d_in, N, accumulate, s);
-  return gemm64_t<uint16_t, true, uint16_t, true>(static_cast<const uint16_t*>(X), d_in,
-                                                  static_cast<const uint16_t*>(X), d_in, Hs, d_in,
-                                                  d_in, d_in, N, accumulate, s);
+    return gemm64_t<float, true, float, true, 2>(static_cast<const float*>(X), d_in,
+                                                 static_cast<const float*>(X), d_in, Hs, d_in,
+                                                 d_in, d_in, N, accumulate, s);
+  return gemm64_t<uint16_t, true, uint16_t, true, 2>(static_cast<const uint16_t*>(X), d_in,
+                                                     static_cast<const uint16_t*>(X), d_in, Hs,
+                                                     d_in, d_in, d_in, N, accumulate, s);
 }
 
 size_t calibrated_scratch_bytes(int d_out, int d_in) { return cal_ws(d_out, d_in).total; }
@@ -644,8 +719,8 @@ hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const do
   double* w = reinterpret_cast<double*>(base + l.w);
   double* Q = reinterpret_cast<double*>(base + l.q);
   hipLaunchKernelGGL(delta_kernel, dim3(1), dim3(256), 0, s, Hs, d_in, damp, delta);
-  hipError_t e = gemm64_t<float, false, double, false>(dWq, d_in, Hs, d_in, Q, d_in, d_out, d_in,
-                                                       d_in, 0, s);
+  hipError_t e = gemm64_t<float, false, double, false, 4>(dWq, d_in, Hs, d_in, Q, d_in, d_out,
+                                                          d_in, d_in, 0, s);
   if (e != hipSuccess) return e;
   switch (log_n) {
 #define QWHA_CASE(L) \
