@@ -65,7 +65,8 @@ __all__ = [
     "select", "values", "refine_ls", "csc", "init_select", "splitmix64", "magnitude_keys",
     "random_keys", "global_select", "init_select_global", "hessian", "damped",
     "activation_error_norms", "refine_system", "cholesky_lower", "refine_values",
-    "init_select_calibrated", "layer_output_error", "scatter_dense",
+    "init_select_calibrated", "layer_output_error", "unpack_codes", "dequantize",
+    "merge_weights", "layer_forward", "scatter_dense",
     "materialize", "forward", "backward", "backward_dc_rows", "sign_update",
     "rel_err",
 ]
@@ -497,6 +498,45 @@ def layer_output_error(dwq: np.ndarray, X: np.ndarray, E: np.ndarray, c: np.ndar
     resid = np.asarray(dwq, dtype=np.float64) - F @ sylvester(d_in) / float(d_in)
     r = resid @ np.asarray(X, dtype=np.float64).T
     return float(np.sum(r * r))
+
+
+# --------------------------------------------------------------------------
+# O15-O17: the quantized base layer with the adapter (inference path):
+# packed b-bit codes with per-group scale and zero ([PN] 损失函数 / 训练策略:
+# the adapter is merged into the quantized model, group quantization), the
+# merged weights W_Q + alpha dW, and y = x W_Q^T + alpha z F^T.
+# --------------------------------------------------------------------------
+
+def unpack_codes(words: np.ndarray, d_in: int, bits: int) -> np.ndarray:
+    """Codes q [rows][d_in] from uint32 words: code j of a row sits in word
+    j // cpw, cpw = floor(32 / bits), at bit (j % cpw) * bits."""
+    cpw = 32 // bits
+    words = np.asarray(words, dtype=np.uint64)
+    j = np.arange(d_in)
+    shift = ((j % cpw) * bits).astype(np.uint64)
+    return ((words[:, j // cpw] >> shift) & np.uint64((1 << bits) - 1)).astype(np.int64)
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int) -> np.ndarray:
+    """W_Q = (q - z) * s per group of `group` columns, in fp32 (the
+    quantizer's own arithmetic)."""
+    g = np.arange(q.shape[1]) // group
+    z = np.asarray(zeros, dtype=np.float32)[:, g]
+    s = np.asarray(scales, dtype=np.float32)[:, g]
+    return ((q.astype(np.float32) - z) * s).astype(np.float32)
+
+
+def merge_weights(W_Q: np.ndarray, E: np.ndarray, c: np.ndarray, alpha: float) -> np.ndarray:
+    """W_Q + alpha F H^-1 (fp64): the adapter merged into the base weights."""
+    d_out, d_in = W_Q.shape
+    return np.asarray(W_Q, dtype=np.float64) + materialize(E, c, d_out, d_in, alpha)
+
+
+def layer_forward(x: np.ndarray, W_Q: np.ndarray, E: np.ndarray, c: np.ndarray,
+                  alpha: float) -> np.ndarray:
+    """y = x W_Q^T + alpha z F^T (fp64): the quantized layer with its
+    adapter, by the plain definition x (W_Q + alpha F H^-1)^T."""
+    return np.asarray(x, dtype=np.float64) @ merge_weights(W_Q, E, c, alpha).T
 
 
 # --------------------------------------------------------------------------

@@ -30,6 +30,8 @@ __all__ = [
     "make_activations",
     "make_calibration",
     "rtn_quantize",
+    "rtn_codes",
+    "pack_codes",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "round_to_bf16",
@@ -124,15 +126,7 @@ def config_specs(name: str) -> List[LayerSpec]:
 # Upstream quantizer (produces the adapter's input, the quantization error)
 # --------------------------------------------------------------------------
 
-def rtn_quantize(w0: np.ndarray, bits: int, group: int) -> np.ndarray:
-    """Asymmetric min/max round-to-nearest quantization along d_in, fp32.
-
-    Per group of ``group`` consecutive input columns:
-      s = (max - min) / (2^b - 1), z = floor(-min/s + 1/2),
-      q = clip(floor(w/s + 1/2) + z, 0, 2^b - 1), W_Q = (q - z) * s.
-    Rounding is half-up so the in-range error lies in [-s/2, s/2), the
-    half-open interval the QWHA notes give (研究背景与动机 › 切入角度).
-    Returns W_Q (fp32, same shape)."""
+def _rtn_parts(w0: np.ndarray, bits: int, group: int):
     d_out, d_in = w0.shape
     assert d_in % group == 0
     w = w0.astype(np.float32).reshape(d_out, d_in // group, group)
@@ -144,6 +138,48 @@ def rtn_quantize(w0: np.ndarray, bits: int, group: int) -> np.ndarray:
     half = np.float32(0.5)
     z = np.floor(-mn / safe + half).astype(np.float32)
     q = np.clip(np.floor(w / safe + half) + z, np.float32(0), qmax)
+    return w, s, safe, z, q
+
+
+def rtn_codes(w0: np.ndarray, bits: int, group: int):
+    """The same quantizer in integer form: codes q (uint8 [d_out][d_in]) and
+    per-group scale s and zero z (fp32 [d_out][d_in/group], z integer-valued)
+    with W_Q = (q - z) * s in fp32, exactly what rtn_quantize returns.
+    Groups of equal values (s = 0) are not representable and raise."""
+    d_out, d_in = w0.shape
+    w, s, safe, z, q = _rtn_parts(w0, bits, group)
+    if not np.all(s > 0):
+        raise ValueError("constant quantization group")
+    return (q.reshape(d_out, d_in).astype(np.uint8), safe[..., 0].astype(np.float32),
+            z[..., 0].astype(np.float32))
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Storage of b-bit codes: each uint32 word holds floor(32/b) codes of a
+    row, code j in word j // cpw at bits (j % cpw) * b (least significant
+    first); rows padded to whole words with zero codes."""
+    d_out, d_in = q.shape
+    cpw = 32 // bits
+    nw = -(-d_in // cpw)
+    words = np.zeros((d_out, nw), dtype=np.uint64)
+    j = np.arange(d_in)
+    sh = ((j % cpw) * bits).astype(np.uint64)
+    for col in range(d_in):
+        words[:, col // cpw] |= q[:, col].astype(np.uint64) << sh[col]
+    return words.astype(np.uint32)
+
+
+def rtn_quantize(w0: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Asymmetric min/max round-to-nearest quantization along d_in, fp32.
+
+    Per group of ``group`` consecutive input columns:
+      s = (max - min) / (2^b - 1), z = floor(-min/s + 1/2),
+      q = clip(floor(w/s + 1/2) + z, 0, 2^b - 1), W_Q = (q - z) * s.
+    Rounding is half-up so the in-range error lies in [-s/2, s/2), the
+    half-open interval the QWHA notes give (研究背景与动机 › 切入角度).
+    Returns W_Q (fp32, same shape)."""
+    d_out, d_in = w0.shape
+    w, s, safe, z, q = _rtn_parts(w0, bits, group)
     wq = ((q - z) * safe).astype(np.float32)
     wq = np.where(s > 0, wq, w).astype(np.float32)
     return wq.reshape(d_out, d_in)

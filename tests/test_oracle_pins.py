@@ -729,3 +729,54 @@ def test_refine_rows_without_a_definite_system_keep_the_dense_solution():
     Hd = O.damped(O.hessian(X), 0.01)
     assert np.allclose(np.diag(Hd) - np.diag(O.hessian(X)),
                        0.01 * np.mean(np.diag(O.hessian(X))), rtol=1e-12)
+
+
+# ---------------------------------------------- quantized base layer (O15-O17)
+
+import synth  # noqa: E402  (the fixture's quantizer and code storage)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_unpack_codes_golden(bits):
+    g = read_golden("packed_codes.txt")
+    codes = g[f"b{bits} codes"][0].astype(np.int64)
+    words = g[f"b{bits} words"][0].astype(np.uint64).astype(np.uint32)[None, :]
+    assert np.array_equal(O.unpack_codes(words, len(codes), bits)[0], codes)
+    assert np.array_equal(synth.pack_codes(codes[None, :].astype(np.uint8), bits), words)
+
+
+def test_dequantize_golden():
+    g = read_golden("packed_codes.txt")
+    q = g["dq codes"].astype(np.int64)
+    w = O.dequantize(q, g["dq scales"], g["dq zeros"], 2)
+    assert np.array_equal(w, g["dq weights"].astype(np.float32))
+
+
+@pytest.mark.parametrize("bits,group", [(2, 64), (3, 128), (4, 128), (4, 64), (8, 32)])
+def test_dequantized_codes_are_the_quantizer_output(bits, group):
+    rng = np.random.default_rng(bits * 100 + group)
+    w0 = (0.02 * rng.standard_normal((12, 256))).astype(np.float32)
+    q, s, z = synth.rtn_codes(w0, bits, group)
+    words = synth.pack_codes(q, bits)
+    got = O.dequantize(O.unpack_codes(words, 256, bits), s, z, group)
+    assert np.array_equal(got, synth.rtn_quantize(w0, bits, group))     # bit for bit
+
+
+def test_merge_and_layer_forward_definitions():
+    rng = np.random.default_rng(3)
+    d_out, d_in = 6, 16
+    W_Q = rng.standard_normal((d_out, d_in)).astype(np.float32)
+    dwq = _rand_dwq(d_out, d_in, 4)
+    r = O.init_select(dwq, 30, m=3)
+    F = O.scatter_dense(r["E"], r["c"], d_out, d_in)
+    H = O.sylvester(d_in)
+    merged = O.merge_weights(W_Q, r["E"], r["c"], 0.7)
+    assert np.allclose(merged, W_Q + 0.7 * F @ H / d_in, rtol=1e-13, atol=1e-13)
+    x = rng.standard_normal((5, d_in))
+    y = O.layer_forward(x, W_Q, r["E"], r["c"], 0.7)
+    # base GEMM plus the adapter's own forward (FWHT, then the sparse product)
+    z = x @ H / d_in
+    assert np.allclose(y, x @ W_Q.astype(np.float64).T + 0.7 * z @ F.T, rtol=1e-12, atol=1e-12)
+    # no adapter: the plain quantized layer
+    y0 = O.layer_forward(x, W_Q, r["E"], np.zeros_like(r["c"]), 0.7)
+    assert np.allclose(y0, x @ W_Q.astype(np.float64).T, rtol=1e-13, atol=1e-13)
