@@ -234,6 +234,44 @@ qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const d
                                size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The quantized base layer with its adapter: the inference path
+ * (papernotes.org, 损失函数 / 训练策略: the adapter is merged into the
+ * group-quantized model; gist.science §4 for its inference cost).
+ *
+ * Base weights W_Q [d_out][d_in] are b-bit codes (b in {2, 3, 4, 8}) with
+ * an fp32 scale s and an fp32 integer-valued zero z per group of `group`
+ * consecutive input columns (group a power of two dividing d_in):
+ *   W_Q[i][j] = (q[i][j] - z[i][j/group]) * s[i][j/group]   (fp32).
+ * codes: uint32 [d_out][ceil(d_in / cpw)], cpw = floor(32 / b) codes per
+ * word, code j of a row in word j / cpw at bit (j % cpw) * b (least
+ * significant first; the last word of a row padded with zero codes).
+ * scales, zeros: fp32 [d_out][d_in / group].
+ *
+ * qwha_merge: W = W_Q + alpha F H^-1 (the adapter merged into dense
+ *   weights), written in out_dtype [d_out][d_in]; fp32 math, one rounding
+ *   for bf16 output.
+ *
+ * qwha_layer_fwd: y = x W_Q^T + alpha z F^T, z = FWHT(x)/d_in, for bf16
+ *   activations x [T][d_in] (QWHA_ERR_DTYPE otherwise), y bf16 [T][d_out].
+ *   The base product runs on the bf16 matrix cores with the weight operand
+ *   q - z (exact in bf16 when |q - z| <= 256, always so for a min/max
+ *   quantizer whose groups span zero), each group's fp32 partial sums
+ *   scaled by s; the adapter's fp32 output is added before the single
+ *   rounding to bf16. Requires d_in >= 32, group >= 32, and a workspace of
+ *   qwha_layer_fwd_workspace_bytes(T, d_in, d_out, p) bytes.
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* zeros,
+                       int32_t bits, int32_t group, int32_t d_out, int32_t d_in, int64_t p,
+                       const int32_t* row_ptr, const int32_t* E, const float* c, float alpha,
+                       qwha_dtype out_dtype, void* W, hipStream_t stream);
+size_t qwha_layer_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p);
+qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                           int32_t d_out, const uint32_t* codes, const float* scales,
+                           const float* zeros, int32_t bits, int32_t group, int64_t p,
+                           const int32_t* row_ptr, const int32_t* E, const float* c, float alpha,
+                           void* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Profiling aid: the next launch of kernel `kernel` made by this thread
  * (inside any entry point above) is bracketed by hipEventRecord(start) and
  * hipEventRecord(stop) on that launch's stream; the request is then
@@ -256,7 +294,9 @@ typedef enum qwha_kernel {
   QWHA_KERNEL_HESSIAN = 11,     /* qwha_hessian */
   QWHA_KERNEL_CALIB_PREPARE = 12, /* dW_Q Hs, norms and Q inside qwha_init_select_calibrated */
   QWHA_KERNEL_CALIB_SYSTEM = 13,  /* rhs gather and G inside qwha_init_select_calibrated */
-  QWHA_KERNEL_REFINE = 14       /* the per-row solves of qwha_refine_values */
+  QWHA_KERNEL_REFINE = 14,      /* the per-row solves of qwha_refine_values */
+  QWHA_KERNEL_MERGE = 15,       /* qwha_merge */
+  QWHA_KERNEL_QGEMM = 16        /* the base GEMM inside qwha_layer_fwd */
 } qwha_kernel;
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 

@@ -21,7 +21,8 @@ __all__ = [
     "QWHA_F32", "QWHA_BF16", "QwhaError", "lib",
     "QWHA_SELECT_MAGNITUDE", "QWHA_SELECT_RANDOM",
     "qwha_init_select", "qwha_init_select_global", "qwha_hessian",
-    "qwha_init_select_calibrated", "qwha_refine_values", "qwha_materialize", "qwha_fwd", "qwha_bwd",
+    "qwha_init_select_calibrated", "qwha_refine_values", "qwha_merge", "qwha_layer_fwd",
+    "qwha_materialize", "qwha_fwd", "qwha_bwd",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
@@ -169,6 +170,36 @@ def qwha_refine_values(row_ptr, E, G, rhs, c: torch.Tensor,
                                  d_in, p, c.data_ptr(), _ptr(status), ws.data_ptr(), ws.numel(),
                                  _stream()), "qwha_refine_values")
     return c, status
+
+
+# ---------------------------------------------------------------- quantized base
+def qwha_merge(codes, scales, zeros, bits: int, group: int, row_ptr, E, c, d_in: int,
+               alpha: float = 1.0, out_dtype=torch.float32) -> torch.Tensor:
+    """W = W_Q + alpha F H^-1 from packed codes (uint32 words as int32)."""
+    d_out = row_ptr.numel() - 1
+    W = torch.empty((d_out, d_in), dtype=out_dtype, device=codes.device)
+    p = c.numel()
+    check(lib.qwha_merge(_ptr(codes), _ptr(scales), _ptr(zeros), bits, group, d_out, d_in, p,
+                         _ptr(row_ptr), E.data_ptr(), c.data_ptr(), float(alpha),
+                         _DT[out_dtype], _ptr(W), _stream()), "qwha_merge")
+    return W
+
+
+def qwha_layer_fwd(x: torch.Tensor, codes, scales, zeros, bits: int, group: int, row_ptr, E,
+                   c, alpha: float = 1.0, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W_Q^T + alpha z F^T for bf16 x [T][d_in]; y bf16 [T][d_out]."""
+    T, d_in = x.shape
+    d_out = row_ptr.numel() - 1
+    p = c.numel()
+    y = torch.empty((T, d_out), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(lib.qwha_layer_fwd_workspace_bytes(T, d_in, d_out, p), x.device)
+    check(lib.qwha_layer_fwd(_ptr(x) if T else None, _dt(x), T, d_in, d_out, _ptr(codes),
+                             _ptr(scales), _ptr(zeros), bits, group, p, _ptr(row_ptr),
+                             E.data_ptr(), c.data_ptr(), float(alpha),
+                             _ptr(y) if T else None, ws.data_ptr(), ws.numel(), _stream()),
+          "qwha_layer_fwd")
+    return y
 
 
 # ---------------------------------------------------------------- materialize

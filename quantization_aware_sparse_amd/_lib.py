@@ -44,6 +44,14 @@ SIGNATURES = {
     "qwha_refine_workspace_bytes": (c_size_t, [c_void_p, c_int32]),
     "qwha_refine_values": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                      c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qwha_merge": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                             c_int64, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_void_p,
+                             c_void_p]),
+    "qwha_layer_fwd_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),
+    "qwha_layer_fwd": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_void_p,
+                                 c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p,
+                                 c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]),
     "qwha_materialize": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
                                    c_float, c_int32, c_void_p, c_int32, c_void_p]),
     "qwha_fwd_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),

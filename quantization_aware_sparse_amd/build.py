@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqwha.so")
 
-SOURCES = ["api.hip", "fwht.hip", "init.hip", "materialize.hip", "refine.hip",
+SOURCES = ["api.hip", "fwht.hip", "init.hip", "materialize.hip", "quant.hip", "refine.hip",
            "select_global.hip", "spmm.hip"]
 
 ARCH = "gfx950"

@@ -32,7 +32,7 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 struct Hook {
   hipEvent_t start, stop;
 };
-constexpr int kNumKernelIds = 15;
+constexpr int kNumKernelIds = 17;
 thread_local Hook g_hook[kNumKernelIds] = {};
 
 // Runs `launch` (a callable returning hipError_t) for kernel id `k`, with the
@@ -69,6 +69,15 @@ qwha_status check_p(int64_t p, int32_t d_out, int32_t d_in) {
   if (p < 0 || p > INT32_MAX || p > static_cast<int64_t>(d_out) * d_in)
     return fail(QWHA_ERR_BUDGET, "p=%lld outside [0, min(2^31-1, d_out*d_in)]",
                 static_cast<long long>(p));
+  return QWHA_OK;
+}
+
+qwha_status check_quant(int32_t bits, int32_t group, int32_t d_in, int32_t min_group) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(QWHA_ERR_INVALID_ARG, "bits=%d is not one of 2, 3, 4, 8", bits);
+  if (group < min_group || group > d_in || (group & (group - 1)) != 0)
+    return fail(QWHA_ERR_INVALID_ARG, "group=%d is not a power of two in [%d, d_in]", group,
+                min_group);
   return QWHA_OK;
 }
 
@@ -391,6 +400,97 @@ qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const d
                    "refine");
 }
 
+// ------------------------------------------------------------------ quantized base
+qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* zeros,
+                       int32_t bits, int32_t group, int32_t d_out, int32_t d_in, int64_t p,
+                       const int32_t* row_ptr, const int32_t* E, const float* c, float alpha,
+                       qwha_dtype out_dtype, void* W, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_quant(bits, group, d_in, 1));
+  QWHA_TRY(check_dt(out_dtype, "out_dtype"));
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  QWHA_NEED(codes, 4);
+  QWHA_NEED(scales, 4);
+  QWHA_NEED(zeros, 4);
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(W, 16);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+  }
+  const QuantW qw = make_quant(codes, scales, zeros, bits, group, d_in);
+  return hip_check(timed(QWHA_KERNEL_MERGE, stream,
+                         [&] {
+                           return launch_merge(row_ptr, E, c, d_out, log_n, alpha, qw,
+                                               static_cast<Dt>(out_dtype), W, stream);
+                         }),
+                   "merge");
+}
+
+size_t qwha_layer_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  return fwd_ws(T, d_in, d_out, p).total + align256(static_cast<size_t>(T) * d_out * 4);
+}
+
+qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                           int32_t d_out, const uint32_t* codes, const float* scales,
+                           const float* zeros, int32_t bits, int32_t group, int64_t p,
+                           const int32_t* row_ptr, const int32_t* E, const float* c, float alpha,
+                           void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  if (d_in < 32) return fail(QWHA_ERR_SHAPE, "d_in=%d below 32", d_in);
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_dt(act, "act"));
+  if (act != QWHA_BF16)
+    return fail(QWHA_ERR_DTYPE, "the base GEMM runs on bf16 activations");
+  QWHA_TRY(check_quant(bits, group, d_in, 32));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  QWHA_NEED(codes, 4);
+  QWHA_NEED(scales, 4);
+  QWHA_NEED(zeros, 4);
+  QWHA_NEED(row_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+  }
+  if (T == 0) return QWHA_OK;
+  QWHA_NEED(x, 16);
+  QWHA_NEED(y, 16);
+  const FwdWs l = fwd_ws(T, d_in, d_out, p);
+  const size_t total = l.total + align256(static_cast<size_t>(T) * d_out * 4);
+  if (workspace == nullptr || workspace_bytes < total)
+    return fail(QWHA_ERR_WORKSPACE, "layer fwd workspace needs %zu bytes", total);
+  QWHA_NEED(workspace, 256);
+
+  float* y32 = nullptr;
+  if (p > 0) {
+    float* z = reinterpret_cast<float*>(at(workspace, l.z));
+    void* prep = at(workspace, l.prep);
+    y32 = reinterpret_cast<float*>(at(workspace, l.total));
+    QWHA_TRY(hip_check(launch_fwht(x, Dt::BF16, z, Dt::F32, T, log_n,
+                                   1.0f / static_cast<float>(d_in), 0, stream),
+                       "layer fwht"));
+    QWHA_TRY(hip_check(launch_prep_csr(row_ptr, E, c, d_out, p, l.plan, prep, stream),
+                       "layer prep"));
+    QWHA_TRY(hip_check(launch_spmm(z, Dt::F32, T, d_in, prep, p, d_out, l.plan, alpha, y32,
+                                   Dt::F32, 0, nullptr, nullptr, stream),
+                       "layer spmm"));
+  }
+  const QuantW qw = make_quant(codes, scales, zeros, bits, group, d_in);
+  return hip_check(timed(QWHA_KERNEL_QGEMM, stream,
+                         [&] {
+                           return launch_qgemm(static_cast<const uint16_t*>(x), T, d_in, d_out,
+                                               qw, y32, static_cast<uint16_t*>(y), stream);
+                         }),
+                   "base gemm");
+}
+
 // ------------------------------------------------------------------ materialize
 qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const float* c,
                              int32_t d_out, int32_t d_in, int64_t p, float alpha,
@@ -590,7 +690,7 @@ qwha_status qwha_fwht(const void* in, qwha_dtype in_dtype, void* out, qwha_dtype
 
 qwha_status qwha_profile_next(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
   g_err[0] = 0;
-  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_REFINE ||
+  if (kernel < QWHA_KERNEL_NONE || kernel > QWHA_KERNEL_QGEMM ||
       kernel >= kNumKernelIds)
     return fail(QWHA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
   if (kernel == QWHA_KERNEL_NONE) {

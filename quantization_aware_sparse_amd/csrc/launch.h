@@ -56,6 +56,29 @@ hipError_t launch_refine(const int32_t* row_ptr, const int32_t* E, const double*
                          const double* rhs, int d_out, float* c, int32_t* status, void* ws,
                          size_t ws_bytes, double pivot_tol, hipStream_t s);
 
+// ---- quantized base layer (quant.hip)
+// b-bit codes, floor(32/b) per uint32 word (code j in word j / cpw at bit
+// (j % cpw) * b), scale and zero per group of 2^lg_group columns
+struct QuantW {
+  const uint32_t* codes;
+  const float* scales;
+  const float* zeros;
+  int bits, cpw;
+  uint32_t cpw_magic;   // ceil(2^32 / cpw): j / cpw = umulhi(j, cpw_magic) for j < 2^16
+  int wpr;              // words per row
+  int lg_group;
+  int gpr;              // groups per row
+};
+QuantW make_quant(const uint32_t* codes, const float* scales, const float* zeros, int bits,
+                  int group, int d_in);
+// W = W_Q + alpha F H^-1
+hipError_t launch_merge(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
+                        int log_n, float alpha, const QuantW& qw, Dt out_dt, void* W,
+                        hipStream_t s);
+// y = bf16(x W_Q^T + add), x bf16 [T][K], add fp32 [T][N], y bf16 [T][N]
+hipError_t launch_qgemm(const uint16_t* x, int64_t T, int K, int N, const QuantW& qw,
+                        const float* add, uint16_t* y, hipStream_t s);
+
 // ---- materialize
 hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                               int log_n, float alpha, Dt out_dt, void* dW, int accumulate,

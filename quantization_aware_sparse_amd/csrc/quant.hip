@@ -1,0 +1,329 @@
+// The quantized base layer with the adapter (the inference path; QWHA notes,
+// papernotes.org, 损失函数 / 训练策略: the adapter is merged into the
+// group-quantized model; gist.science summary §4 for its inference cost).
+//
+// Weights are b-bit codes q with a scale s and zero z per group of `group`
+// input columns: W_Q = (q - z) * s. Codes are stored floor(32/b) to a uint32
+// word, code j of a row in word j / cpw at bit (j % cpw) * b.
+//
+//   merge_kernel  W = W_Q + alpha F H^-1 per row: the materialisation of
+//                 the adapter (scatter c into LDS, FWHT) with the
+//                 dequantized row added before the single store;
+//   qgemm_kernel  y = x W_Q^T + add on the bf16 matrix cores
+//                 (v_mfma_f32_16x16x32_bf16): the weight operand is q - z,
+//                 an integer that bf16 holds exactly; each group's partial
+//                 sums are scaled by s in fp32 and accumulated, so the only
+//                 roundings are those of the fp32 sums. `add` carries the
+//                 adapter's alpha z F^T (fp32) into the single bf16 store.
+#include "fwht_core.h"
+#include "launch.h"
+
+namespace qwha {
+
+namespace {
+
+__device__ __forceinline__ float dequant(const QuantW& qw, int64_t row, int j) {
+  const uint32_t wi = __umulhi(static_cast<uint32_t>(j), qw.cpw_magic);   // j / cpw
+  const int sh = (j - static_cast<int>(wi) * qw.cpw) * qw.bits;
+  const uint32_t w = qw.codes[row * qw.wpr + wi];
+  const float q = static_cast<float>((w >> sh) & ((1u << qw.bits) - 1u));
+  const int64_t g = row * qw.gpr + (j >> qw.lg_group);
+  return (q - qw.zeros[g]) * qw.scales[g];
+}
+
+template <int LOG_N>
+struct MergeCfg {
+  using F = Fwht<LOG_N>;
+  static constexpr int BLOCK = F::TPR > 256 ? F::TPR : 256;
+  static constexpr int RPW = BLOCK / F::TPR;
+};
+
+template <int LOG_N, typename TOut>
+__global__ __launch_bounds__(MergeCfg<LOG_N>::BLOCK) void merge_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ E,
+    const float* __restrict__ c, int d_out, float scale, QuantW qw, TOut* __restrict__ W) {
+  using F = Fwht<LOG_N>;
+  constexpr int RPW = MergeCfg<LOG_N>::RPW;
+  __shared__ float lds_all[RPW * F::LDS];
+  const int slot = threadIdx.x / F::TPR;
+  const int u = threadIdx.x % F::TPR;
+  const int row = blockIdx.x * RPW + slot;
+  const bool live = row < d_out;
+  float* lds = lds_all + slot * F::LDS;
+
+  for (int j = u; j < F::LDS; j += F::TPR) lds[j] = 0.f;
+  __syncthreads();
+  if (live) {
+    const int k1 = row_ptr[row + 1];
+    for (int k = row_ptr[row] + u; k < k1; k += F::TPR)
+      lds[F::pad(E[2 * static_cast<int64_t>(k) + 1])] = c[k];
+  }
+  __syncthreads();
+  float v[F::EPT];
+#pragma unroll
+  for (int r = 0; r < F::EPT; ++r) v[r] = lds[F::pad(u * F::EPT + r)];
+  F::run(v, lds, u);
+  if (live) {
+    TOut* dst = W + static_cast<int64_t>(row) * F::N;
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) {
+      const int j = F::out_index(u, r);
+      Elem<TOut>::st(dst, j, dequant(qw, row, j) + v[r] * scale);
+    }
+  }
+}
+
+template <int LOG_N, typename TOut>
+hipError_t merge_t(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
+                   float scale, const QuantW& qw, void* W, hipStream_t s) {
+  constexpr int RPW = MergeCfg<LOG_N>::RPW;
+  const int blocks = (d_out + RPW - 1) / RPW;
+  hipLaunchKernelGGL((merge_kernel<LOG_N, TOut>), dim3(blocks), dim3(MergeCfg<LOG_N>::BLOCK), 0,
+                     s, row_ptr, E, c, d_out, scale, qw, static_cast<TOut*>(W));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ GEMM
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQT = 128;       // tile: tokens and output rows
+constexpr int kQK = 32;        // K per step (one MFMA deep)
+constexpr int kQLd = kQK + 8;  // LDS row stride, bf16
+
+__device__ __forceinline__ uint16_t bf16_bits_exact(float v) {
+  return static_cast<uint16_t>(__float_as_uint(v) >> 16);   // v is a small integer
+}
+
+// Code words covering 16 consecutive columns of a row: 16 / CPW whole words
+// when CPW divides 16, else up to 3 words from the one holding the first.
+template <int BITS>
+struct Codes16 {
+  static constexpr int CPW = 32 / BITS;
+  static constexpr bool ALIGNED = (16 % CPW) == 0;
+  static constexpr int NW = ALIGNED ? 16 / CPW : 3;
+};
+
+// words for columns k0..k0+15 of the row (wpr words long)
+template <int BITS>
+__device__ __forceinline__ void load_codes16(const uint32_t* __restrict__ row_words, int k0,
+                                             int wpr, uint32_t* w) {
+  using C = Codes16<BITS>;
+  const int base = k0 / C::CPW;
+#pragma unroll
+  for (int i = 0; i < C::NW; ++i) w[i] = row_words[min(base + i, wpr - 1)];
+}
+
+// those 16 codes as q - z in bf16 (exact for |q - z| <= 256), two to a word
+template <int BITS>
+__device__ __forceinline__ void unpack16(const uint32_t* w, int k0, float z, uint32_t* out) {
+  using C = Codes16<BITS>;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  const int base = k0 / C::CPW;
+  uint16_t h[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    uint32_t q;
+    if constexpr (C::ALIGNED) {
+      q = (w[e / C::CPW] >> ((e % C::CPW) * BITS)) & MASK;
+    } else {
+      const int j = k0 + e;
+      q = (w[j / C::CPW - base] >> ((j % C::CPW) * BITS)) & MASK;
+    }
+    h[e] = bf16_bits_exact(static_cast<float>(q) - z);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    out[i] = static_cast<uint32_t>(h[2 * i]) | (static_cast<uint32_t>(h[2 * i + 1]) << 16);
+}
+
+// y[t][n] = bf16(sum_g s[n][g] * sum_{k in g} x[t][k] (q[n][k] - z[n][g]) + add[t][n]).
+// 256 threads, a 128 (tokens) x 128 (output rows) tile, 64x64 per wave as
+// 4x4 blocks of 16x16; K in steps of 32 through double-buffered LDS (one
+// barrier per step), the next step's loads in flight during the MFMAs.
+// MFMA operands: lane l holds row / column l%16 and k 8(l/16)..+8; result
+// register r of lane l is row 4(l/16)+r, column l%16, so a lane's results
+// share one output row n and one group scale.
+template <int BITS>
+__global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                       int K, int N, QuantW qw,
+                                                       const float* __restrict__ add,
+                                                       uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kQT][kQLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kQT][kQLd];
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kQT;
+  const int n0 = blockIdx.x * kQT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+
+  f32x4 acc[4][4], gacc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // staging: thread -> row tid/2, 16 columns at (tid&1)*16
+  const int sr = tid >> 1, sk = (tid & 1) * 16;
+  const int64_t xrow = m0 + sr;
+  const bool xlive = xrow < T;
+  const uint16_t* xp = x + (xlive ? xrow : 0) * K + sk;
+  const int wrow = n0 + sr;
+  const bool wlive = wrow < N;
+  const uint32_t* wp = qw.codes + static_cast<int64_t>(wlive ? wrow : 0) * qw.wpr;
+  const float* zp = qw.zeros + static_cast<int64_t>(wlive ? wrow : 0) * qw.gpr;
+
+  uint4 xa[2];
+  uint32_t cw[Codes16<BITS>::NW];
+  float zc = 0.f;
+  int kf = 0;
+  // global loads of a step (raw code words; unpacked when staged)
+  auto fetch = [&](int k0) {
+    kf = k0 + sk;
+    if (xlive) {
+      const uint4* q = reinterpret_cast<const uint4*>(xp + k0);
+      xa[0] = q[0];
+      xa[1] = q[1];
+    } else {
+      xa[0] = xa[1] = uint4{0u, 0u, 0u, 0u};
+    }
+    if (wlive) {
+      load_codes16<BITS>(wp, kf, qw.wpr, cw);
+      zc = zp[kf >> qw.lg_group];
+    }
+  };
+  auto stage = [&](int buf) {
+    uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][sk]);
+    da[0] = xa[0];
+    da[1] = xa[1];
+    uint32_t wb[8];
+    if (wlive) {
+      unpack16<BITS>(cw, kf, zc, wb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wb[i] = 0u;
+    }
+    uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr][sk]);
+    db[0] = uint4{wb[0], wb[1], wb[2], wb[3]};
+    db[1] = uint4{wb[4], wb[5], wb[6], wb[7]};
+  };
+
+  const int steps_per_group = (1 << qw.lg_group) / kQK;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  int buf = 0;
+  const int nsteps = K / kQK;
+  for (int st = 0; st < nsteps; ++st) {
+    const int k0 = st * kQK;
+    if (st + 1 < nsteps) fetch(k0 + kQK);
+    const int kc = 8 * (lane >> 4);
+    bf16x8 af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm + i * 16 + (lane & 15)][kc]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn + j * 16 + (lane & 15)][kc]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], gacc[i][j], 0, 0, 0);
+    if ((st + 1) % steps_per_group == 0) {
+      const int g = k0 >> qw.lg_group;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + j * 16 + (lane & 15);
+        const float sc = n < N ? qw.scales[static_cast<int64_t>(n) * qw.gpr + g] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][j] += sc * gacc[i][j];
+          gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    if (st + 1 < nsteps) stage(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = m0 + wm + i * 16 + 4 * (lane >> 4) + r;
+        if (t < T && n < N) {
+          const int64_t at = t * N + n;
+          y[at] = f32_to_bf16(add ? acc[i][j][r] + add[at] : acc[i][j][r]);
+        }
+      }
+    }
+}
+
+}  // namespace
+
+QuantW make_quant(const uint32_t* codes, const float* scales, const float* zeros, int bits,
+                  int group, int d_in) {
+  QuantW qw;
+  qw.codes = codes;
+  qw.scales = scales;
+  qw.zeros = zeros;
+  qw.bits = bits;
+  qw.cpw = 32 / bits;
+  qw.cpw_magic = static_cast<uint32_t>((0x100000000ull + qw.cpw - 1) / qw.cpw);
+  qw.wpr = (d_in + qw.cpw - 1) / qw.cpw;
+  int lg = 0;
+  while ((1 << lg) < group) ++lg;
+  qw.lg_group = lg;
+  qw.gpr = d_in / group;
+  return qw;
+}
+
+hipError_t launch_merge(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
+                        int log_n, float alpha, const QuantW& qw, Dt out_dt, void* W,
+                        hipStream_t s) {
+  const float scale = alpha / static_cast<float>(1 << log_n);
+  switch (log_n) {
+#define QWHA_CASE(L)                                                        \
+  case L:                                                                   \
+    return out_dt == Dt::F32                                                \
+               ? merge_t<L, float>(row_ptr, E, c, d_out, scale, qw, W, s)   \
+               : merge_t<L, uint16_t>(row_ptr, E, c, d_out, scale, qw, W, s);
+    QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
+    QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
+    QWHA_CASE(14)
+#undef QWHA_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_qgemm(const uint16_t* x, int64_t T, int K, int N, const QuantW& qw,
+                        const float* add, uint16_t* y, hipStream_t s) {
+  const dim3 grid((N + kQT - 1) / kQT, static_cast<unsigned>((T + kQT - 1) / kQT));
+  switch (qw.bits) {
+    case 2:
+      hipLaunchKernelGGL(qgemm_kernel<2>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      break;
+    case 3:
+      hipLaunchKernelGGL(qgemm_kernel<3>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      break;
+    case 4:
+      hipLaunchKernelGGL(qgemm_kernel<4>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      break;
+    case 8:
+      hipLaunchKernelGGL(qgemm_kernel<8>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qwha

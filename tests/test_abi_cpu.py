@@ -195,6 +195,43 @@ def test_refine_workspace_query_on_host_row_ptr(q):
     assert q.qwha_refine_workspace_bytes(np.array([1, 2], np.int32).ctypes.data, 1) == 0
 
 
+def test_quantized_base_validation(q):
+    def merge(**kw):
+        a = dict(codes=FAKE, s=FAKE, z=FAKE, bits=4, group=128, d_out=64, d_in=256, p=500,
+                 row_ptr=FAKE, E=FAKE, c=FAKE, alpha=1.0, out=0, W=FAKE)
+        a.update(kw)
+        return q.qwha_merge(a["codes"], a["s"], a["z"], a["bits"], a["group"], a["d_out"],
+                            a["d_in"], a["p"], a["row_ptr"], a["E"], a["c"], a["alpha"],
+                            a["out"], a["W"], None)
+    assert merge(bits=5) == INVALID
+    assert merge(group=96) == INVALID
+    assert merge(group=512) == INVALID
+    assert merge(out=2) == DTYPE
+    assert merge(codes=None) == INVALID
+    assert merge(W=FAKE + 8) == ALIGN
+    assert merge(d_in=100) == SHAPE
+    assert merge(alpha=float("nan")) == INVALID
+
+    def fwd(**kw):
+        a = dict(x=FAKE, act=1, T=128, d_in=256, d_out=64, codes=FAKE, s=FAKE, z=FAKE, bits=4,
+                 group=128, p=500, row_ptr=FAKE, E=FAKE, c=FAKE, alpha=1.0, y=FAKE, ws=FAKE,
+                 wsb=0)
+        a.update(kw)
+        return q.qwha_layer_fwd(a["x"], a["act"], a["T"], a["d_in"], a["d_out"], a["codes"],
+                                a["s"], a["z"], a["bits"], a["group"], a["p"], a["row_ptr"],
+                                a["E"], a["c"], a["alpha"], a["y"], a["ws"], a["wsb"], None)
+    assert fwd(act=0) == DTYPE                  # the base GEMM takes bf16 activations
+    assert fwd(d_in=16, group=16) == SHAPE
+    assert fwd(group=16) == INVALID              # groups below one MFMA depth
+    assert fwd(bits=1) == INVALID
+    assert fwd(x=FAKE + 2) == ALIGN
+    assert fwd() == WORKSPACE
+    need = q.qwha_layer_fwd_workspace_bytes(128, 256, 64, 500)
+    assert need >= 128 * 64 * 4 + 128 * 256 * 4
+    assert fwd(wsb=need - 1) == WORKSPACE
+    assert fwd(T=0, x=None, y=None) == OK        # nothing to do
+
+
 def test_bwd_materialize_fwht_validation(q):
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 24, 8, 1.0, 0, FAKE, 0, None) == SHAPE
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 16, 8, 1.0, 5, FAKE, 0, None) == DTYPE
