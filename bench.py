@@ -35,6 +35,8 @@ K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_FWHT_X=3, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC
          INIT_SELECT=7, MATERIALIZE=8)
 GLOBAL_THRESHOLD = 10
 KR = dict(HESSIAN=11, CALIB_PREPARE=12, CALIB_SYSTEM=13, REFINE=14)
+KQ = dict(MERGE=15, QGEMM=16)
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
 FP64_MFMA_PEAK_TFLOPS = 78.6     # MI355X dense fp64 matrix
 FP64_VECTOR_PEAK_TFLOPS = 78.6   # MI355X fp64 vector
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--refine-tokens", type=int, default=32768,
                     help="calibration tokens for the refinement measurement (0: skip)")
     ap.add_argument("--refine-reps", type=int, default=3)
+    ap.add_argument("--base-reps", type=int, default=10,
+                    help="timed calls of the quantized base layer (0: skip)")
     ap.add_argument("--variant-reps", type=int, default=10,
                     help="timed calls of each init selection strategy (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -268,6 +272,10 @@ def main():
         out["init_variants"] = init_variants(args.variant_reps, sets, (d_out, d_in, p),
                                              (row_ptr, E, c, col_ptr, perm), ws_i, stream, hip)
 
+    if args.base_reps > 0:
+        out["base_layer"] = base_layer_measure(args.base_reps, spec, layer, sets,
+                                               (row_ptr, E, c), stream, hip)
+
     if args.refine_tokens > 0 and args.refine_reps > 0:
         out["refine"] = refine_measure(args.refine_tokens, args.refine_reps, spec, sets[0][0],
                                        stream, hip)
@@ -342,6 +350,74 @@ def init_variants(reps, sets, dims, outs, ws_i, stream, hip):
     res["calls"] = reps
     res["layer"] = f"{d_out}x{d_in}, p={p}"
     return res
+
+
+def base_layer_measure(reps, spec, layer, sets, adapter, stream, hip):
+    """Time the quantized base layer with the adapter on the workload: the
+    layer forward y = x W_Q^T + alpha z F^T (qwha_layer_fwd, bf16 tokens;
+    W_Q as the fixture's b-bit codes) and the merge W_Q + alpha dW
+    (qwha_merge, bf16 out). Rates: the base GEMM's 2 T d_in d_out flops
+    against the dense bf16 matrix peak; the merge's bytes (codes, scales and
+    zeros, E and c, row_ptr, the bf16 output) against HBM peak."""
+    import numpy as np
+    import torch
+    import synth
+    from quantization_aware_sparse_amd import check, lib
+    d_out, d_in, p, T = spec.d_out, spec.d_in, spec.p, spec.T
+    qc, sc, zr = synth.rtn_codes(layer.w0, spec.bits, spec.group)
+    words = synth.pack_codes(qc, spec.bits)
+    dev = "cuda:0"
+    codes = torch.from_numpy(words.view(np.int32)).to(dev)
+    scales = torch.from_numpy(sc).to(dev)
+    zeros = torch.from_numpy(zr).to(dev)
+    row_ptr, E, c = adapter
+    y = torch.empty((T, d_out), dtype=torch.bfloat16, device=dev)
+    W = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.qwha_layer_fwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
+                     device=dev)
+    ev = {k: (hip.create(), hip.create()) for k in list(KQ) + ["LAYER"]}
+    times = {k: [] for k in ev}
+    for r in range(reps + 2):
+        rec = r >= 2
+        x = sets[r % len(sets)][1]
+        if rec:
+            for k, kid in KQ.items():
+                check(lib.qwha_profile_next(kid, ev[k][0], ev[k][1]), "profile")
+            hip.record(ev["LAYER"][0], stream)
+        check(lib.qwha_layer_fwd(x.data_ptr(), 1, T, d_in, d_out, codes.data_ptr(),
+                                 scales.data_ptr(), zeros.data_ptr(), spec.bits, spec.group, p,
+                                 row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), 1.0,
+                                 y.data_ptr(), ws.data_ptr(), ws.numel(), stream), "layer fwd")
+        if rec:
+            hip.record(ev["LAYER"][1], stream)
+        check(lib.qwha_merge(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), spec.bits,
+                             spec.group, d_out, d_in, p, row_ptr.data_ptr(), E.data_ptr(),
+                             c.data_ptr(), 1.0, 1, W.data_ptr(), stream), "merge")
+        torch.cuda.synchronize()
+        if rec:
+            for k in ev:
+                times[k].append(hip.elapsed_ms(*ev[k]))
+    us = {k: 1e3 * float(np.mean(v)) for k, v in times.items()}
+    flops = 2.0 * T * d_in * d_out
+    a_q = flops / (us["QGEMM"] * 1e-6) / 1e12
+    mbytes = (words.nbytes + sc.nbytes + zr.nbytes + 12 * p + 4 * (d_out + 1)
+              + 2 * d_out * d_in)
+    a_m = mbytes / (us["MERGE"] * 1e-6) / 1e9
+    return {
+        "weights": f"{spec.bits}-bit codes, group {spec.group} (the fixture's RTN), "
+                   f"{d_out}x{d_in}; adapter p={p}; {T} bf16 tokens",
+        "reps": reps,
+        "layer_fwd_us": round(us["LAYER"], 1),
+        "layer_fwd_tokens_per_s": round(T / (us["LAYER"] * 1e-6), 1),
+        "base_gemm_us": round(us["QGEMM"], 1),
+        "merge_us": round(us["MERGE"], 1),
+        "base_gemm_roofline": dict(bound="mfma", achieved=round(a_q, 1), unit="TFLOP/s",
+                                   peak=BF16_MFMA_PEAK_TFLOPS,
+                                   frac=round(a_q / BF16_MFMA_PEAK_TFLOPS, 4), dtype="bf16"),
+        "merge_roofline": dict(bound="hbm", achieved=round(a_m, 1), unit="GB/s",
+                               peak=HBM_PEAK_GBS, frac=round(a_m / HBM_PEAK_GBS, 4),
+                               bytes=int(mbytes)),
+    }
 
 
 def refine_measure(N, reps, spec, dwq, stream, hip):
@@ -431,6 +507,7 @@ KERNEL_SOURCES = {
     "GLOBAL_THRESHOLD": ["select_global.hip", "fwht_core.h"],
     "HESSIAN": ["refine.hip", "fwht_core.h"], "CALIB_PREPARE": ["refine.hip", "fwht_core.h"],
     "CALIB_SYSTEM": ["refine.hip", "fwht_core.h"], "REFINE": ["refine.hip", "fwht_core.h"],
+    "MERGE": ["quant.hip", "fwht_core.h"], "QGEMM": ["quant.hip"],
 }
 SHARED_SOURCES = ["common.h", "launch.h", "api.hip"]
 

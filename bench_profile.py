@@ -47,6 +47,9 @@ KERNEL_IDS = {
     "refine_offsets_kernel": ["REFINE"],
     "refine_kernel": ["REFINE"],
     "fill_i32_kernel": ["REFINE"],
+    # quantized base layer
+    "merge_kernel": ["MERGE"],
+    "qgemm_kernel": ["QGEMM"],
 }
 
 

@@ -257,7 +257,7 @@ qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const d
  *   q - z (exact in bf16 when |q - z| <= 256, always so for a min/max
  *   quantizer whose groups span zero), each group's fp32 partial sums
  *   scaled by s; the adapter's fp32 output is added before the single
- *   rounding to bf16. Requires d_in >= 32, group >= 32, and a workspace of
+ *   rounding to bf16. Requires d_in >= 64, group >= 32, and a workspace of
  *   qwha_layer_fwd_workspace_bytes(T, d_in, d_out, p) bytes.
  * --------------------------------------------------------------------------- */
 qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* zeros,

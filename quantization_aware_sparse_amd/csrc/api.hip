@@ -443,7 +443,7 @@ qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_i
   g_err[0] = 0;
   int log_n;
   QWHA_TRY(check_dims(d_out, d_in, &log_n));
-  if (d_in < 32) return fail(QWHA_ERR_SHAPE, "d_in=%d below 32", d_in);
+  if (d_in < 64) return fail(QWHA_ERR_SHAPE, "d_in=%d below 64", d_in);
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_dt(act, "act"));
   if (act != QWHA_BF16)

@@ -88,8 +88,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQT = 128;       // tile: tokens and output rows
-constexpr int kQK = 32;        // K per step (one MFMA deep)
+constexpr int kQK = 64;        // K per step (two MFMAs deep)
 constexpr int kQLd = kQK + 8;  // LDS row stride, bf16
+constexpr int kXcd = 8;        // XCDs (workgroups go round-robin over them)
 
 __device__ __forceinline__ uint16_t bf16_bits_exact(float v) {
   return static_cast<uint16_t>(__float_as_uint(v) >> 16);   // v is a small integer
@@ -139,8 +140,12 @@ __device__ __forceinline__ void unpack16(const uint32_t* w, int k0, float z, uin
 
 // y[t][n] = bf16(sum_g s[n][g] * sum_{k in g} x[t][k] (q[n][k] - z[n][g]) + add[t][n]).
 // 256 threads, a 128 (tokens) x 128 (output rows) tile, 64x64 per wave as
-// 4x4 blocks of 16x16; K in steps of 32 through double-buffered LDS (one
+// 4x4 blocks of 16x16; K in steps of 64 through double-buffered LDS (one
 // barrier per step), the next step's loads in flight during the MFMAs.
+// Tile order: workgroup b runs on XCD b % 8; when the output-row tiles
+// split evenly over the XCDs, each XCD keeps its own 1/8 of them (their
+// codes stay in its L2) and walks the token tiles, so a token tile is read
+// by its XCD's workgroups at about the same time.
 // MFMA operands: lane l holds row / column l%16 and k 8(l/16)..+8; result
 // register r of lane l is row 4(l/16)+r, column l%16, so a lane's results
 // share one output row n and one group scale.
@@ -151,8 +156,21 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kQT][kQLd];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kQT][kQLd];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kQT;
-  const int n0 = blockIdx.x * kQT;
+  const int ntn = (N + kQT - 1) / kQT;
+  int tm, tn;
+  {
+    const int b = blockIdx.x;
+    if (ntn % kXcd == 0) {
+      const int per = ntn / kXcd, slot = b / kXcd;
+      tm = slot / per;
+      tn = (b % kXcd) * per + slot % per;
+    } else {
+      tm = b / ntn;
+      tn = b % ntn;
+    }
+  }
+  const int64_t m0 = static_cast<int64_t>(tm) * kQT;
+  const int n0 = tn * kQT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
 
@@ -165,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
       gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // staging: thread -> row tid/2, 16 columns at (tid&1)*16
-  const int sr = tid >> 1, sk = (tid & 1) * 16;
+  // staging: thread -> row tid/2, 32 columns at (tid&1)*32 (two 16-column halves)
+  const int sr = tid >> 1, sk = (tid & 1) * 32;
   const int64_t xrow = m0 + sr;
   const bool xlive = xrow < T;
   const uint16_t* xp = x + (xlive ? xrow : 0) * K + sk;
@@ -175,42 +193,49 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
   const uint32_t* wp = qw.codes + static_cast<int64_t>(wlive ? wrow : 0) * qw.wpr;
   const float* zp = qw.zeros + static_cast<int64_t>(wlive ? wrow : 0) * qw.gpr;
 
-  uint4 xa[2];
-  uint32_t cw[Codes16<BITS>::NW];
+  uint4 xa[4];
+  uint32_t cw[2][Codes16<BITS>::NW];
   float zc = 0.f;
   int kf = 0;
-  // global loads of a step (raw code words; unpacked when staged)
+  // global loads of a step (raw code words; unpacked when staged); the 32
+  // columns of a thread lie in one group (groups are >= 32 columns, aligned)
   auto fetch = [&](int k0) {
     kf = k0 + sk;
     if (xlive) {
       const uint4* q = reinterpret_cast<const uint4*>(xp + k0);
-      xa[0] = q[0];
-      xa[1] = q[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = q[i];
     } else {
-      xa[0] = xa[1] = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = uint4{0u, 0u, 0u, 0u};
     }
     if (wlive) {
-      load_codes16<BITS>(wp, kf, qw.wpr, cw);
+      load_codes16<BITS>(wp, kf, qw.wpr, cw[0]);
+      load_codes16<BITS>(wp, kf + 16, qw.wpr, cw[1]);
       zc = zp[kf >> qw.lg_group];
     }
   };
   auto stage = [&](int buf) {
     uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][sk]);
-    da[0] = xa[0];
-    da[1] = xa[1];
-    uint32_t wb[8];
-    if (wlive) {
-      unpack16<BITS>(cw, kf, zc, wb);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wb[i] = 0u;
-    }
+    for (int i = 0; i < 4; ++i) da[i] = xa[i];
     uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr][sk]);
-    db[0] = uint4{wb[0], wb[1], wb[2], wb[3]};
-    db[1] = uint4{wb[4], wb[5], wb[6], wb[7]};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wb[8];
+      if (wlive) {
+        unpack16<BITS>(cw[h], kf + 16 * h, zc, wb);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wb[i] = 0u;
+      }
+      db[2 * h] = uint4{wb[0], wb[1], wb[2], wb[3]};
+      db[2 * h + 1] = uint4{wb[4], wb[5], wb[6], wb[7]};
+    }
   };
 
-  const int steps_per_group = (1 << qw.lg_group) / kQK;
+  // group >= 64: whole steps per group; group 32: two groups per step
+  const int steps_per_group = (1 << qw.lg_group) >= kQK ? (1 << qw.lg_group) / kQK : 1;
   fetch(0);
   stage(0);
   __syncthreads();
@@ -219,29 +244,36 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
   for (int st = 0; st < nsteps; ++st) {
     const int k0 = st * kQK;
     if (st + 1 < nsteps) fetch(k0 + kQK);
-    const int kc = 8 * (lane >> 4);
-    bf16x8 af[4], bf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm + i * 16 + (lane & 15)][kc]);
+    for (int kh = 0; kh < kQK / 32; ++kh) {
+      const int kc = kh * 32 + 8 * (lane >> 4);
+      bf16x8 af[4], bf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn + j * 16 + (lane & 15)][kc]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm + i * 16 + (lane & 15)][kc]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], gacc[i][j], 0, 0, 0);
-    if ((st + 1) % steps_per_group == 0) {
-      const int g = k0 >> qw.lg_group;
+        bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn + j * 16 + (lane & 15)][kc]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn + j * 16 + (lane & 15);
-        const float sc = n < N ? qw.scales[static_cast<int64_t>(n) * qw.gpr + g] : 0.f;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i][j] += sc * gacc[i][j];
-          gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j)
+          gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], gacc[i][j], 0, 0, 0);
+      // a group ends after this half-step: with 32-column groups every half,
+      // else at the end of the group's last step
+      const bool ends = (1 << qw.lg_group) < kQK ? true
+                                                 : (kh == kQK / 32 - 1 && (st + 1) % steps_per_group == 0);
+      if (ends) {
+        const int g = (k0 + kh * 32) >> qw.lg_group;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn + j * 16 + (lane & 15);
+          const float sc = n < N ? qw.scales[static_cast<int64_t>(n) * qw.gpr + g] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][j] += sc * gacc[i][j];
+            gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
     }
@@ -306,7 +338,7 @@ hipError_t launch_merge(const int32_t* row_ptr, const int32_t* E, const float* c
 
 hipError_t launch_qgemm(const uint16_t* x, int64_t T, int K, int N, const QuantW& qw,
                         const float* add, uint16_t* y, hipStream_t s) {
-  const dim3 grid((N + kQT - 1) / kQT, static_cast<unsigned>((T + kQT - 1) / kQT));
+  const dim3 grid(static_cast<unsigned>(((N + kQT - 1) / kQT) * ((T + kQT - 1) / kQT)));
   switch (qw.bits) {
     case 2:
       hipLaunchKernelGGL(qgemm_kernel<2>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);

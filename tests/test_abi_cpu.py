@@ -222,6 +222,7 @@ def test_quantized_base_validation(q):
                                 a["E"], a["c"], a["alpha"], a["y"], a["ws"], a["wsb"], None)
     assert fwd(act=0) == DTYPE                  # the base GEMM takes bf16 activations
     assert fwd(d_in=16, group=16) == SHAPE
+    assert fwd(d_in=32, group=32) == SHAPE       # below one 64-deep step
     assert fwd(group=16) == INVALID              # groups below one MFMA depth
     assert fwd(bits=1) == INVALID
     assert fwd(x=FAKE + 2) == ALIGN

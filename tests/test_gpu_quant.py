@@ -84,7 +84,7 @@ def test_merge(q, d_out, d_in, bits, group, p, out):
 
 
 @pytest.mark.parametrize("T,d_out,d_in,bits,group,p", [
-    (1, 37, 32, 4, 32, 40), (5, 200, 64, 2, 64, 700), (130, 129, 256, 3, 128, 1500),
+    (1, 37, 64, 4, 32, 40), (5, 200, 64, 2, 64, 700), (130, 129, 256, 3, 128, 1500),
     (300, 256, 1024, 4, 128, 4000), (77, 64, 4096, 8, 128, 3000), (200, 96, 512, 4, 64, 0),
     (129, 300, 128, 4, 32, 300 * 128)])
 def test_layer_forward(q, T, d_out, d_in, bits, group, p):
