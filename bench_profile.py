@@ -25,7 +25,7 @@ import bench
 # ids timed over several kernels: listed in the table, no per-launch traffic line
 MULTI_KERNEL_IDS = {"GLOBAL_THRESHOLD", "CALIB_PREPARE", "CALIB_SYSTEM", "REFINE"}
 # ids with no bench.py event of their own: listed in the table only
-TABLE_ONLY_IDS = {"INIT_SELECT_GLOBAL"}
+TABLE_ONLY_IDS = {"INIT_SELECT_GLOBAL", "LAYER_SPMM"}
 
 # kernel symbol prefix -> profiling ids (spmm and fwht resolved by template arguments)
 KERNEL_IDS = {
@@ -68,8 +68,13 @@ def kernel_ids(name: str):
     if n.startswith("rows_dc_kernel<"):
         return ["BWD_SPMM"]
     if n.startswith("rows_kernel<"):
-        # the plain gather: forward (source z, fp32); bench.py's backward always forms dc
-        return ["FWD_SPMM"] if template_args(n)[0] == "float" else []
+        # the plain gather: forward (source z, fp32; bf16 output as in the
+        # step); the quantized layer's adapter writes fp32; bench.py's
+        # backward always forms dc
+        a = template_args(n)
+        if a[0] != "float":
+            return []
+        return ["FWD_SPMM"] if a[1] == "unsigned short" else ["LAYER_SPMM"]
     if n.startswith("gemm64_kernel<"):
         # A read k-major (calibration tokens): the Hessian; else dW_Q Hs
         return ["HESSIAN"] if template_args(n)[1] == "true" else ["CALIB_PREPARE"]
