@@ -21,6 +21,9 @@ Sources (cited by page title and section):
 
 Readings of points the pages leave open (all listed in the design notes):
   * H is the Sylvester (natural-order) +-1 matrix, unnormalised; H^-1 = H/n.
+    For an input width d_in that is not a power of two, H is block-diagonal
+    with Sylvester blocks of order b, the largest power of two dividing
+    d_in, and H^-1 = H/b (``wht_matrix``).
   * AdaAlloc's budget formula is missing from the notes; it is read as
     p_i proportional to w_i^(1/t) (t = 1: proportional), floor rounding, a
     per-row floor m and cap d_in enforced by fix-and-reallocate passes (rows
@@ -61,7 +64,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 __all__ = [
-    "sylvester", "transform", "row_norms", "adaalloc", "adaalloc_margins",
+    "sylvester", "block_size", "wht_matrix", "wht", "transform", "row_norms", "adaalloc", "adaalloc_margins",
     "select", "values", "refine_ls", "csc", "init_select", "splitmix64", "magnitude_keys",
     "random_keys", "global_select", "init_select_global", "hessian", "damped",
     "activation_error_norms", "refine_system", "cholesky_lower", "refine_values",
@@ -95,6 +98,40 @@ def sylvester(n: int) -> np.ndarray:
     return _sylvester_cached(int(n))
 
 
+def block_size(d_in: int) -> int:
+    """b = the largest power of two dividing d_in."""
+    d_in = int(d_in)
+    if d_in < 1:
+        raise ValueError("d_in must be positive")
+    return d_in & -d_in
+
+
+def wht_matrix(d_in: int) -> np.ndarray:
+    """The transform H for an input width d_in (dense, fp64). For a power of
+    two it is the Sylvester matrix of that order. Otherwise, d_in = m * b
+    with b the largest power of two dividing it and m odd, and H is
+    block-diagonal with m copies of the Sylvester matrix of order b. This
+    is the reading for widths the pages do not cover: it keeps +-1 entries,
+    orthogonality (H H^T = b I, so H^-1 = H / b) and the add/subtract
+    transform."""
+    b = block_size(d_in)
+    m = d_in // b
+    Hb = sylvester(b)
+    if m == 1:
+        return Hb
+    return np.kron(np.eye(m), Hb)
+
+
+def wht(A: np.ndarray, d_in: int) -> np.ndarray:
+    """A @ H for H = wht_matrix(d_in), fp64, applied block by block (the
+    product with a block-diagonal matrix, without forming it)."""
+    A = np.asarray(A, dtype=np.float64)
+    b = block_size(d_in)
+    m = d_in // b
+    lead = A.shape[:-1]
+    return (A.reshape(lead + (m, b)) @ sylvester(b)).reshape(lead + (d_in,))
+
+
 # --------------------------------------------------------------------------
 # O2, O3: dense solution and row error norms   ([PN] 关键设计 2, 3)
 # --------------------------------------------------------------------------
@@ -104,7 +141,7 @@ def transform(dwq: np.ndarray) -> np.ndarray:
     refinement sub-problem with R = I ([PN] 关键设计 3), the candidates AdaAlloc
     picks from ([PN] 关键设计 2)."""
     d_in = dwq.shape[1]
-    return np.asarray(dwq, dtype=np.float64) @ sylvester(d_in)
+    return wht(dwq, d_in)
 
 
 def row_norms(dwq: np.ndarray) -> np.ndarray:
@@ -415,10 +452,10 @@ def refine_system(dwq: np.ndarray, Hs: np.ndarray) -> Tuple[np.ndarray, np.ndarr
     """G = H Hs H / n^2 (the Gram matrix of the rows of B = H^-1 R) and
     Q = dW_Q Hs H / n (row i holds v B^T), both fp64 dense."""
     d_in = dwq.shape[1]
-    H = sylvester(d_in)
+    b = float(block_size(d_in))
     Hs = np.asarray(Hs, dtype=np.float64)
-    G = (H @ Hs @ H) / float(d_in) ** 2
-    Q = (np.asarray(dwq, dtype=np.float64) @ Hs @ H) / float(d_in)
+    G = wht(wht(Hs, d_in).T, d_in) / b ** 2        # H Hs H (H and Hs symmetric)
+    Q = wht(np.asarray(dwq, dtype=np.float64) @ Hs, d_in) / b
     return G, Q
 
 
@@ -495,7 +532,7 @@ def layer_output_error(dwq: np.ndarray, X: np.ndarray, E: np.ndarray, c: np.ndar
     init's objective ([PN] 损失函数 / 训练策略)."""
     d_out, d_in = dwq.shape
     F = scatter_dense(E, np.asarray(c, dtype=np.float64), d_out, d_in)
-    resid = np.asarray(dwq, dtype=np.float64) - F @ sylvester(d_in) / float(d_in)
+    resid = np.asarray(dwq, dtype=np.float64) - wht(F, d_in) / float(block_size(d_in))
     r = resid @ np.asarray(X, dtype=np.float64).T
     return float(np.sum(r * r))
 
@@ -565,9 +602,10 @@ def materialize(E: np.ndarray, c: np.ndarray, d_out: int, d_in: int,
 
     F is held as a scipy sparse matrix so the product skips its zeros; every
     output entry is the same sum as the dense product F @ H."""
-    H = sylvester(d_in)
     F = _scatter_sparse(E, c, d_out, d_in)
-    return (alpha / d_in) * np.asarray(F @ H)
+    if block_size(d_in) == d_in:
+        return (alpha / d_in) * np.asarray(F @ sylvester(d_in))
+    return (alpha / block_size(d_in)) * wht(F.toarray(), d_in)
 
 
 def forward(x: np.ndarray, dW: np.ndarray) -> np.ndarray:
@@ -587,7 +625,7 @@ def backward(x: np.ndarray, dy: np.ndarray, E: np.ndarray, c: np.ndarray,
     dy64 = np.asarray(dy, dtype=np.float64)
     dx = dy64 @ dW
     G = dy64.T @ x64
-    dF = (alpha / d_in) * (G @ sylvester(d_in))
+    dF = (alpha / block_size(d_in)) * wht(G, d_in)
     dc = dF[E[:, 0], E[:, 1]]
     return dx, dc
 
@@ -601,7 +639,7 @@ def backward_dc_rows(x: np.ndarray, dy: np.ndarray, E: np.ndarray,
     rows = np.asarray(rows, dtype=np.int64)
     x64 = np.asarray(x, dtype=np.float64)
     G = np.asarray(dy, dtype=np.float64)[:, rows].T @ x64   # [len(rows)][d_in]
-    dF = (alpha / d_in) * (G @ sylvester(d_in))
+    dF = (alpha / block_size(d_in)) * wht(G, d_in)
     where = {int(r): a for a, r in enumerate(rows)}
     ks = np.nonzero(np.isin(E[:, 0], rows))[0]
     vals = np.array([dF[where[int(E[k, 0])], int(E[k, 1])] for k in ks])

@@ -780,3 +780,70 @@ def test_merge_and_layer_forward_definitions():
     # no adapter: the plain quantized layer
     y0 = O.layer_forward(x, W_Q, r["E"], np.zeros_like(r["c"]), 0.7)
     assert np.allclose(y0, x @ W_Q.astype(np.float64).T, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------- widths that are not powers of two
+
+@pytest.mark.parametrize("d_in", [12, 24, 40, 96, 112, 14336])
+def test_block_size_and_structure(d_in):
+    b = O.block_size(d_in)
+    assert b & (b - 1) == 0 and d_in % b == 0 and (d_in // b) % 2 == 1
+    if d_in <= 112:
+        from scipy.linalg import block_diag, hadamard
+        H = O.wht_matrix(d_in)
+        assert np.array_equal(H, block_diag(*[hadamard(b).astype(np.float64)] * (d_in // b)))
+        assert np.array_equal(H @ H.T, b * np.eye(d_in))        # H^-1 = H / b
+        A = np.random.default_rng(d_in).standard_normal((5, d_in))
+        assert np.allclose(O.wht(A, d_in), A @ H, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 64, 1024])
+def test_wht_matrix_is_sylvester_for_powers_of_two(n):
+    assert np.array_equal(O.wht_matrix(n), O.sylvester(n))
+
+
+@pytest.mark.parametrize("d_in", [12, 40])
+def test_full_budget_reconstructs_at_block_widths(d_in):
+    dwq = _rand_dwq(5, d_in, d_in)
+    r = O.init_select(dwq, 5 * d_in, m=3)
+    C = O.transform(dwq)
+    dW = O.materialize(r["E"], C[r["E"][:, 0], r["E"][:, 1]], 5, d_in, 1.0)
+    assert np.allclose(dW, dwq.astype(np.float64), rtol=0, atol=1e-14)
+
+
+def test_fwd_bwd_against_torch_autograd_at_a_block_width():
+    torch = pytest.importorskip("torch")
+    alpha, d_out, n = 0.7, 9, 24                    # b = 8, three blocks
+    dwq = _rand_dwq(d_out, n, 31)
+    r = O.init_select(dwq, 60, m=3)
+    E, c = r["E"], r["c"]
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((7, n))
+    dy = rng.standard_normal((7, d_out))
+    H = torch.tensor(O.wht_matrix(n))
+    ct = torch.tensor(c.astype(np.float64), requires_grad=True)
+    xt = torch.tensor(x, requires_grad=True)
+    F = torch.zeros(d_out, n, dtype=torch.float64)
+    F = F.index_put((torch.tensor(E[:, 0]).long(), torch.tensor(E[:, 1]).long()), ct)
+    y = xt @ (alpha * F @ torch.linalg.inv(H)).T
+    y.backward(torch.tensor(dy))
+    dx, dc = O.backward(x, dy, E, c, d_out, n, alpha)
+    assert np.allclose(y.detach().numpy(), O.forward(x, O.materialize(E, c, d_out, n, alpha)),
+                       rtol=0, atol=1e-12)
+    assert np.allclose(xt.grad.numpy(), dx, rtol=0, atol=1e-12)
+    assert np.allclose(ct.grad.numpy(), dc, rtol=0, atol=1e-12)
+
+
+def test_refine_matches_lstsq_at_a_block_width():
+    d_out, d_in = 6, 48                             # b = 16, three blocks
+    dwq = _rand_dwq(d_out, d_in, 33)
+    X = _calib(120, d_in, 34)
+    r = O.init_select_calibrated(dwq, O.hessian(X), 80, m=3)
+    H = O.wht_matrix(d_in)
+    b = O.block_size(d_in)
+    for i in range(d_out):
+        a, e = r["row_ptr"][i], r["row_ptr"][i + 1]
+        S = r["E"][a:e, 1]
+        D = (H / b)[S, :] @ X.T
+        sol, *_ = np.linalg.lstsq(D.T, dwq[i].astype(np.float64) @ X.T, rcond=None)
+        assert np.allclose(r["x"][a:e], sol, rtol=1e-9, atol=1e-12 * np.abs(sol).max())
