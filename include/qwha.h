@@ -27,9 +27,15 @@
  *  - Alignment: dense activation / weight arrays and workspaces must be
  *    16-byte aligned, index and value arrays 4-byte aligned
  *    (QWHA_ERR_ALIGN otherwise).
- *  - Shapes: d_in is a power of two in [2, 16384] (QWHA_ERR_SHAPE
- *    otherwise; the pages only use power-of-two transform lengths),
- *    1 <= d_out <= 1048576, T >= 0 (T == 0 is a no-op), p <= 2^31 - 1.
+ *  - Shapes: 2 <= d_in <= 16384, 1 <= d_out <= 1048576, T >= 0 (T == 0
+ *    is a no-op), p <= 2^31 - 1 (QWHA_ERR_SHAPE otherwise). The transform
+ *    H is the Sylvester matrix of order d_in when d_in is a power of two.
+ *    Otherwise d_in = m * b, with b the largest power of two dividing it
+ *    (m odd), and H is block-diagonal with m Sylvester blocks of order b,
+ *    H^-1 = H / b, so every "/ n" below reads "/ b". The pages only use
+ *    power-of-two widths; this reading keeps the +-1 entries, orthogonality
+ *    and the fast transform. It requires b >= 64 (d_in = 14336 = 7 * 2048
+ *    qualifies, 96 = 3 * 32 does not). qwha_fwht takes powers of two only.
  *  - Aliasing: inputs and outputs must not overlap, except that an output is
  *    read back when its `accumulate` flag is set.
  *  - Preconditions not checked (they would need device reads): inputs are

@@ -58,12 +58,23 @@ int log2_pow2(int32_t n) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-qwha_status check_dims(int32_t d_out, int32_t d_in, int* log_n) {
-  *log_n = log2_pow2(d_in);
-  if (*log_n < 0) return fail(QWHA_ERR_SHAPE, "d_in=%d is not a power of two in [2, 16384]", d_in);
+// d_in = nblk * 2^log_b with 2^log_b the largest power of two dividing it:
+// the transform is one Sylvester matrix (nblk = 1) or nblk Sylvester blocks
+// on the diagonal, which needs blocks of at least 64 columns.
+qwha_status check_width(int32_t d_out, int32_t d_in, int* log_b, int* nblk) {
+  if (d_in < 2 || d_in > 16384)
+    return fail(QWHA_ERR_SHAPE, "d_in=%d outside [2, 16384]", d_in);
+  const int32_t b = d_in & -d_in;
+  *nblk = d_in / b;
+  *log_b = log2_pow2(b);
+  if (*nblk > 1 && b < 64)
+    return fail(QWHA_ERR_SHAPE,
+                "d_in=%d: a width that is not a power of two needs a power-of-two factor of at "
+                "least 64 (block-diagonal transform)", d_in);
   if (d_out < 1 || d_out > (1 << 20)) return fail(QWHA_ERR_SHAPE, "d_out=%d out of [1, 2^20]", d_out);
   return QWHA_OK;
 }
+
 
 qwha_status check_p(int64_t p, int32_t d_out, int32_t d_in) {
   if (p < 0 || p > INT32_MAX || p > static_cast<int64_t>(d_out) * d_in)
@@ -181,7 +192,8 @@ qwha_status qwha_init_select(const float* dWq, int32_t d_out, int32_t d_in, int6
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   if (min_per_row < 0 || min_per_row > d_in)
     return fail(QWHA_ERR_INVALID_ARG, "min_per_row=%d outside [0, d_in]", min_per_row);
   if (!(temperature > 0.0) || !isfinite(temperature))
@@ -211,7 +223,7 @@ qwha_status qwha_init_select(const float* dWq, int32_t d_out, int32_t d_in, int6
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_INIT_SELECT, stream,
                            [&] {
                              return launch_init_select(dWq, d_out, log_n, row_ptr, E, c, 0,
-                                                       nullptr, 0, stream);
+                                                       nullptr, 0, stream, nblk);
                            }),
                      "init_select"));
   QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
@@ -234,7 +246,8 @@ qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_i
                                     hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   if (strategy != QWHA_SELECT_MAGNITUDE && strategy != QWHA_SELECT_RANDOM)
     return fail(QWHA_ERR_INVALID_ARG, "strategy=%d is neither QWHA_SELECT_MAGNITUDE nor "
                 "QWHA_SELECT_RANDOM", strategy);
@@ -257,13 +270,14 @@ qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_i
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_GLOBAL_THRESHOLD, stream,
                            [&] {
                              return launch_global_budgets(dWq, d_out, log_n, p, strategy, seed,
-                                                          row_ptr, workspace, &gtau, stream);
+                                                          row_ptr, workspace, &gtau, stream,
+                                                          nblk);
                            }),
                      "global_threshold"));
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_INIT_SELECT, stream,
                            [&] {
                              return launch_init_select(dWq, d_out, log_n, row_ptr, E, c,
-                                                       strategy, gtau, seed, stream);
+                                                       strategy, gtau, seed, stream, nblk);
                            }),
                      "init_select"));
   QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
@@ -276,8 +290,10 @@ qwha_status qwha_init_select_global(const float* dWq, int32_t d_out, int32_t d_i
 qwha_status qwha_hessian(const void* X, qwha_dtype x_dtype, int64_t N, int32_t d_in, double* Hs,
                          int32_t accumulate, hipStream_t stream) {
   g_err[0] = 0;
-  if (log2_pow2(d_in) < 0)
-    return fail(QWHA_ERR_SHAPE, "d_in=%d is not a power of two in [2, 16384]", d_in);
+  {
+    int log_b, nblk;
+    QWHA_TRY(check_width(1, d_in, &log_b, &nblk));
+  }
   if (N < 0 || N > (static_cast<int64_t>(1) << 40))
     return fail(QWHA_ERR_SHAPE, "N=%lld out of [0, 2^40]", static_cast<long long>(N));
   QWHA_TRY(check_dt(x_dtype, "x_dtype"));
@@ -308,7 +324,8 @@ qwha_status qwha_init_select_calibrated(const float* dWq, int32_t d_out, int32_t
                                         hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   if (min_per_row < 0 || min_per_row > d_in)
     return fail(QWHA_ERR_INVALID_ARG, "min_per_row=%d outside [0, d_in]", min_per_row);
   if (!(temperature > 0.0) || !isfinite(temperature))
@@ -341,13 +358,14 @@ qwha_status qwha_init_select_calibrated(const float* dWq, int32_t d_out, int32_t
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_CALIB_PREPARE, stream,
                            [&] {
                              return launch_calib_prepare(dWq, d_out, log_n, Hs, damp, workspace,
-                                                         &w, stream);
+                                                         &w, stream, nblk);
                            }),
                      "calib_prepare"));
   QWHA_TRY(hip_check(launch_adaalloc(w, d_out, d_in, p, min_per_row, temperature, row_ptr,
                                      at(workspace, cal), stream),
                      "adaalloc"));
-  QWHA_TRY(hip_check(launch_init_select(dWq, d_out, log_n, row_ptr, E, c, 0, nullptr, 0, stream),
+  QWHA_TRY(hip_check(launch_init_select(dWq, d_out, log_n, row_ptr, E, c, 0, nullptr, 0, stream,
+                                        nblk),
                      "init_select"));
   QWHA_TRY(hip_check(launch_csc_build(row_ptr, E, d_out, d_in, col_ptr, csc_perm,
                                       at(workspace, cal + alloc), stream),
@@ -355,7 +373,7 @@ qwha_status qwha_init_select_calibrated(const float* dWq, int32_t d_out, int32_t
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_CALIB_SYSTEM, stream,
                            [&] {
                              return launch_calib_finish(E, p, d_out, log_n, Hs, workspace, G, rhs,
-                                                        stream);
+                                                        stream, nblk);
                            }),
                      "calib_system"));
   return QWHA_OK;
@@ -378,7 +396,8 @@ qwha_status qwha_refine_values(const int32_t* row_ptr, const int32_t* E, const d
                                size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_NEED(row_ptr, 4);
   QWHA_NEED(G, 8);
@@ -407,7 +426,8 @@ qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* 
                        qwha_dtype out_dtype, void* W, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_quant(bits, group, d_in, 1));
   QWHA_TRY(check_dt(out_dtype, "out_dtype"));
@@ -425,7 +445,7 @@ qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* 
   return hip_check(timed(QWHA_KERNEL_MERGE, stream,
                          [&] {
                            return launch_merge(row_ptr, E, c, d_out, log_n, alpha, qw,
-                                               static_cast<Dt>(out_dtype), W, stream);
+                                               static_cast<Dt>(out_dtype), W, stream, nblk);
                          }),
                    "merge");
 }
@@ -442,7 +462,8 @@ qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_i
                            void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   if (d_in < 64) return fail(QWHA_ERR_SHAPE, "d_in=%d below 64", d_in);
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_dt(act, "act"));
@@ -473,8 +494,8 @@ qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_i
     float* z = reinterpret_cast<float*>(at(workspace, l.z));
     void* prep = at(workspace, l.prep);
     y32 = reinterpret_cast<float*>(at(workspace, l.total));
-    QWHA_TRY(hip_check(launch_fwht(x, Dt::BF16, z, Dt::F32, T, log_n,
-                                   1.0f / static_cast<float>(d_in), 0, stream),
+    QWHA_TRY(hip_check(launch_fwht(x, Dt::BF16, z, Dt::F32, T * nblk, log_n,
+                                   1.0f / static_cast<float>(1 << log_n), 0, stream),
                        "layer fwht"));
     QWHA_TRY(hip_check(launch_prep_csr(row_ptr, E, c, d_out, p, l.plan, prep, stream),
                        "layer prep"));
@@ -498,7 +519,8 @@ qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const flo
                              hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_dt(out_dtype, "out_dtype"));
   if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
@@ -513,7 +535,7 @@ qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const flo
                          [&] {
                            return launch_materialize(row_ptr, E, c, d_out, log_n, alpha,
                                                      static_cast<Dt>(out_dtype), dW, accumulate,
-                                                     stream);
+                                                     stream, nblk);
                          }),
                    "materialize");
 }
@@ -530,7 +552,8 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
                      size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_dt(act, "act"));
   if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
@@ -554,8 +577,8 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
   const Dt adt = static_cast<Dt>(act);
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
                            [&] {
-                             return launch_fwht(x, adt, z, Dt::F32, T, log_n,
-                                                1.0f / static_cast<float>(d_in), 0, stream);
+                             return launch_fwht(x, adt, z, Dt::F32, T * nblk, log_n,
+                                                1.0f / static_cast<float>(1 << log_n), 0, stream);
                            }),
                      "fwd fwht"));
   QWHA_TRY(hip_check(launch_prep_csr(row_ptr, E, c, d_out, p, l.plan, prep, stream), "fwd prep"));
@@ -583,7 +606,8 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
                      size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
-  QWHA_TRY(check_dims(d_out, d_in, &log_n));
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_dt(act, "act"));
   if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
@@ -622,8 +646,9 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
   if (dc)
     QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_X, stream,
                              [&] {
-                               return launch_fwht(x, adt, z, Dt::F32, T, log_n,
-                                                  1.0f / static_cast<float>(d_in), 0, stream);
+                               return launch_fwht(x, adt, z, Dt::F32, T * nblk, log_n,
+                                                  1.0f / static_cast<float>(1 << log_n), 0,
+                                                  stream);
                              }),
                        "bwd fwht(x)"));
   QWHA_TRY(hip_check(launch_prep_csc(col_ptr, csc_perm, E, c, d_in, p, l.plan, prep, stream),
@@ -637,8 +662,9 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
   if (dx)
     QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_DX, stream,
                              [&] {
-                               return launch_fwht(dz, Dt::F32, dx, adt, T, log_n,
-                                                  alpha / static_cast<float>(d_in), accumulate_dx,
+                               return launch_fwht(dz, Dt::F32, dx, adt, T * nblk, log_n,
+                                                  alpha / static_cast<float>(1 << log_n),
+                                                  accumulate_dx,
                                                   stream);
                              }),
                        "bwd fwht(dz)"));

@@ -303,24 +303,35 @@ struct SelCfg {
 // keys equal to it, as many as its budget leaves (lowest column first); the
 // keys are |C| (mode 1) or the complement of the position's SplitMix64 draw
 // (mode 2, output row*N + col of the generator seeded with `seed`).
-template <int LOG_N, int MODE>
-__global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
+//
+// BLOCKED: a row of nblk * N columns under the block-diagonal transform (nblk
+// Sylvester blocks of order N): thread t = blk * TPR + u transforms its part
+// of block blk in that block's slice of the dynamic LDS; the selection runs
+// over the whole row, and thread t holds columns t*EPT .. t*EPT + EPT - 1 in
+// both cases.
+template <int LOG_N, int MODE, bool BLOCKED>
+__global__ __launch_bounds__(BLOCKED ? 1024 : SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     const float* __restrict__ dWq, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ E,
     float* __restrict__ c, const unsigned long long* __restrict__ gtau,
-    unsigned long long seed) {
+    unsigned long long seed, int nblk) {
   using F = Fwht<LOG_N>;
-  __shared__ double lds[F::LDS];
+  extern __shared__ double lds_blocks[];
+  __shared__ double lds_row[BLOCKED ? 1 : F::LDS];
   __shared__ int red[32];
   __shared__ int scan_tmp[16];
   const int row = blockIdx.x;
-  const int u = threadIdx.x;
-  const bool active = u < F::TPR;
+  const int t = threadIdx.x;
+  const int u = BLOCKED ? t % F::TPR : t;
+  const int d_in = BLOCKED ? nblk * F::N : F::N;
+  const bool active = BLOCKED ? t < nblk * F::TPR : t < F::TPR;
+  double* lds = BLOCKED ? lds_blocks + (t / F::TPR) * F::LDS : lds_row;
+  const int col0 = t * F::EPT;     // first column this thread holds
   const int base = row_ptr[row];
   const int k = row_ptr[row + 1] - base;
 
   double v[F::EPT];
   if (active) {
-    const float* src = dWq + static_cast<int64_t>(row) * F::N + u * F::EPT;
+    const float* src = dWq + static_cast<int64_t>(row) * d_in + col0;
     if constexpr (F::EPT == 16) {
       load16(src, v);
     } else {
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     for (int r = 0; r < F::EPT; ++r) {
       v[r] = lds[F::pad(u * F::EPT + r)];
       key[r] = MODE == 2
-                   ? ~splitmix64(seed, static_cast<unsigned long long>(row) * F::N + u * F::EPT + r)
+                   ? ~splitmix64(seed, static_cast<unsigned long long>(row) * d_in + col0 + r)
                    : static_cast<unsigned long long>(__double_as_longlong(v[r])) &
                          0x7FFFFFFFFFFFFFFFull;
     }
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
   // keys >= lo are exactly k.
   unsigned long long tau = 0;
   int need = 0;      // how many |C| == tau are taken (lowest index first)
-  bool all = (k >= F::N), none = (k <= 0);
+  bool all = (k >= d_in), none = (k <= 0);
   int parity = 0;
   if (!all && !none && MODE != 0) {
     tau = *gtau;
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     };
     // count(top32 >= lo32) >= k > count(top32 >= hi32); keys are < 2^63
     unsigned lo32 = 0, hi32 = 1u << 31;
-    int cnt_lo = F::N;
+    int cnt_lo = d_in;
     while (hi32 - lo32 > 1 && cnt_lo != k) {
       const unsigned mid = lo32 + ((hi32 - lo32) >> 1);
       const int cnt = count_ge32(mid);
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     for (int r = 0; r < F::EPT; ++r) {
       if (sel & (1u << r)) {
         E[2 * static_cast<int64_t>(pos)] = row;
-        E[2 * static_cast<int64_t>(pos) + 1] = u * F::EPT + r;
+        E[2 * static_cast<int64_t>(pos) + 1] = col0 + r;
         c[pos] = __double2float_rn(v[r]);
         ++pos;
       }
@@ -450,34 +461,58 @@ __global__ __launch_bounds__(SelCfg<LOG_N>::BLOCK) void init_select_kernel(
   }
 }
 
-template <int L>
+template <int L, bool BLOCKED>
 hipError_t launch_select_mode(const float* dWq, int d_out, const int32_t* row_ptr, int32_t* E,
                               float* c, int mode, const unsigned long long* gtau,
-                              unsigned long long seed, hipStream_t s) {
-  const dim3 grid(d_out), block(SelCfg<L>::BLOCK);
-  if (mode == 0)
-    hipLaunchKernelGGL((init_select_kernel<L, 0>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
-                       seed);
-  else if (mode == 1)
-    hipLaunchKernelGGL((init_select_kernel<L, 1>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
-                       seed);
-  else
-    hipLaunchKernelGGL((init_select_kernel<L, 2>), grid, block, 0, s, dWq, row_ptr, E, c, gtau,
-                       seed);
-  return hipGetLastError();
+                              unsigned long long seed, int nblk, hipStream_t s) {
+  using F = Fwht<L>;
+  const dim3 grid(d_out);
+  int threads = SelCfg<L>::BLOCK;
+  size_t lds = 0;
+  if (BLOCKED) {
+    threads = nblk * F::TPR < 64 ? 64 : nblk * F::TPR;
+    lds = static_cast<size_t>(nblk) * F::LDS * sizeof(double);
+  }
+  const dim3 block(threads);
+  auto go = [&](auto kernel) {
+    if (BLOCKED) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, dWq, row_ptr, E, c, gtau, seed, nblk);
+    return hipGetLastError();
+  };
+  if (mode == 0) return go(init_select_kernel<L, 0, BLOCKED>);
+  if (mode == 1) return go(init_select_kernel<L, 1, BLOCKED>);
+  return go(init_select_kernel<L, 2, BLOCKED>);
 }
 
 hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
                               int32_t* E, float* c, int mode, const unsigned long long* gtau,
-                              unsigned long long seed, hipStream_t s) {
-  if (mode < 0 || mode > 2) return hipErrorInvalidValue;
-  switch (log_n) {
+                              unsigned long long seed, hipStream_t s, int nblk) {
+  if (mode < 0 || mode > 2 || nblk < 1) return hipErrorInvalidValue;
+  if (nblk == 1) {
+    switch (log_n) {
 #define QWHA_CASE(L)                                                                       \
   case L:                                                                                  \
-    return launch_select_mode<L>(dWq, d_out, row_ptr, E, c, mode, gtau, seed, s);
-    QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
-    QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
-    QWHA_CASE(14)
+    return launch_select_mode<L, false>(dWq, d_out, row_ptr, E, c, mode, gtau, seed, 1, s);
+      QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6)
+      QWHA_CASE(7) QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12)
+      QWHA_CASE(13) QWHA_CASE(14)
+#undef QWHA_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  // block widths: blocks of 64 .. 4096 columns, at most 1024 threads a row
+  switch (log_n) {
+#define QWHA_CASE(L)                                                                      \
+  case L:                                                                                 \
+    return launch_select_mode<L, true>(dWq, d_out, row_ptr, E, c, mode, gtau, seed, nblk, s);
+    QWHA_CASE(6) QWHA_CASE(7) QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11)
+    QWHA_CASE(12)
 #undef QWHA_CASE
     default:
       return hipErrorInvalidValue;

@@ -23,9 +23,11 @@ hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int 
 size_t adaalloc_scratch_bytes(int d_out);
 // mode 0: AdaAlloc budgets in row_ptr, per-row threshold; mode 1 / 2: the
 // global threshold *gtau on |C| / random keys (see select_global.hip)
+// nblk > 1: rows of nblk blocks of 2^log_n columns under the block-diagonal
+// transform (2^log_n in [64, 4096])
 hipError_t launch_init_select(const float* dWq, int d_out, int log_n, const int32_t* row_ptr,
                               int32_t* E, float* c, int mode, const unsigned long long* gtau,
-                              unsigned long long seed, hipStream_t s);
+                              unsigned long long seed, hipStream_t s, int nblk = 1);
 
 // ---- global selection variants (magnitude / random)
 size_t global_select_scratch_bytes(int d_out, int d_in, int mode);
@@ -33,7 +35,7 @@ size_t global_select_scratch_bytes(int d_out, int d_in, int mode);
 // writes row_ptr and the threshold at *gtau (inside the scratch)
 hipError_t launch_global_budgets(const float* dWq, int d_out, int log_n, int64_t p, int mode,
                                  unsigned long long seed, int32_t* row_ptr, void* scratch,
-                                 const unsigned long long** gtau, hipStream_t s);
+                                 const unsigned long long** gtau, hipStream_t s, int nblk = 1);
 size_t csc_scratch_bytes(int d_out, int d_in);
 hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
                             int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s);
@@ -46,11 +48,12 @@ size_t calibrated_scratch_bytes(int d_out, int d_in);
 // delta = damp * mean(diag Hs); M = dW_Q Hs; per row w_i (activation error
 // norm, returned in *w_out, inside the scratch) and Q = (M + delta dW_Q) H / n
 hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const double* Hs,
-                                double damp, void* scratch, double** w_out, hipStream_t s);
+                                double damp, void* scratch, double** w_out, hipStream_t s,
+                                int nblk = 1);
 // rhs[k] = Q[E_k]; G = H Hs H / n^2 + (delta / n) I
 hipError_t launch_calib_finish(const int32_t* E, int64_t p, int d_out, int log_n,
                                const double* Hs, void* scratch, double* G, double* rhs,
-                               hipStream_t s);
+                               hipStream_t s, int nblk = 1);
 size_t refine_header_bytes(int d_out);
 hipError_t launch_refine(const int32_t* row_ptr, const int32_t* E, const double* G, int d_in,
                          const double* rhs, int d_out, float* c, int32_t* status, void* ws,
@@ -74,15 +77,16 @@ QuantW make_quant(const uint32_t* codes, const float* scales, const float* zeros
 // W = W_Q + alpha F H^-1
 hipError_t launch_merge(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                         int log_n, float alpha, const QuantW& qw, Dt out_dt, void* W,
-                        hipStream_t s);
+                        hipStream_t s, int nblk = 1);
 // y = bf16(x W_Q^T + add), x bf16 [T][K], add fp32 [T][N], y bf16 [T][N]
 hipError_t launch_qgemm(const uint16_t* x, int64_t T, int K, int N, const QuantW& qw,
                         const float* add, uint16_t* y, hipStream_t s);
 
 // ---- materialize
+// nblk > 1: rows of nblk blocks of 2^log_n columns (block-diagonal transform)
 hipError_t launch_materialize(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                               int log_n, float alpha, Dt out_dt, void* dW, int accumulate,
-                              hipStream_t s);
+                              hipStream_t s, int nblk = 1);
 
 // ---- adapter forward / backward (gather SpMM / SDDMM)
 struct SpmmPlan {

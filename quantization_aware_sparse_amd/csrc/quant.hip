@@ -41,22 +41,27 @@ struct MergeCfg {
 template <int LOG_N, typename TOut>
 __global__ __launch_bounds__(MergeCfg<LOG_N>::BLOCK) void merge_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ E,
-    const float* __restrict__ c, int d_out, float scale, QuantW qw, TOut* __restrict__ W) {
+    const float* __restrict__ c, int d_out, int nblk, float scale, QuantW qw,
+    TOut* __restrict__ W) {
   using F = Fwht<LOG_N>;
   constexpr int RPW = MergeCfg<LOG_N>::RPW;
   __shared__ float lds_all[RPW * F::LDS];
   const int slot = threadIdx.x / F::TPR;
   const int u = threadIdx.x % F::TPR;
-  const int row = blockIdx.x * RPW + slot;
-  const bool live = row < d_out;
+  // virtual row r of the [d_out * nblk][N] view: block blk of row i
+  const int vrow = blockIdx.x * RPW + slot;
+  const bool live = vrow < d_out * nblk;
+  const int row = vrow / nblk, blk = vrow - row * nblk;
   float* lds = lds_all + slot * F::LDS;
 
   for (int j = u; j < F::LDS; j += F::TPR) lds[j] = 0.f;
   __syncthreads();
   if (live) {
     const int k1 = row_ptr[row + 1];
-    for (int k = row_ptr[row] + u; k < k1; k += F::TPR)
-      lds[F::pad(E[2 * static_cast<int64_t>(k) + 1])] = c[k];
+    for (int k = row_ptr[row] + u; k < k1; k += F::TPR) {
+      const int j = E[2 * static_cast<int64_t>(k) + 1];
+      if ((j >> LOG_N) == blk) lds[F::pad(j & (F::N - 1))] = c[k];
+    }
   }
   __syncthreads();
   float v[F::EPT];
@@ -64,22 +69,22 @@ __global__ __launch_bounds__(MergeCfg<LOG_N>::BLOCK) void merge_kernel(
   for (int r = 0; r < F::EPT; ++r) v[r] = lds[F::pad(u * F::EPT + r)];
   F::run(v, lds, u);
   if (live) {
-    TOut* dst = W + static_cast<int64_t>(row) * F::N;
+    TOut* dst = W + static_cast<int64_t>(vrow) * F::N;
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) {
       const int j = F::out_index(u, r);
-      Elem<TOut>::st(dst, j, dequant(qw, row, j) + v[r] * scale);
+      Elem<TOut>::st(dst, j, dequant(qw, row, blk * F::N + j) + v[r] * scale);
     }
   }
 }
 
 template <int LOG_N, typename TOut>
 hipError_t merge_t(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
-                   float scale, const QuantW& qw, void* W, hipStream_t s) {
+                   int nblk, float scale, const QuantW& qw, void* W, hipStream_t s) {
   constexpr int RPW = MergeCfg<LOG_N>::RPW;
-  const int blocks = (d_out + RPW - 1) / RPW;
+  const int blocks = (d_out * nblk + RPW - 1) / RPW;
   hipLaunchKernelGGL((merge_kernel<LOG_N, TOut>), dim3(blocks), dim3(MergeCfg<LOG_N>::BLOCK), 0,
-                     s, row_ptr, E, c, d_out, scale, qw, static_cast<TOut*>(W));
+                     s, row_ptr, E, c, d_out, nblk, scale, qw, static_cast<TOut*>(W));
   return hipGetLastError();
 }
 
@@ -319,14 +324,14 @@ QuantW make_quant(const uint32_t* codes, const float* scales, const float* zeros
 
 hipError_t launch_merge(const int32_t* row_ptr, const int32_t* E, const float* c, int d_out,
                         int log_n, float alpha, const QuantW& qw, Dt out_dt, void* W,
-                        hipStream_t s) {
+                        hipStream_t s, int nblk) {
   const float scale = alpha / static_cast<float>(1 << log_n);
   switch (log_n) {
 #define QWHA_CASE(L)                                                        \
   case L:                                                                   \
     return out_dt == Dt::F32                                                \
-               ? merge_t<L, float>(row_ptr, E, c, d_out, scale, qw, W, s)   \
-               : merge_t<L, uint16_t>(row_ptr, E, c, d_out, scale, qw, W, s);
+               ? merge_t<L, float>(row_ptr, E, c, d_out, nblk, scale, qw, W, s)   \
+               : merge_t<L, uint16_t>(row_ptr, E, c, d_out, nblk, scale, qw, W, s);
     QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
     QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
     QWHA_CASE(14)

@@ -250,22 +250,30 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 // Row i of M = dW_Q Hs: v = M[i,:] + delta dW_Q[i,:]; w_i = sqrt(max(v.dW_Q[i,:], 0));
 // Q[i,:] = v H / n (natural column order). Q may alias M.
-template <int LOG_N>
-__global__ __launch_bounds__(Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR) void calib_rows_kernel(
-    const double* M, const float* __restrict__ dWq, const double* __restrict__ delta, double* Q,
-    double* __restrict__ w) {
+// BLOCKED: rows of nblk blocks of N columns under the block-diagonal
+// transform; thread t = blk * TPR + u transforms its part of block blk in
+// that block's slice of the dynamic LDS; the dot spans the whole row.
+template <int LOG_N, bool BLOCKED>
+__global__ __launch_bounds__(BLOCKED ? 1024 : (Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR))
+void calib_rows_kernel(const double* M, const float* __restrict__ dWq,
+                       const double* __restrict__ delta, double* Q, double* __restrict__ w,
+                       int nblk) {
   using F = Fwht<LOG_N>;
-  __shared__ double lds[F::LDS];
+  extern __shared__ double lds_blocks[];
+  __shared__ double lds_row[BLOCKED ? 1 : F::LDS];
   __shared__ double red[16];
   const int64_t row = blockIdx.x;
-  const int u = threadIdx.x;
-  const bool active = u < F::TPR;
+  const int t = threadIdx.x;
+  const int u = BLOCKED ? t % F::TPR : t;
+  const int64_t d_in = BLOCKED ? static_cast<int64_t>(nblk) * F::N : F::N;
+  const bool active = BLOCKED ? t < nblk * F::TPR : t < F::TPR;
+  double* lds = BLOCKED ? lds_blocks + (t / F::TPR) * F::LDS : lds_row;
   const double dl = *delta;
   double v[F::EPT];
   double dot = 0.0;
   if (active) {
-    const double* src = M + row * F::N + u * F::EPT;
-    const float* dq = dWq + row * F::N + u * F::EPT;
+    const double* src = M + row * d_in + t * F::EPT;
+    const float* dq = dWq + row * d_in + t * F::EPT;
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) {
       const double d = static_cast<double>(dq[r]);
@@ -280,19 +288,21 @@ __global__ __launch_bounds__(Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR) void
   if (threadIdx.x == 0) w[row] = sqrt(dot > 0.0 ? dot : 0.0);
   F::run(v, lds, u, active);
   if (active) {
-    double* dst = Q + row * F::N;
+    double* dst = Q + row * d_in + (t / F::TPR) * F::N;
     const double inv_n = 1.0 / static_cast<double>(F::N);
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) dst[F::out_index(u, r)] = v[r] * inv_n;
   }
 }
 
-// out[r][:] = scale * in[r][:] H (fp64); with diag_num, out[r][r] += *diag_num * diag_mul.
-// in may alias out.
+// out[r][:] = scale * in[r][:] H (fp64); with diag_num, *diag_num * diag_mul
+// is added on the diagonal of the square matrix whose rows are nblk of these
+// rows each (row r is block r % nblk of matrix row r / nblk). in may alias
+// out.
 template <int LOG_N>
 __global__ __launch_bounds__(Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR) void fwht64_rows_kernel(
     const double* in, double* out, double scale, const double* __restrict__ diag_num,
-    double diag_mul) {
+    double diag_mul, int nblk) {
   using F = Fwht<LOG_N>;
   __shared__ double lds[F::LDS];
   const int64_t row = blockIdx.x;
@@ -310,13 +320,15 @@ __global__ __launch_bounds__(Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR) void
   __syncthreads();
   F::run(v, lds, u, active);
   const double dadd = diag_num ? *diag_num * diag_mul : 0.0;
+  const int64_t mrow = row / nblk;                         // matrix row
+  const int64_t mcol0 = (row - mrow * nblk) * F::N;        // first matrix column
   if (active) {
     double* dst = out + row * F::N;
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) {
       const int j = F::out_index(u, r);
       double o = v[r] * scale;
-      if (j == row) o += dadd;
+      if (mcol0 + j == mrow) o += dadd;
       dst[j] = o;
     }
   }
@@ -679,19 +691,34 @@ CalWs cal_ws(int d_out, int d_in) {
 
 template <int L>
 hipError_t fwht64_t(const double* in, double* out, int64_t rows, double scale,
-                    const double* diag_num, double diag_mul, hipStream_t s) {
+                    const double* diag_num, double diag_mul, int nblk, hipStream_t s) {
   hipLaunchKernelGGL(fwht64_rows_kernel<L>, dim3(static_cast<unsigned>(rows)),
                      dim3(Fwht<L>::TPR < 64 ? 64 : Fwht<L>::TPR), 0, s, in, out, scale, diag_num,
-                     diag_mul);
+                     diag_mul, nblk);
   return hipGetLastError();
 }
 
 template <int L>
 hipError_t calib_rows_t(const double* M, const float* dWq, const double* delta, double* Q,
-                        double* w, int d_out, hipStream_t s) {
-  hipLaunchKernelGGL(calib_rows_kernel<L>, dim3(d_out), dim3(Fwht<L>::TPR < 64 ? 64 : Fwht<L>::TPR),
-                     0, s, M, dWq, delta, Q, w);
-  return hipGetLastError();
+                        double* w, int d_out, int nblk, hipStream_t s) {
+  using F = Fwht<L>;
+  if (nblk == 1) {
+    hipLaunchKernelGGL((calib_rows_kernel<L, false>), dim3(d_out),
+                       dim3(F::TPR < 64 ? 64 : F::TPR), 0, s, M, dWq, delta, Q, w, 1);
+    return hipGetLastError();
+  }
+  if constexpr (L >= 6 && L <= 12) {
+    const int threads = nblk * F::TPR < 64 ? 64 : nblk * F::TPR;
+    const size_t lds = static_cast<size_t>(nblk) * F::LDS * sizeof(double);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&calib_rows_kernel<L, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((calib_rows_kernel<L, true>), dim3(d_out), dim3(threads), lds, s, M, dWq,
+                       delta, Q, w, nblk);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -711,8 +738,9 @@ hipError_t launch_hessian(const void* X, Dt x_dt, int64_t N, int d_in, double* H
 size_t calibrated_scratch_bytes(int d_out, int d_in) { return cal_ws(d_out, d_in).total; }
 
 hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const double* Hs,
-                                double damp, void* scratch, double** w_out, hipStream_t s) {
-  const int d_in = 1 << log_n;
+                                double damp, void* scratch, double** w_out, hipStream_t s,
+                                int nblk) {
+  const int d_in = nblk << log_n;
   const CalWs l = cal_ws(d_out, d_in);
   char* base = static_cast<char*>(scratch);
   double* delta = reinterpret_cast<double*>(base + l.delta);
@@ -724,7 +752,7 @@ hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const do
   if (e != hipSuccess) return e;
   switch (log_n) {
 #define QWHA_CASE(L) \
-  case L: e = calib_rows_t<L>(Q, dWq, delta, Q, w, d_out, s); break;
+  case L: e = calib_rows_t<L>(Q, dWq, delta, Q, w, d_out, nblk, s); break;
     QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
     QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)
     QWHA_CASE(14)
@@ -737,8 +765,8 @@ hipError_t launch_calib_prepare(const float* dWq, int d_out, int log_n, const do
 }
 
 hipError_t launch_calib_finish(const int32_t* E, int64_t p, int d_out, int log_n, const double* Hs,
-                               void* scratch, double* G, double* rhs, hipStream_t s) {
-  const int d_in = 1 << log_n;
+                               void* scratch, double* G, double* rhs, hipStream_t s, int nblk) {
+  const int d_in = nblk << log_n;
   const CalWs l = cal_ws(d_out, d_in);
   char* base = static_cast<char*>(scratch);
   const double* delta = reinterpret_cast<const double*>(base + l.delta);
@@ -747,16 +775,18 @@ hipError_t launch_calib_finish(const int32_t* E, int64_t p, int d_out, int log_n
   if (p > 0)
     hipLaunchKernelGGL(rhs_gather_kernel, dim3(static_cast<unsigned>((p + 255) / 256)), dim3(256),
                        0, s, Q, d_in, E, p, rhs);
-  const double inv_n2 = 1.0 / (static_cast<double>(d_in) * d_in);
+  const double b = static_cast<double>(1 << log_n);
+  const double inv_b2 = 1.0 / (b * b);
+  const int64_t vrows = static_cast<int64_t>(d_in) * nblk;   // [d_in * nblk][b] views
   hipError_t e = hipSuccess;
   switch (log_n) {
 #define QWHA_CASE(L)                                                                     \
   case L:                                                                                \
-    e = fwht64_t<L>(Hs, G, d_in, 1.0, nullptr, 0.0, s);                                  \
+    e = fwht64_t<L>(Hs, G, vrows, 1.0, nullptr, 0.0, nblk, s);                         \
     if (e != hipSuccess) return e;                                                       \
     hipLaunchKernelGGL(transpose64_kernel, dim3((d_in + 31) / 32, (d_in + 31) / 32),      \
                        dim3(256), 0, s, G, T1, d_in);                                    \
-    e = fwht64_t<L>(T1, G, d_in, inv_n2, delta, 1.0 / d_in, s);                          \
+    e = fwht64_t<L>(T1, G, vrows, inv_b2, delta, 1.0 / b, nblk, s);                      \
     break;
     QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)
     QWHA_CASE(8) QWHA_CASE(9) QWHA_CASE(10) QWHA_CASE(11) QWHA_CASE(12) QWHA_CASE(13)

@@ -60,7 +60,8 @@ size_t global_select_scratch_bytes(int d_out, int d_in, int mode) {
   return gs_layout(d_out, d_in, mode).total;
 }
 
-// |C| keys of one row (fp64 FWHT, natural column order).
+// |C| keys of one row of N columns (fp64 FWHT, natural column order); under
+// the block-diagonal transform a row of nblk blocks is nblk such rows.
 template <int LOG_N>
 __global__ __launch_bounds__(Fwht<LOG_N>::TPR < 64 ? 64 : Fwht<LOG_N>::TPR) void mag_keys_kernel(
     const float* __restrict__ dWq, unsigned long long* __restrict__ keys) {
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(1024) void global_budget_kernel(const int32_t* __re
 
 hipError_t launch_global_budgets(const float* dWq, int d_out, int log_n, int64_t p, int mode,
                                  unsigned long long seed, int32_t* row_ptr, void* scratch,
-                                 const unsigned long long** gtau, hipStream_t s) {
-  const int d_in = 1 << log_n;
+                                 const unsigned long long** gtau, hipStream_t s, int nblk) {
+  const int d_in = nblk << log_n;
   const GsLayout l = gs_layout(d_out, d_in, mode);
   char* base = static_cast<char*>(scratch);
   SelState* st = reinterpret_cast<SelState*>(base + l.state);
@@ -253,7 +254,7 @@ hipError_t launch_global_budgets(const float* dWq, int d_out, int log_n, int64_t
     switch (log_n) {
 #define QWHA_CASE(L)                                                                           \
   case L:                                                                                      \
-    hipLaunchKernelGGL(mag_keys_kernel<L>, dim3(d_out),                                        \
+    hipLaunchKernelGGL(mag_keys_kernel<L>, dim3(d_out * nblk),                                 \
                        dim3(Fwht<L>::TPR < 64 ? 64 : Fwht<L>::TPR), 0, s, dWq, keys);           \
     break;
       QWHA_CASE(1) QWHA_CASE(2) QWHA_CASE(3) QWHA_CASE(4) QWHA_CASE(5) QWHA_CASE(6) QWHA_CASE(7)

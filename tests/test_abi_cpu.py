@@ -233,6 +233,18 @@ def test_quantized_base_validation(q):
     assert fwd(T=0, x=None, y=None) == OK        # nothing to do
 
 
+def test_block_widths_pass_shape_validation(q):
+    # widths m * b with b >= 64 reach the workspace check; narrower blocks do not
+    for d_in, ok in ((14336, True), (192, True), (11008, True), (96, False), (100, False),
+                     (20480, False)):
+        r = _fwd(q, d_in=d_in, p=2048)
+        assert r == (WORKSPACE if ok else SHAPE), (d_in, r)
+        r = q.qwha_init_select(FAKE, 64, d_in, 192, 3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                               None)
+        assert r == (WORKSPACE if ok else SHAPE), (d_in, r)
+    assert q.qwha_fwht(FAKE, 0, FAKE, 0, 4, 192, 1.0, None) == SHAPE   # powers of two only
+
+
 def test_bwd_materialize_fwht_validation(q):
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 24, 8, 1.0, 0, FAKE, 0, None) == SHAPE
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 16, 8, 1.0, 5, FAKE, 0, None) == DTYPE
