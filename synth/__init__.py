@@ -112,6 +112,11 @@ CONFIGS: Dict[str, List[LayerSpec]] = {
         LayerSpec("c5.o", 4096, 4096, 0.001, 20.0, 4, 128,
                   _lora_budget(4096, 4096), 32768, "bf16", seed_key=4),
     ],
+    # Not one of the five measured workloads: the down_proj shape of the same
+    # models, whose input width 14336 = 7 * 2048 is not a power of two
+    # (block-diagonal transform).
+    "down": [LayerSpec("down", 4096, 14336, 0.001, 20.0, 4, 128,
+                       _lora_budget(4096, 14336), 8192, "bf16", seed_key=6)],
 }
 
 # Which activation stream each c5 projection reads: q/k/v share one.

@@ -129,8 +129,7 @@ def test_quantized_layer_block_widths(q, T, d_out, d_in, bits, group, p):
 def test_full_down_proj_layer(q):
     # the down_proj shape of the same models: 4096 x 14336 (7 blocks of 2048),
     # budget P(r=64), 8192 bf16 tokens; init bit-exact, sampled fwd / bwd
-    spec = synth.LayerSpec("down", 4096, 14336, 0.001, 20.0, 4, 128, 64 * (4096 + 14336),
-                           8192, "bf16", seed_key=6)
+    spec = synth.config_specs("down")[0]
     layer = synth.make_layer(spec, seed=0)
     x, dy = synth.make_activations(spec, seed=0)
     say("full down_proj layer")
