@@ -3,8 +3,9 @@
 One step = one pass of the whole hot path over one batch, every kernel in
 the library's HIP code, on torch's current stream:
   init (row norms, AdaAlloc budgets, fp64 transform + in-row top-k, column
-  index) -> materialize dW -> forward (FWHT(x), gather-SpMM) -> backward
-  (gather-SpMM dz and dc partials, FWHT(dz) -> dx, dc reduction) ->
+  index) -> materialize dW -> forward (FWHT(x), gather-SpMM; z = FWHT(x)/n
+  kept as the saved activation) -> backward (gather-SpMM dz and dc partials
+  against the saved z, FWHT(dz) -> dx, dc reduction) ->
   c += 1e-3 sign(dc) -> re-materialize dW.
 value = tokens per second of that step (T / step time), inputs resident in HBM.
 
@@ -31,7 +32,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X vector fp32 (packed FMA)
 
-K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_FWHT_X=3, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC_REDUCE=6,
+# timed kernels of the step (the backward takes the forward's z, so the
+# library's BWD_FWHT_X transform does not run)
+K = dict(FWD_FWHT=1, FWD_SPMM=2, BWD_SPMM=4, BWD_FWHT_DX=5, BWD_DC_REDUCE=6,
          INIT_SELECT=7, MATERIALIZE=8)
 GLOBAL_THRESHOLD = 10
 KR = dict(HESSIAN=11, CALIB_PREPARE=12, CALIB_SYSTEM=13, REFINE=14)
@@ -139,6 +142,7 @@ def main():
     y = torch.empty((T, d_out), dtype=adt, device=dev)
     dx = torch.empty((T, d_in), dtype=adt, device=dev)
     dc = torch.empty(p, dtype=torch.float32, device=dev)
+    zsave = torch.empty((T, d_in), dtype=torch.float32, device=dev)   # saved activation
     ws_i = torch.empty(lib.qwha_init_workspace_bytes(d_out, d_in), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
                        device=dev)
@@ -161,13 +165,13 @@ def main():
               "init")
         check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
                                    p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "materialize")
-        check(lib.qwha_fwd(x.data_ptr(), act, T, d_in, d_out, p, row_ptr.data_ptr(),
-                           E.data_ptr(), c.data_ptr(), 1.0, y.data_ptr(), 0, ws_f.data_ptr(),
-                           ws_f.numel(), stream), "fwd")
-        check(lib.qwha_bwd(x.data_ptr(), dy.data_ptr(), act, T, d_in, d_out, p,
-                           row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), col_ptr.data_ptr(),
-                           perm.data_ptr(), 1.0, dx.data_ptr(), 0, dc.data_ptr(),
-                           ws_b.data_ptr(), ws_b.numel(), stream), "bwd")
+        check(lib.qwha_fwd_save(x.data_ptr(), act, T, d_in, d_out, p, row_ptr.data_ptr(),
+                                E.data_ptr(), c.data_ptr(), 1.0, y.data_ptr(), 0,
+                                zsave.data_ptr(), ws_f.data_ptr(), ws_f.numel(), stream), "fwd")
+        check(lib.qwha_bwd_saved(zsave.data_ptr(), dy.data_ptr(), act, T, d_in, d_out, p,
+                                 row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(),
+                                 col_ptr.data_ptr(), perm.data_ptr(), 1.0, dx.data_ptr(), 0,
+                                 dc.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream), "bwd")
         check(lib.qwha_sign_update(c.data_ptr(), dc.data_ptr(), p, 1e-3, stream), "update")
         check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
                                    p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "rematerialize")
@@ -210,7 +214,6 @@ def main():
     # algorithmic work per launch
     nbytes = {
         "FWD_FWHT": T * d_in * (esz + 4),
-        "BWD_FWHT_X": T * d_in * (esz + 4),
         "BWD_FWHT_DX": T * d_in * (4 + esz),
         "INIT_SELECT": d_out * d_in * 4 + p * 12 + (d_out + 1) * 4,
         "MATERIALIZE": p * 12 + (d_out + 1) * 4 + d_out * d_in * 4,
@@ -237,8 +240,8 @@ def main():
     roof["avg_us"] = round(avg_us[dom], 2)
     roof["traffic"] = measured_traffic(dom, args.config)
 
-    fwd_bwd_us = sum(avg_us[k] for k in ("FWD_FWHT", "FWD_SPMM", "BWD_FWHT_X", "BWD_SPMM",
-                                         "BWD_FWHT_DX", "BWD_DC_REDUCE"))
+    fwd_bwd_us = sum(avg_us[k] for k in ("FWD_FWHT", "FWD_SPMM", "BWD_SPMM", "BWD_FWHT_DX",
+                                         "BWD_DC_REDUCE"))
     out = {
         "metric": "adapter fwd+bwd tokens/s per layer; FWHT/gather achieved HBM GB/s vs peak",
         "value": round(value, 1),

@@ -82,8 +82,8 @@ def kernel_ids(name: str):
         # the AdaAlloc instance (selection mode 0) is the one of the step
         return ["INIT_SELECT"] if template_args(n)[1] == "0" else ["INIT_SELECT_GLOBAL"]
     if n.startswith("fwht_rows_kernel<"):
-        # FWHT(x) -> fp32 z in forward and backward; FWHT(dz) -> activations
-        return ["FWD_FWHT", "BWD_FWHT_X"] if template_args(n)[2] == "float" else ["BWD_FWHT_DX"]
+        # FWHT(x) -> fp32 z (the forward's, kept for the backward); FWHT(dz) -> activations
+        return ["FWD_FWHT"] if template_args(n)[2] == "float" else ["BWD_FWHT_DX"]
     for key, kids in KERNEL_IDS.items():
         if n.startswith(key):
             return kids

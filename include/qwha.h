@@ -151,6 +151,25 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
                      size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The same forward and backward with the forward's transform kept, as
+ * autograd keeps a saved activation: qwha_fwd_save also writes
+ * z = FWHT(x)/d_in to z (fp32 [T][d_in], caller-owned, 16-byte aligned),
+ * and qwha_bwd_saved takes that z in place of x (dc uses it; x is neither
+ * read nor transformed again). Workspaces as qwha_fwd / qwha_bwd. z must
+ * hold the transform of the x the forward saw.
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_fwd_save(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                          int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                          const float* c, float alpha, void* y, int32_t accumulate, float* z,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+qwha_status qwha_bwd_saved(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                           int32_t d_in, int32_t d_out, int64_t p, const int32_t* row_ptr,
+                           const int32_t* E, const float* c, const int32_t* col_ptr,
+                           const int32_t* csc_perm, float alpha, void* dx,
+                           int32_t accumulate_dx, float* dc, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Coefficient update of the attention-block training step:
  *   c[k] += step * sign(dc[k])   (sign(0) = 0), fp32, in place.
  * --------------------------------------------------------------------------- */
@@ -289,7 +308,7 @@ typedef enum qwha_kernel {
   QWHA_KERNEL_NONE = 0,
   QWHA_KERNEL_FWD_FWHT = 1,     /* z = FWHT(x)/n inside qwha_fwd */
   QWHA_KERNEL_FWD_SPMM = 2,     /* y = alpha z F^T inside qwha_fwd */
-  QWHA_KERNEL_BWD_FWHT_X = 3,   /* z recomputed inside qwha_bwd */
+  QWHA_KERNEL_BWD_FWHT_X = 3,   /* z recomputed inside qwha_bwd (not qwha_bwd_saved) */
   QWHA_KERNEL_BWD_SPMM = 4,     /* dz = dy F and the dc partials inside qwha_bwd */
   QWHA_KERNEL_BWD_FWHT_DX = 5,  /* dx = alpha FWHT(dz)/n inside qwha_bwd */
   QWHA_KERNEL_BWD_DC_REDUCE = 6,

@@ -218,7 +218,10 @@ def qwha_materialize(row_ptr, E, c, d_out: int, d_in: int, alpha: float = 1.0,
 # ---------------------------------------------------------------- forward
 def qwha_fwd(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
              y: Optional[torch.Tensor] = None, accumulate: bool = False,
-             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+             ws: Optional[torch.Tensor] = None,
+             z_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = alpha z F^T; with z_out (fp32 [T][d_in]) z = FWHT(x)/n is kept
+    there for qwha_bwd(..., z=z_out)."""
     T, d_in = x.shape
     p = int(c.numel())
     if y is None:
@@ -226,6 +229,12 @@ def qwha_fwd(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
     need = lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p)
     if ws is None:
         ws = workspace(need, x.device)
+    if z_out is not None:
+        check(lib.qwha_fwd_save(_ptr(x), _dt(x), T, d_in, d_out, p, _ptr(row_ptr),
+                                E.data_ptr(), c.data_ptr(), float(alpha), _ptr(y),
+                                int(accumulate), _ptr(z_out), ws.data_ptr(), ws.numel(),
+                                _stream()), "qwha_fwd_save")
+        return y
     check(lib.qwha_fwd(_ptr(x), _dt(x), T, d_in, d_out, p, _ptr(row_ptr), E.data_ptr(),
                        c.data_ptr(), float(alpha), _ptr(y), int(accumulate), ws.data_ptr(),
                        ws.numel(), _stream()), "qwha_fwd")
@@ -233,24 +242,33 @@ def qwha_fwd(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
 
 
 # ---------------------------------------------------------------- backward
-def qwha_bwd(x: torch.Tensor, dy: torch.Tensor, row_ptr, E, c, col_ptr, csc_perm,
+def qwha_bwd(x: Optional[torch.Tensor], dy: torch.Tensor, row_ptr, E, c, col_ptr, csc_perm,
              alpha: float = 1.0, need_dx: bool = True, need_dc: bool = True,
              dx: Optional[torch.Tensor] = None, accumulate_dx: bool = False,
-             dc: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
-    T, d_in = x.shape
+             dc: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+             z: Optional[torch.Tensor] = None):
+    """dx and dc; with z (the forward's z_out) x is not needed (may be None)."""
+    T, d_in = (z if z is not None else x).shape
     d_out = dy.shape[1]
     p = int(c.numel())
     if need_dx and dx is None:
-        dx = torch.empty((T, d_in), dtype=x.dtype, device=x.device)
+        dx = torch.empty((T, d_in), dtype=dy.dtype, device=dy.device)
     if need_dc and dc is None:
-        dc = torch.empty(max(p, 1), dtype=torch.float32, device=x.device)[:p]
+        dc = torch.empty(max(p, 1), dtype=torch.float32, device=dy.device)[:p]
     if not need_dx:
         dx = None
     if not need_dc:
         dc = None
     need = lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p)
     if ws is None:
-        ws = workspace(need, x.device)
+        ws = workspace(need, dy.device)
+    if z is not None:
+        check(lib.qwha_bwd_saved(_ptr(z), _ptr(dy), _dt(dy), T, d_in, d_out, p, _ptr(row_ptr),
+                                 E.data_ptr(), c.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(),
+                                 float(alpha), _ptr(dx), int(accumulate_dx),
+                                 dc.data_ptr() if dc is not None else None,
+                                 ws.data_ptr(), ws.numel(), _stream()), "qwha_bwd_saved")
+        return dx, dc
     check(lib.qwha_bwd(_ptr(x), _ptr(dy), _dt(dy), T, d_in, d_out, p, _ptr(row_ptr),
                        E.data_ptr(), c.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(),
                        float(alpha), _ptr(dx), int(accumulate_dx),
@@ -280,17 +298,31 @@ def qwha_fwht(x: torch.Tensor, scale: float = 1.0, out_dtype=None,
 # ---------------------------------------------------------------- autograd
 class WHAFunction(torch.autograd.Function):
     """y = x dW^T for the adapter branch; gradients flow to x and c only
-    (W_Q and H frozen: papernotes.org, 损失函数 / 训练策略)."""
+    (W_Q and H frozen: papernotes.org, 损失函数 / 训练策略). When c needs a
+    gradient the forward keeps z = FWHT(x)/n (fp32) for the backward's dc,
+    as a saved activation, instead of transforming x again."""
 
     @staticmethod
     def forward(ctx, x, c, row_ptr, E, col_ptr, csc_perm, d_out, alpha):
-        ctx.save_for_backward(x, c, row_ptr, E, col_ptr, csc_perm)
+        x = x.contiguous()
         ctx.alpha = alpha
-        return qwha_fwd(x.contiguous(), d_out, row_ptr, E, c, alpha)
+        ctx.saved_z = bool(ctx.needs_input_grad[1])
+        if ctx.saved_z:
+            z = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+            y = qwha_fwd(x, d_out, row_ptr, E, c, alpha, z_out=z)
+            ctx.save_for_backward(z, c, row_ptr, E, col_ptr, csc_perm)
+            return y
+        ctx.save_for_backward(x, c, row_ptr, E, col_ptr, csc_perm)
+        return qwha_fwd(x, d_out, row_ptr, E, c, alpha)
 
     @staticmethod
     def backward(ctx, dy):
-        x, c, row_ptr, E, col_ptr, csc_perm = ctx.saved_tensors
-        dx, dc = qwha_bwd(x, dy.contiguous(), row_ptr, E, c, col_ptr, csc_perm, ctx.alpha,
-                          need_dx=ctx.needs_input_grad[0], need_dc=ctx.needs_input_grad[1])
-        return dx, dc, None, None, None, None, None, None
+        saved, c, row_ptr, E, col_ptr, csc_perm = ctx.saved_tensors
+        dy = dy.contiguous()
+        if ctx.saved_z:
+            dx, dc = qwha_bwd(None, dy, row_ptr, E, c, col_ptr, csc_perm, ctx.alpha,
+                              need_dx=ctx.needs_input_grad[0], need_dc=True, z=saved)
+            return dx, dc, None, None, None, None, None, None
+        dx, _ = qwha_bwd(saved, dy, row_ptr, E, c, col_ptr, csc_perm, ctx.alpha,
+                         need_dx=ctx.needs_input_grad[0], need_dc=False)
+        return dx, None, None, None, None, None, None, None

@@ -58,6 +58,13 @@ SIGNATURES = {
     "qwha_fwd": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
                            c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
                            c_void_p, c_size_t, c_void_p]),
+    "qwha_fwd_save": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
+                                c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
+                                c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qwha_bwd_saved": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32,
+                                 c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]),
     "qwha_bwd_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),
     "qwha_bwd": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float,

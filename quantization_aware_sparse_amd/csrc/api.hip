@@ -546,9 +546,15 @@ size_t qwha_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t 
   return fwd_ws(T, d_in, d_out, p).total;
 }
 
-qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+}  // extern "C"
+
+namespace {
+
+// qwha_fwd; with z_out, z = FWHT(x)/n goes there (kept for the backward)
+// instead of into the workspace.
+qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
                      int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
-                     float alpha, void* y, int32_t accumulate, void* workspace,
+                     float alpha, void* y, int32_t accumulate, float* z_out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
@@ -572,7 +578,8 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
     return fail(QWHA_ERR_WORKSPACE, "fwd workspace needs %zu bytes", l.total);
   QWHA_NEED(workspace, 256);
 
-  float* z = reinterpret_cast<float*>(at(workspace, l.z));
+  if (z_out != nullptr) QWHA_NEED(z_out, 16);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(at(workspace, l.z));
   void* prep = at(workspace, l.prep);
   const Dt adt = static_cast<Dt>(act);
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
@@ -591,6 +598,28 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
   return QWHA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+                     int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
+                     float alpha, void* y, int32_t accumulate, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(x, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, nullptr,
+                  workspace, workspace_bytes, stream);
+}
+
+qwha_status qwha_fwd_save(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                          int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                          const float* c, float alpha, void* y, int32_t accumulate, float* z,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (z == nullptr && T > 0) return fail(QWHA_ERR_INVALID_ARG, "z is NULL");
+  return fwd_impl(x, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, z, workspace,
+                  workspace_bytes, stream);
+}
+
 // ------------------------------------------------------------------ backward
 size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
   if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
@@ -599,11 +628,17 @@ size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t 
   return a > b ? a : b;
 }
 
-qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, int32_t d_in,
-                     int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
-                     const float* c, const int32_t* col_ptr, const int32_t* csc_perm,
-                     float alpha, void* dx, int32_t accumulate_dx, float* dc, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// qwha_bwd; with z_in (the forward's z = FWHT(x)/n), x is not read and z is
+// not recomputed.
+qwha_status bwd_impl(const void* x, const float* z_in, const void* dy, qwha_dtype act,
+                     int64_t T, int32_t d_in, int32_t d_out, int64_t p, const int32_t* row_ptr,
+                     const int32_t* E, const float* c, const int32_t* col_ptr,
+                     const int32_t* csc_perm, float alpha, void* dx, int32_t accumulate_dx,
+                     float* dc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
   int nblk;
@@ -632,21 +667,27 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
     return QWHA_OK;
   }
   QWHA_NEED(dy, 16);
-  if (dc != nullptr) QWHA_NEED(x, 16);
+  if (dc != nullptr) {
+    if (z_in != nullptr)
+      QWHA_NEED(z_in, 16);
+    else
+      QWHA_NEED(x, 16);
+  }
   const BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr);
   if (workspace == nullptr || workspace_bytes < l.total)
     return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", l.total);
   QWHA_NEED(workspace, 256);
 
-  float* z = reinterpret_cast<float*>(at(workspace, l.z));
+  const float* z = z_in ? z_in : reinterpret_cast<float*>(at(workspace, l.z));
   float* dz = reinterpret_cast<float*>(at(workspace, l.dz));
   void* prep = at(workspace, l.prep);
   float* partial = dc ? reinterpret_cast<float*>(at(workspace, l.partial)) : nullptr;
   const Dt adt = static_cast<Dt>(act);
-  if (dc)
+  if (dc && z_in == nullptr)
     QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_X, stream,
                              [&] {
-                               return launch_fwht(x, adt, z, Dt::F32, T * nblk, log_n,
+                               return launch_fwht(x, adt, at(workspace, l.z), Dt::F32,
+                                                  T * nblk, log_n,
                                                   1.0f / static_cast<float>(1 << log_n), 0,
                                                   stream);
                              }),
@@ -677,6 +718,31 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
                              }),
                        "dc reduce"));
   return QWHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, int32_t d_in,
+                     int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                     const float* c, const int32_t* col_ptr, const int32_t* csc_perm,
+                     float alpha, void* dx, int32_t accumulate_dx, float* dc, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(x, nullptr, dy, act, T, d_in, d_out, p, row_ptr, E, c, col_ptr, csc_perm,
+                  alpha, dx, accumulate_dx, dc, workspace, workspace_bytes, stream);
+}
+
+qwha_status qwha_bwd_saved(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                           int32_t d_in, int32_t d_out, int64_t p, const int32_t* row_ptr,
+                           const int32_t* E, const float* c, const int32_t* col_ptr,
+                           const int32_t* csc_perm, float alpha, void* dx,
+                           int32_t accumulate_dx, float* dc, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (z == nullptr && T > 0 && dc != nullptr) return fail(QWHA_ERR_INVALID_ARG, "z is NULL");
+  return bwd_impl(nullptr, z, dy, act, T, d_in, d_out, p, row_ptr, E, c, col_ptr, csc_perm,
+                  alpha, dx, accumulate_dx, dc, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------ update

@@ -245,6 +245,22 @@ def test_block_widths_pass_shape_validation(q):
     assert q.qwha_fwht(FAKE, 0, FAKE, 0, 4, 192, 1.0, None) == SHAPE   # powers of two only
 
 
+def test_saved_activation_validation(q):
+    # qwha_fwd_save: as qwha_fwd plus z; qwha_bwd_saved: z in place of x
+    r = q.qwha_fwd_save(FAKE, 1, 16, 256, 256, 2048, FAKE, FAKE, FAKE, 1.0, FAKE, 0, None,
+                        FAKE, 1 << 30, None)
+    assert r == INVALID
+    r = q.qwha_fwd_save(FAKE, 1, 16, 256, 256, 2048, FAKE, FAKE, FAKE, 1.0, FAKE, 0, FAKE + 4,
+                        FAKE, 1 << 30, None)
+    assert r == ALIGN
+    r = q.qwha_bwd_saved(None, FAKE, 1, 64, 256, 256, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0,
+                         FAKE, 0, FAKE, FAKE, 1 << 30, None)
+    assert r == INVALID                          # dc wanted, no z
+    r = q.qwha_bwd_saved(FAKE + 8, FAKE, 1, 64, 256, 256, 2048, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         1.0, FAKE, 0, FAKE, FAKE, 1 << 30, None)
+    assert r == ALIGN
+
+
 def test_bwd_materialize_fwht_validation(q):
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 24, 8, 1.0, 0, FAKE, 0, None) == SHAPE
     assert q.qwha_materialize(FAKE, FAKE, FAKE, 4, 16, 8, 1.0, 5, FAKE, 0, None) == DTYPE

@@ -321,6 +321,30 @@ def test_fwd_bwd_small(q, d_out, d_in, p, T, act):
     assert O.rel_err(to_np(dc), dc_ref) <= tol(act)
 
 
+@pytest.mark.parametrize("d_out,d_in,p,T,act", [(300, 64, 2500, 77, "f32"),
+                                                 (513, 128, 4000, 129, "bf16"),
+                                                 (37, 192, 600, 33, "bf16")])
+def test_saved_activation_path_matches(q, d_out, d_in, p, T, act):
+    # qwha_fwd_save / qwha_bwd_saved: the same kernels on the kept z, so the
+    # outputs equal the plain calls bit for bit; z is the forward transform
+    say("saved activation", d_out, d_in, p, T, act)
+    r, x, dy = _small_case(d_out, d_in, p, T, act, d_out + T)
+    a = _dev_adapter(r)
+    xt, dyt = to_dev(x), to_dev(dy)
+    y0 = q.qwha_fwd(xt, d_out, a["row_ptr"], a["E"], a["c"], 0.9)
+    dx0, dc0 = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"],
+                          0.9)
+    z = torch.empty((T, d_in), dtype=torch.float32, device=DEV)
+    y1 = q.qwha_fwd(xt, d_out, a["row_ptr"], a["E"], a["c"], 0.9, z_out=z)
+    dx1, dc1 = q.qwha_bwd(None, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"],
+                          0.9, z=z)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(dx0, dx1) and torch.equal(dc0, dc1)
+    b = O.block_size(d_in)
+    z_ref = O.wht(synth.act_to_f64(x), d_in) / b
+    assert O.rel_err(to_np(z), z_ref) <= 1e-6
+
+
 def test_fwd_bwd_accumulate_and_partial_outputs(q):
     say("accumulate")
     r, x, dy = _small_case(300, 64, 2500, 77, "f32", 3)
