@@ -191,7 +191,15 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
   }
   __syncthreads();
 
-  // leftover
+  // leftover. Thread tid owns the contiguous rows [tid * rpt, (tid+1) * rpt)
+  // and the budget values [tid * vpt, (tid+1) * vpt), so that one block scan
+  // orders a pass (row order and value order are thread order).
+  const int rpt = (d_out + kAllocThreads - 1) / kAllocThreads;
+  const int vpt = (d_in + 1 + kAllocThreads - 1) / kAllocThreads;
+  const int r0 = tid * rpt, r1 = min(r0 + rpt, d_out);
+  const int v0 = tid * vpt, v1 = min(v0 + vpt, d_in + 1);
+  __shared__ int vstar;
+  __shared__ int below_star;
   for (;;) {
     long long tot = 0;
     for (int i = tid; i < d_out; i += kAllocThreads) tot += budget[i];
@@ -199,33 +207,30 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
     for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
     if (lane == 0) red_l[parity][wid] = tot;
     for (int v = tid; v <= d_in; v += kAllocThreads) hist[v] = 0;
+    if (tid == 0) vstar = -1;
     __syncthreads();
     long long TOT = 0;
     for (int i = 0; i < NW; ++i) TOT += red_l[parity][i];
     parity ^= 1;
-    long long r = p - TOT;
+    const long long r = p - TOT;
     if (r <= 0) break;
     for (int i = tid; i < d_out; i += kAllocThreads)
       if (budget[i] < d_in) atomicAdd(&hist[budget[i]], 1);
     __syncthreads();
-    // inclusive scan of hist over values 0..d_in (chunks of 1024, carried)
-    __shared__ long long carry;
-    __shared__ int vstar;
-    __shared__ long long below_star;
-    if (tid == 0) { carry = 0; vstar = -1; below_star = 0; }
-    __syncthreads();
-    for (int base = 0; base <= d_in; base += kAllocThreads) {
-      const int v = base + tid;
-      const int h = (v <= d_in) ? hist[v] : 0;
-      int tot_chunk;
-      const int ex = block_excl_scan_i32(h, scan_tmp, &tot_chunk);
-      const long long before = carry + ex;       // eligible rows with budget < v
-      const long long incl = before + h;
-      if (v <= d_in && h > 0 && before < r && incl >= r) { vstar = v; below_star = before; }
-      __syncthreads();
-      if (tid == 0) carry += tot_chunk;
-      __syncthreads();
+    // v* = the budget value at which the eligible rows, counted from the
+    // smallest budget up, reach r: before(v*) < r <= before(v*) + hist[v*]
+    {
+      int h = 0;
+      for (int v = v0; v < v1; ++v) h += hist[v];
+      int all_h;
+      int before = block_excl_scan_i32(h, scan_tmp, &all_h);
+      for (int v = v0; v < v1; ++v) {
+        const int hv = hist[v];
+        if (hv > 0 && before < r && before + hv >= r) { vstar = v; below_star = before; }
+        before += hv;
+      }
     }
+    __syncthreads();
     const int vs = vstar;
     if (vs < 0) {
       // fewer eligible rows than the leftover: every eligible row gets one
@@ -235,42 +240,36 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
       continue;
     }
     const long long need = r - below_star;       // rows at vs that get a unit
-    // rank rows with budget == vs by index (chunks, carried)
-    __shared__ long long rcarry;
-    if (tid == 0) rcarry = 0;
-    __syncthreads();
-    for (int base = 0; base < d_out; base += kAllocThreads) {
-      const int i = base + tid;
-      const long long b = (i < d_out) ? budget[i] : -1;
-      const int eq = (b == vs) ? 1 : 0;
-      int tot_chunk;
-      const int ex = block_excl_scan_i32(eq, scan_tmp, &tot_chunk);
-      if (i < d_out) {
-        if (b < vs) budget[i] = b + 1;
-        else if (eq && rcarry + ex < need) budget[i] = b + 1;
+    // rows below vs get one; rows at vs get one in row order while need lasts
+    int eq = 0;
+    for (int i = r0; i < r1; ++i) eq += budget[i] == vs ? 1 : 0;
+    int all_eq;
+    int rank = block_excl_scan_i32(eq, scan_tmp, &all_eq);
+    for (int i = r0; i < r1; ++i) {
+      const long long bi = budget[i];
+      if (bi < vs) {
+        budget[i] = bi + 1;
+      } else if (bi == vs) {
+        if (rank < need) budget[i] = bi + 1;
+        ++rank;
       }
-      __syncthreads();
-      if (tid == 0) rcarry += tot_chunk;
-      __syncthreads();
     }
+    __syncthreads();
   }
   __syncthreads();
 
   // row_ptr = exclusive scan of budgets
-  __shared__ long long pcarry;
-  if (tid == 0) pcarry = 0;
-  __syncthreads();
-  for (int base = 0; base < d_out; base += kAllocThreads) {
-    const int i = base + tid;
-    const int b = (i < d_out) ? static_cast<int>(budget[i]) : 0;
-    int tot_chunk;
-    const int ex = block_excl_scan_i32(b, scan_tmp, &tot_chunk);
-    if (i < d_out) row_ptr[i] = static_cast<int32_t>(pcarry + ex);
-    __syncthreads();
-    if (tid == 0) pcarry += tot_chunk;
-    __syncthreads();
+  {
+    int sum = 0;
+    for (int i = r0; i < r1; ++i) sum += static_cast<int>(budget[i]);
+    int total;
+    int pos = block_excl_scan_i32(sum, scan_tmp, &total);
+    for (int i = r0; i < r1; ++i) {
+      row_ptr[i] = pos;
+      pos += static_cast<int>(budget[i]);
+    }
+    if (tid == 0) row_ptr[d_out] = total;
   }
-  if (tid == 0) row_ptr[d_out] = static_cast<int32_t>(pcarry);
 }
 
 hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int m, double t,
