@@ -549,45 +549,63 @@ __global__ __launch_bounds__(kCscThreads) void csc_hist_kernel(const int32_t* __
     hist[static_cast<int64_t>(ch) * d_in + j] = h[j];
 }
 
-// Per column j (one thread each): hist[ch][j] -> number of entries of column
-// j in chunks before ch; the column's total goes to cnt[j]. Chunks go in
-// batches of 16 whose loads are all issued before the running sum.
-__global__ __launch_bounds__(256) void csc_colsum_kernel(int32_t* __restrict__ hist, int d_in,
-                                                         int nchunks, int32_t* __restrict__ cnt) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= d_in) return;
-  int run = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += 16) {
-    int hv[16];
+// hist[ch][j] -> number of entries of column j in chunks before ch; the
+// column's total goes to cnt[j]. A workgroup takes 16 columns; thread
+// (g, jj) sums chunks g*cpg .. g*cpg + cpg - 1 of column j0 + jj (all loads
+// issued before the sum), the 16 group sums are scanned in LDS, and each
+// thread then writes its chunks' running counts.
+constexpr int kColsumCols = 16;
+constexpr int kColsumGroups = 16;
+
+__global__ __launch_bounds__(kColsumCols * kColsumGroups) void csc_colsum_kernel(
+    int32_t* __restrict__ hist, int d_in, int nchunks, int32_t* __restrict__ cnt) {
+  __shared__ int gsum[kColsumGroups][kColsumCols];
+  const int jj = threadIdx.x % kColsumCols;
+  const int g = threadIdx.x / kColsumCols;
+  const int j = blockIdx.x * kColsumCols + jj;
+  const int cpg = (nchunks + kColsumGroups - 1) / kColsumGroups;   // <= 16
+  const int c0 = g * cpg;
+  int hv[16];
+  int mine = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      hv[u] = c0 + u < nchunks ? hist[static_cast<int64_t>(c0 + u) * d_in + j] : 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (c0 + u < nchunks) hist[static_cast<int64_t>(c0 + u) * d_in + j] = run;
-      run += hv[u];
-    }
+  for (int u = 0; u < 16; ++u) {
+    hv[u] = (u < cpg && c0 + u < nchunks && j < d_in)
+                ? hist[static_cast<int64_t>(c0 + u) * d_in + j] : 0;
+    mine += hv[u];
   }
-  cnt[j] = run;
+  gsum[g][jj] = mine;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int q = 0; q < kColsumGroups; ++q) {
+    const int v = gsum[q][jj];
+    if (q < g) run += v;
+    total += v;
+  }
+  if (j >= d_in) return;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (u < cpg && c0 + u < nchunks) hist[static_cast<int64_t>(c0 + u) * d_in + j] = run;
+    run += hv[u];
+  }
+  if (g == 0) cnt[j] = total;
 }
 
 // col_ptr = exclusive scan of the column counts (cnt may alias col_ptr).
+// Thread t owns the contiguous columns [t * cpt, (t+1) * cpt): one block scan.
 __global__ __launch_bounds__(1024) void csc_scan_kernel(int32_t* __restrict__ col_ptr, int d_in) {
   __shared__ int scan_tmp[16];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < d_in; base += 1024) {
-    const int j = base + threadIdx.x;
-    const int c = (j < d_in) ? col_ptr[j] : 0;
-    int tot;
-    const int ex = block_excl_scan_i32(c, scan_tmp, &tot);
-    if (j < d_in) col_ptr[j] = carry + ex;
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
+  const int cpt = (d_in + 1023) / 1024;
+  const int j0 = threadIdx.x * cpt, j1 = min(j0 + cpt, d_in);
+  int sum = 0;
+  for (int j = j0; j < j1; ++j) sum += col_ptr[j];
+  int total;
+  int pos = block_excl_scan_i32(sum, scan_tmp, &total);
+  for (int j = j0; j < j1; ++j) {
+    const int c = col_ptr[j];
+    col_ptr[j] = pos;
+    pos += c;
   }
-  if (threadIdx.x == 0) col_ptr[d_in] = carry;
+  if (threadIdx.x == 0) col_ptr[d_in] = total;
 }
 
 __global__ __launch_bounds__(kCscThreads) void csc_place_kernel(const int32_t* __restrict__ row_ptr,
@@ -620,8 +638,8 @@ hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out,
   const size_t sh = static_cast<size_t>(d_in) * 4;
   hipLaunchKernelGGL(csc_hist_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
                      d_in, nchunks, hist);
-  hipLaunchKernelGGL(csc_colsum_kernel, dim3((d_in + 255) / 256), dim3(256), 0, s, hist, d_in,
-                     nchunks, col_ptr);
+  hipLaunchKernelGGL(csc_colsum_kernel, dim3((d_in + kColsumCols - 1) / kColsumCols),
+                     dim3(kColsumCols * kColsumGroups), 0, s, hist, d_in, nchunks, col_ptr);
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, col_ptr, d_in);
   hipLaunchKernelGGL(csc_place_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
                      d_in, nchunks, col_ptr, hist, csc_perm);
