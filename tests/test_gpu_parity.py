@@ -105,7 +105,10 @@ def _edge_dwq(d_out, d_in, seed):
 @pytest.mark.parametrize("d_out,d_in,p,m", [
     (37, 2, 40, 1), (5, 4, 12, 2), (64, 16, 300, 3), (300, 64, 2500, 3),
     (129, 128, 9000, 3), (17, 1024, 2000, 3), (3, 8192, 900, 3), (2, 16384, 1000, 3),
-    (64, 256, 64 * 256, 3), (50, 512, 150, 3)])
+    (64, 256, 64 * 256, 3), (50, 512, 150, 3),
+    # more rows than the allocator's threads: several rows (and budget
+    # values) per thread, the last threads with none
+    (1025, 128, 20000, 3), (2500, 64, 30000, 3), (4100, 32, 50000, 3)])
 def test_init_select_edges(q, d_out, d_in, p, m):
     say("init edge", d_out, d_in, p, m)
     dwq = _edge_dwq(d_out, d_in, d_out + d_in)
