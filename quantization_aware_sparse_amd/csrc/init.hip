@@ -631,6 +631,38 @@ __global__ __launch_bounds__(kCscThreads) void csc_place_kernel(const int32_t* _
   }
 }
 
+// The same placement with every row of the chunk at once, for chunks of at
+// most 64 rows: bit r of mask[j] marks that row r0 + r holds column j (a
+// row's columns are distinct), so an entry's rank among its column's entries
+// in earlier rows of the chunk is a popcount, whatever the order the bits
+// were set in.
+constexpr int kCscMaskRows = 64;
+
+__global__ __launch_bounds__(kCscThreads) void csc_place_mask_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ E, int d_out, int d_in,
+    int nchunks, const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ before,
+    int32_t* __restrict__ perm) {
+  extern __shared__ unsigned long long mask[];
+  const int ch = blockIdx.x;
+  const int r0 = static_cast<int>(static_cast<int64_t>(d_out) * ch / nchunks);
+  const int r1 = static_cast<int>(static_cast<int64_t>(d_out) * (ch + 1) / nchunks);
+  for (int j = threadIdx.x; j < d_in; j += kCscThreads) mask[j] = 0;
+  __syncthreads();
+  const int k0 = row_ptr[r0], k1 = row_ptr[r1];
+  for (int k = k0 + threadIdx.x; k < k1; k += kCscThreads) {
+    const int r = E[2 * static_cast<int64_t>(k)] - r0;
+    const int j = E[2 * static_cast<int64_t>(k) + 1];
+    atomicOr(&mask[j], 1ull << r);
+  }
+  __syncthreads();
+  for (int k = k0 + threadIdx.x; k < k1; k += kCscThreads) {
+    const int r = E[2 * static_cast<int64_t>(k)] - r0;
+    const int j = E[2 * static_cast<int64_t>(k) + 1];
+    const int rank = __popcll(mask[j] & ((1ull << r) - 1ull));
+    perm[col_ptr[j] + before[static_cast<int64_t>(ch) * d_in + j] + rank] = k;
+  }
+}
+
 hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out, int d_in,
                             int32_t* col_ptr, int32_t* csc_perm, void* scratch, hipStream_t s) {
   const int nchunks = csc_chunks(d_out);
@@ -641,8 +673,20 @@ hipError_t launch_csc_build(const int32_t* row_ptr, const int32_t* E, int d_out,
   hipLaunchKernelGGL(csc_colsum_kernel, dim3((d_in + kColsumCols - 1) / kColsumCols),
                      dim3(kColsumCols * kColsumGroups), 0, s, hist, d_in, nchunks, col_ptr);
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, s, col_ptr, d_in);
-  hipLaunchKernelGGL(csc_place_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E, d_out,
-                     d_in, nchunks, col_ptr, hist, csc_perm);
+  // rows per chunk <= 64 and the masks fit in LDS: all rows of a chunk at once
+  const int rows_per_chunk = (d_out + nchunks - 1) / nchunks;
+  const size_t shm = static_cast<size_t>(d_in) * 8;
+  if (rows_per_chunk <= kCscMaskRows && shm <= 160 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(csc_place_mask_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(shm));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(csc_place_mask_kernel, dim3(nchunks), dim3(kCscThreads), shm, s, row_ptr,
+                       E, d_out, d_in, nchunks, col_ptr, hist, csc_perm);
+  } else {
+    hipLaunchKernelGGL(csc_place_kernel, dim3(nchunks), dim3(kCscThreads), sh, s, row_ptr, E,
+                       d_out, d_in, nchunks, col_ptr, hist, csc_perm);
+  }
   return hipGetLastError();
 }
 
