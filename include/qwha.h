@@ -61,7 +61,7 @@ typedef struct ihipEvent_t* hipEvent_t;   /* HIP's opaque event handle */
 typedef enum qwha_status {
   QWHA_OK = 0,
   QWHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad flag or scalar */
-  QWHA_ERR_SHAPE = 2,       /* d_in not a power of two in [2,16384], d_out or T out of range */
+  QWHA_ERR_SHAPE = 2,       /* d_in not a supported width (see Shapes), d_out or T out of range */
   QWHA_ERR_BUDGET = 3,      /* p outside its allowed range */
   QWHA_ERR_DTYPE = 4,       /* unknown qwha_dtype */
   QWHA_ERR_ALIGN = 5,       /* pointer not aligned as required */

@@ -108,7 +108,9 @@ def _edge_dwq(d_out, d_in, seed):
     (64, 256, 64 * 256, 3), (50, 512, 150, 3),
     # more rows than the allocator's threads: several rows (and budget
     # values) per thread, the last threads with none
-    (1025, 128, 20000, 3), (2500, 64, 30000, 3), (4100, 32, 50000, 3)])
+    (1025, 128, 20000, 3), (2500, 64, 30000, 3), (4100, 32, 50000, 3),
+    # more than 64 rows per CSC chunk: the row-at-a-time placement
+    (20000, 8, 80000, 3)])
 def test_init_select_edges(q, d_out, d_in, p, m):
     say("init edge", d_out, d_in, p, m)
     dwq = _edge_dwq(d_out, d_in, d_out + d_in)
