@@ -13,19 +13,6 @@
 namespace qwha {
 
 // ------------------------------------------------------------ block helpers
-// Sum over the block; every thread gets the total. red must hold 2*16 ints;
-// alternate `parity` between consecutive calls so one barrier suffices.
-__device__ __forceinline__ int block_sum_i32(int v, int* red, int parity) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int nw = (blockDim.x + 63) >> 6;
-  v = wave_sum_i32(v);
-  if (lane == 0) red[parity * 16 + wid] = v;
-  __syncthreads();
-  int t = 0;
-  for (int i = 0; i < nw; ++i) t += red[parity * 16 + i];
-  return t;
-}
-
 // Sum over the block of a wave-uniform value (lane 0 of each wave posts it).
 __device__ __forceinline__ int block_total_i32(int v, int* red, int parity) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;

@@ -10,8 +10,6 @@ namespace qwha {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
-inline size_t dt_size(Dt d) { return d == Dt::F32 ? 4 : 2; }
-
 // out[r][:] = scale * FWHT(in[r][:]) (+ out[r][:] if accumulate)
 hipError_t launch_fwht(const void* in, Dt in_dt, void* out, Dt out_dt, int64_t rows,
                        int log_n, float scale, int accumulate, hipStream_t s);
