@@ -28,7 +28,11 @@
  *    16-byte aligned, index and value arrays 4-byte aligned
  *    (QWHA_ERR_ALIGN otherwise).
  *  - Shapes: 2 <= d_in <= 16384, 1 <= d_out <= 1048576, T >= 0 (T == 0
- *    is a no-op), p <= 2^31 - 1 (QWHA_ERR_SHAPE otherwise). The transform
+ *    is a no-op), p <= 2^31 - 1 (QWHA_ERR_SHAPE otherwise). The calls that
+ *    run the gather-SpMM (qwha_fwd, qwha_fwd_save, qwha_bwd, qwha_bwd_saved,
+ *    qwha_layer_fwd) take p <= (2^31 - 65) / 2 = 1073741791, since their
+ *    prepared stream of at most 2p + 16 entries is indexed in int32
+ *    (QWHA_ERR_BUDGET otherwise; their workspace queries return 0). The transform
  *    H is the Sylvester matrix of order d_in when d_in is a power of two.
  *    Otherwise d_in = m * b, with b the largest power of two dividing it
  *    (m odd), and H is block-diagonal with m Sylvester blocks of order b,

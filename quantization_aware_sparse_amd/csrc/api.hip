@@ -83,6 +83,16 @@ qwha_status check_p(int64_t p, int32_t d_out, int32_t d_in) {
   return QWHA_OK;
 }
 
+// The SpMMs' prepared stream addresses its entries with int32 positions;
+// padded to whole pairs it holds at most 2p + 16 entries.
+constexpr int64_t kMaxStreamP = (static_cast<int64_t>(INT32_MAX) - 64) / 2;
+qwha_status check_stream_p(int64_t p) {
+  if (p > kMaxStreamP)
+    return fail(QWHA_ERR_BUDGET, "p=%lld exceeds %lld, the most the SpMM stream addresses",
+                static_cast<long long>(p), static_cast<long long>(kMaxStreamP));
+  return QWHA_OK;
+}
+
 qwha_status check_quant(int32_t bits, int32_t group, int32_t d_in, int32_t min_group) {
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
     return fail(QWHA_ERR_INVALID_ARG, "bits=%d is not one of 2, 3, 4, 8", bits);
@@ -451,7 +461,7 @@ qwha_status qwha_merge(const uint32_t* codes, const float* scales, const float* 
 }
 
 size_t qwha_layer_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
-  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0 || p > kMaxStreamP) return 0;
   return fwd_ws(T, d_in, d_out, p).total + align256(static_cast<size_t>(T) * d_out * 4);
 }
 
@@ -466,6 +476,7 @@ qwha_status qwha_layer_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_i
   QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   if (d_in < 64) return fail(QWHA_ERR_SHAPE, "d_in=%d below 64", d_in);
   QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
   QWHA_TRY(check_dt(act, "act"));
   if (act != QWHA_BF16)
     return fail(QWHA_ERR_DTYPE, "the base GEMM runs on bf16 activations");
@@ -542,7 +553,7 @@ qwha_status qwha_materialize(const int32_t* row_ptr, const int32_t* E, const flo
 
 // ------------------------------------------------------------------ forward
 size_t qwha_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
-  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0 || p > kMaxStreamP) return 0;
   return fwd_ws(T, d_in, d_out, p).total;
 }
 
@@ -561,6 +572,7 @@ qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
   int nblk;
   QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
   QWHA_TRY(check_dt(act, "act"));
   if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
   if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
@@ -622,7 +634,7 @@ qwha_status qwha_fwd_save(const void* x, qwha_dtype act, int64_t T, int32_t d_in
 
 // ------------------------------------------------------------------ backward
 size_t qwha_bwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t p) {
-  if (T < 0 || d_in < 1 || d_out < 1 || p < 0) return 0;
+  if (T < 0 || d_in < 1 || d_out < 1 || p < 0 || p > kMaxStreamP) return 0;
   const size_t a = bwd_ws(T, d_in, d_out, p, true).total;
   const size_t b = bwd_ws(T, d_in, d_out, p, false).total;
   return a > b ? a : b;
@@ -644,6 +656,7 @@ qwha_status bwd_impl(const void* x, const float* z_in, const void* dy, qwha_dtyp
   int nblk;
   QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
   QWHA_TRY(check_dt(act, "act"));
   if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
   if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");

@@ -95,6 +95,21 @@ def test_fwd_validation(q):
     assert _fwd(q, T=-3) == SHAPE
 
 
+def test_stream_position_limit(q):
+    # the SpMM stream holds at most 2p + 16 entries at int32 positions: p is
+    # capped at (2^31 - 65) // 2 for the calls that build it
+    big = dict(d_out=65536, d_in=16384)
+    limit = (2**31 - 1 - 64) // 2
+    assert _fwd(q, p=limit + 1, **big) == BUDGET
+    assert b"stream" in q.qwha_last_error()
+    # at the limit the budget passes and the (absent) workspace is what fails
+    assert _fwd(q, p=limit, **big) == WORKSPACE
+    assert q.qwha_fwd_workspace_bytes(16, 16384, 65536, limit + 1) == 0
+    assert q.qwha_bwd_workspace_bytes(16, 16384, 65536, limit + 1) == 0
+    assert q.qwha_layer_fwd_workspace_bytes(16, 16384, 65536, limit + 1) == 0
+    assert q.qwha_fwd_workspace_bytes(16, 16384, 65536, limit) > 0
+
+
 def test_init_validation(q):
     def call(**kw):
         a = dict(dWq=FAKE, d_out=256, d_in=256, p=2048, m=3, t=1.0, row_ptr=FAKE, E=FAKE,
