@@ -515,15 +515,40 @@ KERNEL_SOURCES = {
 SHARED_SOURCES = ["common.h", "launch.h", "api.hip"]
 
 
+def strip_comments(text):
+    """C++ source without its comments and blank space: what the compiler
+    sees, so that a comment edit does not count as a change of the code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(kernel):
-    """sha256 over the HIP sources a kernel is built from: a traffic figure
-    measured on other sources is stale."""
+    """sha256 over the code (comments and spacing left out) of the HIP
+    sources a kernel is built from: a traffic figure measured on other code
+    is stale."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantization_aware_sparse_amd", "csrc")
     for name in sorted(set(KERNEL_SOURCES[kernel] + SHARED_SOURCES)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

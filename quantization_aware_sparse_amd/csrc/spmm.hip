@@ -297,9 +297,10 @@ __device__ __forceinline__ float dpp_row_shr(float v) {
 // Plain SpMM (no dc partials). A workgroup of 16 waves owns a tile of 256
 // tokens and 256 output rows; wave w owns rows row0 .. row0+15 and lane l
 // owns tokens 4l .. 4l+3 of the tile, so a row's segment is the same for the
-// whole wave: its entries are read with scalar loads and each costs one
-// conflict-free ds_read_b128 (1 KiB per wave), one address add and four FMAs
-// with the value as a scalar operand. No entry is masked or padded.
+// whole wave: its entries are read from the run staged in LDS (one broadcast
+// read per pair of entries, issued a pair ahead) and each costs one
+// conflict-free ds_read_b128 (1 KiB per wave), one address add and four FMAs.
+// No entry is masked; segments are padded with zero entries to even lengths.
 //
 // Staging: block b of 64 source columns is held token-minor (row jj of the
 // block is the 256 tokens of column jj), double buffered; thread tid loads
