@@ -15,6 +15,11 @@
 //                 sums are scaled by s in fp32 and accumulated, so the only
 //                 roundings are those of the fp32 sums. `add` carries the
 //                 adapter's alpha z F^T (fp32) into the single bf16 store.
+//                 2-, 3- and 8-bit codes;
+//   qgemm4_ring_kernel  the same product for 4-bit codes, its operands
+//                 loaded straight into LDS two steps ahead.
+#include <type_traits>
+
 #include "fwht_core.h"
 #include "launch.h"
 
@@ -303,6 +308,256 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
     }
 }
 
+// ---- 4-bit codes: a three-step ring of direct-to-LDS loads
+// Same tile, wave split and MFMA layout as qgemm_kernel, with two changes:
+// - x, the code words and the step's scales and zeros go global -> LDS by
+//   global_load_lds (no staging registers), two steps ahead of use, so their
+//   latency hides behind two steps of MFMA;
+// - the weight operand is 128 + q, whose bf16 bits are 0x4300 | q (a byte
+//   permute per pair of codes), and the zero point comes back per group:
+//   sum_k x (q - z) = sum_k x (128 + q) - (128 + z) sum_k x, with sum_k x
+//   from one more MFMA per 16 tokens against a ones operand. Products and
+//   sums stay exact in fp32 up to the order of the fp32 additions.
+constexpr int kRing = 3;
+
+// 16-byte chunk slot of k-chunk c (0..7) in row r of a 128-byte LDS row:
+// conflict-free ds_read_b128 over 16 consecutive rows
+__device__ __forceinline__ int qswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Direct-to-LDS loads (lane l's bytes land at the wave-uniform LDS base +
+// size * l), issued in asm so that the compiler adds no waits of its own
+// before later LDS reads; every wait on them is explicit (wait_vm). The LDS
+// base is the low half of the generic address of an LDS location.
+__device__ __forceinline__ uint32_t lds_base(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+// bf16x8 of 128 + q for the 8 codes of a word (bf16(128 + q) = 0x4300 | q)
+__device__ __forceinline__ bf16x8 unpack_off128(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // q0 q2 q4 q6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // q1 q3 q5 q7
+  uint32_t d[4];
+  // byte 0 <- lo.byte i, byte 2 <- hi.byte i, bytes 1, 3 <- 0
+  d[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+  d[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+  d[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
+  d[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+  bf16x8 r;
+  __builtin_memcpy(&r, d, 16);
+  return r;
+}
+
+// ring slot S: its own LDS arrays, so that the compiler's wait before an LDS
+// read covers only the loads into that slot
+template <int S>
+struct RingSlot {
+  static __device__ __forceinline__ uint16_t* A() {
+    __shared__ __attribute__((aligned(16))) uint16_t a[kQT * kQK];   // 16 KiB
+    return a;
+  }
+  static __device__ __forceinline__ uint32_t* C() {
+    __shared__ __attribute__((aligned(16))) uint32_t c[kQT * 8];     // 4 KiB
+    return c;
+  }
+  static __device__ __forceinline__ float* SZ() {
+    __shared__ __attribute__((aligned(16))) float sz[512];            // scales | zeros, 2 halves
+    return sz;
+  }
+};
+
+template <bool G32>
+__global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t T, int K, int N, QuantW qw,
+                                                             const float* __restrict__ add,
+                                                             uint16_t* __restrict__ y) {
+  const int ntn = (N + kQT - 1) / kQT;
+  int tm, tn;
+  {
+    const int b = blockIdx.x;
+    if (ntn % kXcd == 0) {
+      const int per = ntn / kXcd, slot = b / kXcd;
+      tm = slot / per;
+      tn = (b % kXcd) * per + slot % per;
+    } else {
+      tm = b / ntn;
+      tn = b % ntn;
+    }
+  }
+  const int64_t m0 = static_cast<int64_t>(tm) * kQT;
+  const int n0 = tn * kQT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  // the arrays are written only by the loads into LDS; this store (never
+  // taken) keeps the compiler from treating their contents as undefined
+  if (K < 0) {
+    RingSlot<0>::A()[tid] = 0; RingSlot<1>::A()[tid] = 0; RingSlot<2>::A()[tid] = 0;
+    RingSlot<0>::C()[tid] = 0; RingSlot<1>::C()[tid] = 0; RingSlot<2>::C()[tid] = 0;
+    RingSlot<0>::SZ()[tid] = 0; RingSlot<1>::SZ()[tid] = 0; RingSlot<2>::SZ()[tid] = 0;
+  }
+
+  // per-thread sources of the ring loads
+  const uint16_t* xs_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 32 + w * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ qswz(r);
+    const int64_t row = m0 + r < T ? m0 + r : T - 1;
+    xs_src[i] = x + row * K + 8 * c;
+  }
+  const int cn = (w * 64 + lane) >> 1;                 // code row of this thread
+  const uint32_t* c_src = qw.codes + static_cast<int64_t>(n0 + cn < N ? n0 + cn : N - 1) * qw.wpr +
+                          4 * ((w * 64 + lane) & 1);
+  const int szr = (w * 64 + lane) & 127;
+  const float* sz_src = (w < 2 ? qw.scales : qw.zeros) +
+                        static_cast<int64_t>(n0 + szr < N ? n0 + szr : N - 1) * qw.gpr;
+  constexpr int kLoadsPerStep = 7;
+
+  f32x4 acc[4][4], gacc[4][4], xsum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xsum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  bf16x8 ones;
+  {
+    const uint32_t o[4] = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    __builtin_memcpy(&ones, o, 16);
+  }
+  const int gmask = (1 << qw.lg_group) - 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int aswz = qswz(lr);
+  const int nsteps = K / kQK;
+
+  auto issue = [&](auto slot_c, int st) {
+    using RS = RingSlot<decltype(slot_c)::value>;
+    const int k0 = st * kQK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(xs_src[i] + k0, lds_base(RS::A() + (i * 256 + w * 64) * 8));
+    dma16(c_src + k0 / 8, lds_base(RS::C() + w * 64 * 4));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma4(sz_src + ((k0 + 32 * h) >> qw.lg_group), lds_base(RS::SZ() + h * 256 + w * 64));
+  };
+
+  // one step on ring slot S (its loads are in), issuing step st + 2's loads
+  // into slot (S + 2) % 3 first. Both half-steps' operands are read up
+  // front. A group's first half-step starts its sums from zero (no clears):
+  // with 32-column groups every half-step, else the first half of a step
+  // that starts a group.
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](auto slot_c, int st) {
+    constexpr int S = decltype(slot_c)::value;
+    using RS = RingSlot<S>;
+    if (st + 2 < nsteps) issue(std::integral_constant<int, (S + 2) % kRing>{}, st + 2);
+    const char* abase = reinterpret_cast<const char*>(RS::A());
+    const uint32_t* cbase = RS::C();
+    const float* szb = RS::SZ();
+    bf16x8 af[2][4];
+    uint32_t cw[2][4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kc = kh * 4 + lq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[kh][i] = *reinterpret_cast<const bf16x8*>(abase + (wm + i * 16 + lr) * 128 +
+                                                     16 * (kc ^ aswz));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cw[kh][j] = cbase[(wn + j * 16 + lr) * 8 + kc];
+    }
+    const int k0 = st * kQK;
+    const bool gstart = (k0 & gmask) == 0;
+    auto half = [&](int kh, bool fresh) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xsum[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kh][i], ones, fresh ? zero4 : xsum[i],
+                                                          0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 bf = unpack_off128(cw[kh][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kh][i], bf,
+                                                               fresh ? zero4 : gacc[i][j], 0, 0, 0);
+      }
+    };
+    // y += s (sum x (128 + q) - (128 + z) sum x) for the group of half kh
+    auto close = [&](int kh) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = szb[kh * 256 + wn + j * 16 + lr];
+        const float zo = 128.f + szb[kh * 256 + 128 + wn + j * 16 + lr];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = fmaf(sc, fmaf(-zo, xsum[i][r], gacc[i][j][r]), acc[i][j][r]);
+      }
+    };
+    if (G32) {
+      half(0, true);
+      close(0);
+      half(1, true);
+      close(1);
+    } else {
+      if (gstart) half(0, true); else half(0, false);
+      half(1, false);
+      if (((k0 + kQK) & gmask) == 0) close(1);
+    }
+    if (st + 1 < nsteps) {
+      // this wave's loads of step st + 1 are in (those of st + 2 may still
+      // fly) and its LDS reads of this step are done; then every wave's
+      if (st + 2 < nsteps) wait_vm<kLoadsPerStep>(); else wait_vm<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      lds_barrier();
+    }
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1);
+  if (nsteps > 1) wait_vm<kLoadsPerStep>(); else wait_vm<0>();
+  lds_barrier();
+  for (int st = 0; st < nsteps; st += kRing) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nsteps) step(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < nsteps) step(std::integral_constant<int, 2>{}, st + 2);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = m0 + wm + i * 16 + 4 * lq + r;
+        if (t < T && n < N) {
+          const int64_t at = t * N + n;
+          y[at] = f32_to_bf16(add ? acc[i][j][r] + add[at] : acc[i][j][r]);
+        }
+      }
+    }
+}
+
 }  // namespace
 
 QuantW make_quant(const uint32_t* codes, const float* scales, const float* zeros, int bits,
@@ -352,7 +607,10 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t T, int K, int N, const QuantW
       hipLaunchKernelGGL(qgemm_kernel<3>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
       break;
     case 4:
-      hipLaunchKernelGGL(qgemm_kernel<4>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      if (qw.lg_group == 5)
+        hipLaunchKernelGGL(qgemm4_ring_kernel<true>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
+      else
+        hipLaunchKernelGGL(qgemm4_ring_kernel<false>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
       break;
     case 8:
       hipLaunchKernelGGL(qgemm_kernel<8>, grid, dim3(256), 0, s, x, T, K, N, qw, add, y);
