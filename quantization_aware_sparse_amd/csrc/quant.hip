@@ -332,32 +332,36 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Direct-to-LDS loads (lane l's bytes land at the wave-uniform LDS base +
-// size * l), issued in asm so that the compiler adds no waits of its own
-// before later LDS reads; every wait on them is explicit (wait_vm). The LDS
-// base is the low half of the generic address of an LDS location.
-__device__ __forceinline__ uint32_t lds_base(const void* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+// Direct-to-LDS loads: lane l's bytes go from sbase + voff to LDS at m0 +
+// size * l (m0 wave-uniform). Issued in asm so that the compiler adds no
+// waits of its own before later LDS reads; every wait on them is explicit
+// (wait_vm). An LDS address is the low half of the generic address. M0 is
+// a reserved register the compiler sets itself before each of its own uses
+// (on gfx950 LDS instructions need none; this kernel has no other use), so
+// it is not listed as clobbered.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(m0)
+               : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(m0)
+               : "memory");
 }
 
-// bf16x8 of 128 + q for the 8 codes of a word (bf16(128 + q) = 0x4300 | q)
+// bf16x8 of 128 + q for the 8 codes of a word (bf16(128 + q) = 0x4300 | q):
+// dword i takes byte i of w (low nibble q_2i) and byte i of w >> 4 (low
+// nibble q_2i+1) into its bytes 0 and 2, then keeps those nibbles
 __device__ __forceinline__ bf16x8 unpack_off128(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // q0 q2 q4 q6
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // q1 q3 q5 q7
+  const uint32_t u = w >> 4;
   uint32_t d[4];
-  // byte 0 <- lo.byte i, byte 2 <- hi.byte i, bytes 1, 3 <- 0
-  d[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
-  d[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
-  d[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
-  d[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d[i] = (__builtin_amdgcn_perm(u, w, 0x0C040C00u + 0x00010001u * i) & 0x000F000Fu) | 0x43004300u;
   bf16x8 r;
   __builtin_memcpy(&r, d, 16);
   return r;
@@ -411,21 +415,30 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
     RingSlot<0>::SZ()[tid] = 0; RingSlot<1>::SZ()[tid] = 0; RingSlot<2>::SZ()[tid] = 0;
   }
 
-  // per-thread sources of the ring loads
-  const uint16_t* xs_src[4];
+  // ring loads: per-thread byte offsets from wave-uniform bases; rows past
+  // T or N repeat the last row (their results are never stored). Code rows
+  // are stored with half h of row n at 16-byte position 2n + (h ^ bit 3 of
+  // n), so that the 16 rows a read covers hit distinct banks.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint16_t* xtile = x + m0 * K;
+  uint32_t xoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = i * 32 + w * 8 + (lane >> 3);
     const int c = (lane & 7) ^ qswz(r);
-    const int64_t row = m0 + r < T ? m0 + r : T - 1;
-    xs_src[i] = x + row * K + 8 * c;
+    const int64_t rr = (m0 + r < T ? m0 + r : T - 1) - m0;
+    xoff[i] = static_cast<uint32_t>((rr * K + 8 * c) * 2);
   }
-  const int cn = (w * 64 + lane) >> 1;                 // code row of this thread
-  const uint32_t* c_src = qw.codes + static_cast<int64_t>(n0 + cn < N ? n0 + cn : N - 1) * qw.wpr +
-                          4 * ((w * 64 + lane) & 1);
-  const int szr = (w * 64 + lane) & 127;
-  const float* sz_src = (w < 2 ? qw.scales : qw.zeros) +
-                        static_cast<int64_t>(n0 + szr < N ? n0 + szr : N - 1) * qw.gpr;
+  const int cp = w * 64 + lane;                        // 16-byte position in the code slot
+  const int cn = cp >> 1;                              // its code row
+  const int chalf = (cp & 1) ^ ((cn >> 3) & 1);
+  const uint32_t* ctile = qw.codes + static_cast<int64_t>(n0) * qw.wpr;
+  const uint32_t coff = static_cast<uint32_t>(
+      ((static_cast<int64_t>(n0 + cn < N ? n0 + cn : N - 1) - n0) * qw.wpr + 4 * chalf) * 4);
+  const int szr = cp & 127;
+  const float* sztile = (wu < 2 ? qw.scales : qw.zeros) + static_cast<int64_t>(n0) * qw.gpr;
+  const uint32_t szoff =
+      static_cast<uint32_t>((static_cast<int64_t>(n0 + szr < N ? n0 + szr : N - 1) - n0) * qw.gpr * 4);
   constexpr int kLoadsPerStep = 7;
 
   f32x4 acc[4][4], gacc[4][4], xsum[4];
@@ -452,11 +465,12 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
     using RS = RingSlot<decltype(slot_c)::value>;
     const int k0 = st * kQK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(xs_src[i] + k0, lds_base(RS::A() + (i * 256 + w * 64) * 8));
-    dma16(c_src + k0 / 8, lds_base(RS::C() + w * 64 * 4));
+    for (int i = 0; i < 4; ++i)
+      dma16(xoff[i], xtile + k0, lds_addr(RS::A()) + (i * 256 + wu * 64) * 16);
+    dma16(coff, ctile + k0 / 8, lds_addr(RS::C()) + wu * 64 * 16);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      dma4(sz_src + ((k0 + 32 * h) >> qw.lg_group), lds_base(RS::SZ() + h * 256 + w * 64));
+      dma4(szoff, sztile + ((k0 + 32 * h) >> qw.lg_group), lds_addr(RS::SZ()) + (h * 256 + wu * 64) * 4);
   };
 
   // one step on ring slot S (its loads are in), issuing step st + 2's loads
@@ -482,7 +496,8 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
         af[kh][i] = *reinterpret_cast<const bf16x8*>(abase + (wm + i * 16 + lr) * 128 +
                                                      16 * (kc ^ aswz));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cw[kh][j] = cbase[(wn + j * 16 + lr) * 8 + kc];
+      for (int j = 0; j < 4; ++j)
+        cw[kh][j] = cbase[(2 * (wn + j * 16 + lr) + (kh ^ (lr >> 3))) * 4 + lq];
     }
     const int k0 = st * kQK;
     const bool gstart = (k0 & gmask) == 0;
