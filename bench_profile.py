@@ -50,6 +50,7 @@ KERNEL_IDS = {
     # quantized base layer
     "merge_kernel": ["MERGE"],
     "qgemm_kernel": ["QGEMM"],
+    "qgemm4_ring_kernel": ["QGEMM"],
 }
 
 
