@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256, 2) void qgemm_kernel(const uint16_t* __restric
 //   global_load_lds (no staging registers), two steps ahead of use, so their
 //   latency hides behind two steps of MFMA;
 // - the weight operand is 128 + q, whose bf16 bits are 0x4300 | q (a byte
-//   permute per pair of codes), and the zero point comes back per group:
+//   permute and an and-or per pair of codes), and the zero point comes back
+//   per group:
 //   sum_k x (q - z) = sum_k x (128 + q) - (128 + z) sum_k x, with sum_k x
 //   from one more MFMA per 16 tokens against a ones operand. Products and
 //   sums stay exact in fp32 up to the order of the fp32 additions.
@@ -367,8 +368,8 @@ __device__ __forceinline__ bf16x8 unpack_off128(uint32_t w) {
   return r;
 }
 
-// ring slot S: its own LDS arrays, so that the compiler's wait before an LDS
-// read covers only the loads into that slot
+// ring slot S: its own LDS arrays, so that every LDS address of a step is a
+// compile-time constant (the step loop is unrolled over the three slots)
 template <int S>
 struct RingSlot {
   static __device__ __forceinline__ uint16_t* A() {
