@@ -462,6 +462,8 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
   const int aswz = qswz(lr);
   const int nsteps = K / kQK;
 
+  // exactly kLoadsPerStep loads per thread, always in this order: the
+  // explicit vmcnt waits count on it
   auto issue = [&](auto slot_c, int st) {
     using RS = RingSlot<decltype(slot_c)::value>;
     const int k0 = st * kQK;
