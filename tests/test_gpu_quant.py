@@ -87,7 +87,7 @@ def test_merge(q, d_out, d_in, bits, group, p, out):
     (1, 37, 64, 4, 32, 40), (5, 200, 64, 2, 64, 700), (130, 129, 256, 3, 128, 1500),
     (300, 256, 1024, 4, 128, 4000), (77, 64, 4096, 8, 128, 3000), (200, 96, 512, 4, 64, 0),
     (129, 300, 128, 4, 32, 300 * 128), (257, 130, 320, 4, 64, 2000),
-    (64, 128, 2048, 4, 256, 5000), (3, 1, 128, 4, 32, 1)])
+    (64, 128, 2048, 4, 256, 5000), (3, 1, 128, 4, 32, 1), (150, 200, 4096, 4, 32, 9000)])
 def test_layer_forward(q, T, d_out, d_in, bits, group, p):
     say("layer fwd", T, d_out, d_in, bits, group, p)
     L = quant_layer(d_out, d_in, bits, group, p, seed=T + d_out + d_in)
