@@ -206,6 +206,59 @@ def test_adaalloc_rejects_infeasible():
         O.adaalloc(np.ones(4), 33, 8, m=3)       # p > d_in d_out
 
 
+# ------------------------------------------- AdaAlloc rounding margins (O12)
+# The margin of a row is the distance of its share P s_i / S in the final
+# proportional pass to the nearest integer (inf for a row held at the floor
+# or the cap). The values below are worked by hand.
+
+def test_adaalloc_margin_half():
+    # w = (1, 1), p = 7: both shares are 7/2 = 3.5, half-way between floors
+    got = O.adaalloc_margins(np.array([1.0, 1.0]), 7, 100, m=3)
+    assert np.array_equal(got, [0.5, 0.5])
+    assert np.array_equal(O.adaalloc(np.array([1.0, 1.0]), 7, 100, m=3), [4, 3])
+
+
+def test_adaalloc_margin_of_the_golden_case_and_the_floored_row():
+    # w = (1, 2, 3, 4), p = 20, m = 3: row 0 is held at the floor in the first
+    # pass; the second pass shares P = 17 over S = 9: 34/9, 51/9, 68/9, whose
+    # distances to 4, 6, 8 are 2/9, 3/9, 4/9
+    got = O.adaalloc_margins(np.array([1.0, 2.0, 3.0, 4.0]), 20, 100, m=3)
+    assert got[0] == np.inf
+    assert np.allclose(got[1:], [2 / 9, 3 / 9, 4 / 9], rtol=0, atol=1e-14)
+
+
+def test_adaalloc_margin_near_an_integer():
+    # w = (1, 2 + d), p = 30: the shares are 30/(3+d) and 30(2+d)/(3+d), both
+    # 10 d / (3 + d) from the integers 10 and 20 (about 1e-12 for d = 3e-13)
+    d = 3e-13
+    w = np.array([1.0, 2.0 + d])
+    dd = w[1] - 2.0                          # the d that fp64 actually holds
+    want = 10.0 * dd / (3.0 + dd)
+    got = O.adaalloc_margins(w, 30, 100, m=0)
+    assert np.all(np.abs(got - want) <= 2e-15), (got, want)
+    assert 0.9e-12 < got[0] < 1.1e-12
+    # an exact split has margin 0 in every row
+    assert np.array_equal(O.adaalloc_margins(np.array([1.0, 2.0, 1.0]), 40, 100, m=0),
+                          [0.0, 0.0, 0.0])
+
+
+def test_adaalloc_margin_after_the_cap_releases_the_floor():
+    # w = (1, 1, 100), p = 40, d_in = 16, m = 1: rows 0, 1 fall below the
+    # floor first (40/102 each); then row 2's share 38 exceeds the cap and is
+    # held at 16, which releases rows 0 and 1; they split the remaining 24
+    # evenly: shares 12, 12 (margin 0) and row 2 at the cap (inf)
+    w = np.array([1.0, 1.0, 100.0])
+    assert np.array_equal(O.adaalloc(w, 40, 16, m=1), [12, 12, 16])
+    assert np.array_equal(O.adaalloc_margins(w, 40, 16, m=1), [0.0, 0.0, np.inf])
+
+
+def test_adaalloc_margin_temperature():
+    # t = 2 shares by sqrt(w): w = (1, 4) -> s = (1, 2), p = 10: shares
+    # 10/3 and 20/3, both 1/3 from an integer
+    got = O.adaalloc_margins(np.array([1.0, 4.0]), 10, 100, m=0, t=2.0)
+    assert np.allclose(got, [1 / 3, 1 / 3], rtol=0, atol=1e-14)
+
+
 # -------------------------------------------------------- selection (O5/O6)
 
 @pytest.mark.parametrize("n", [4, 8, 16])
@@ -254,6 +307,60 @@ def test_select_ties_go_to_lower_column():
     Cz = np.array([[0.0, -0.0, 0.0, -0.0]])
     _, E = O.select(Cz, np.array([2]))
     assert np.array_equal(E[:, 1], [0, 1])
+
+
+def _row_with_transform(Crow):
+    """A 1 x n error row whose dense solution dW_Q H is exactly Crow:
+    dW_Q = Crow H / n (H H = n I); every value used here is exact in fp64."""
+    n = len(Crow)
+    return (np.asarray(Crow, dtype=np.float64) @ O.sylvester(n) / n)[None, :]
+
+
+def test_boundary_gap_hand_worked():
+    # C = (4, 3, 2, 1) by construction: the gap between the k-th and
+    # (k+1)-th largest |C| over the k-th is 1/4 (k = 1), 1/3 (k = 2) and
+    # 1/2 (k = 3); no boundary exists for k = 0 or k = n (inf)
+    dwq = _row_with_transform([4.0, 3.0, 2.0, 1.0])
+    assert np.array_equal(dwq, [[2.5, 0.5, 1.0, 0.0]])
+    for k, want in ((0, np.inf), (1, 0.25), (2, 1 / 3), (3, 0.5), (4, np.inf)):
+        r = O.init_select(dwq, k, m=0, with_diagnostics=True)
+        assert np.array_equal(r["C"], [[4.0, 3.0, 2.0, 1.0]])
+        assert r["boundary_gap"][0] == pytest.approx(want, rel=1e-15), k
+    # the order of C's columns does not matter, signs neither
+    dwq = _row_with_transform([-1.0, 3.0, -4.0, 2.0])
+    r = O.init_select(dwq, 2, m=0, with_diagnostics=True)
+    assert r["boundary_gap"][0] == pytest.approx(1 / 3, rel=1e-15)
+    assert np.array_equal(r["E"][:, 1], [1, 2])
+
+
+def test_boundary_gap_tie_and_near_tie():
+    # a spike row has every |C| equal: the boundary sits inside a tie, gap 0
+    spike = np.zeros((1, 16))
+    spike[0, 5] = 0.75
+    r = O.init_select(spike, 3, m=0, with_diagnostics=True)
+    assert r["boundary_gap"][0] == 0.0
+    # C = (4, 4 - 4e, 2, 1) with e = 2^-40: the first boundary is e wide
+    e = 2.0 ** -40
+    dwq = _row_with_transform([4.0, 4.0 - 4.0 * e, 2.0, 1.0])
+    r = O.init_select(dwq, 1, m=0, with_diagnostics=True)
+    assert r["boundary_gap"][0] == e
+    # a row whose k-th largest |C| is zero has no boundary to measure (inf)
+    r = O.init_select(_row_with_transform([8.0, 0.0, 0.0, 0.0]), 2, m=0,
+                      with_diagnostics=True)
+    assert r["boundary_gap"][0] == np.inf
+
+
+def test_diagnostics_per_row():
+    # two rows with hand-worked C and budgets 1 and 2 (w = (5, 5) splits
+    # p = 3 into 1.5 and 1.5: floors 1, 1, leftover to row 0 -> (2, 1)).
+    # Row 0 keeps |C| = 4, 3 and leaves 0: gap (3 - 0) / 3 = 1; row 1 keeps 4
+    # and leaves 3: gap 1/4
+    dwq = np.vstack([_row_with_transform([3.0, 4.0, 0.0, 0.0]),
+                     _row_with_transform([0.0, 0.0, 4.0, 3.0])])
+    r = O.init_select(dwq, 3, m=0, with_diagnostics=True)
+    assert np.array_equal(r["budgets"], [2, 1])
+    assert np.array_equal(r["boundary_gap"], [1.0, 0.25])
+    assert np.array_equal(r["budget_margin"], [0.5, 0.5])
 
 
 def test_select_orders_rows_and_columns():
