@@ -89,13 +89,21 @@ int32_t qwha_version(void);
  * From the quantization error dWq = W0 - W_Q (fp32 [d_out][d_in]):
  *   1. w_i = ||dWq[i,:]||_2 (fp64): each output channel's error magnitude
  *      (identity Hessian: no calibration activations).
- *   2. AdaAlloc budgets p_i with sum p_i = p: p_i = floor(P s_i / S) with
- *      s_i = w_i^(1/temperature) over rows not yet fixed, rows below
- *      min_per_row fixed at min_per_row first, then rows above d_in fixed at
- *      d_in, repeated until nothing is fixed; the leftover (< d_out) goes one
- *      unit each to the rows with the smallest budget (lower row first, rows
- *      at d_in skipped). The exact formula is missing from the pages; this is
- *      the proportional reading (temperature 1 = linear).
+ *   2. AdaAlloc budgets p_i with sum p_i = p, by passes over the rows not
+ *      yet held: each such row gets the share q_i = P s_i / S, with
+ *      s_i = w_i^(1/temperature), P = p minus the budgets of the held rows
+ *      and S the sum of s_i over the free rows, and p_i = floor(q_i). If any
+ *      free row has q_i < min_per_row, those rows are held at min_per_row.
+ *      Otherwise, if any free row has q_i > d_in, those rows are held at
+ *      d_in and every row held at the floor is released again (capping a
+ *      row raises the others' shares). The passes repeat until one holds
+ *      nothing; this reaches the clamped proportional split
+ *      clamp(lambda s_i, min_per_row, d_in). The leftover (< d_out) then
+ *      goes one unit each to the rows with the smallest budget (lower row
+ *      first, rows at d_in skipped). The exact formula is missing from the
+ *      pages (papernotes.org, 关键设计 2 keeps only "proportional to each
+ *      channel's error magnitude" with a temperature); this is that
+ *      proportional reading (temperature 1 = linear).
  *   3. Dense solution C = dWq H (fp64 fast WHT per row).
  *   4. Row i keeps the p_i columns with the largest |C[i,j]|, ties to the
  *      lower column; they are written to E ascending, and

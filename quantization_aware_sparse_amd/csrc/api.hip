@@ -99,6 +99,10 @@ qwha_status check_quant(int32_t bits, int32_t group, int32_t d_in, int32_t min_g
   if (group < min_group || group > d_in || (group & (group - 1)) != 0)
     return fail(QWHA_ERR_INVALID_ARG, "group=%d is not a power of two in [%d, d_in]", group,
                 min_group);
+  // every group holds whole columns: a partial last group would have no
+  // scale and zero of its own (the kernels index groups as j / group)
+  if (d_in % group != 0)
+    return fail(QWHA_ERR_INVALID_ARG, "group=%d does not divide d_in=%d", group, d_in);
   return QWHA_OK;
 }
 

@@ -226,6 +226,10 @@ def test_quantized_base_validation(q):
     assert merge(W=FAKE + 8) == ALIGN
     assert merge(d_in=100) == SHAPE
     assert merge(alpha=float("nan")) == INVALID
+    # a block width (320 = 5 * 64) is a valid d_in, but groups of 128 would
+    # leave a partial last group with no scale / zero of its own
+    assert merge(d_in=320, group=128) == INVALID
+    assert merge(d_in=320, group=64, W=FAKE + 8) == ALIGN   # passes the group check
 
     def fwd(**kw):
         a = dict(x=FAKE, act=1, T=128, d_in=256, d_out=64, codes=FAKE, s=FAKE, z=FAKE, bits=4,
@@ -241,6 +245,8 @@ def test_quantized_base_validation(q):
     assert fwd(group=16) == INVALID              # groups below one MFMA depth
     assert fwd(bits=1) == INVALID
     assert fwd(x=FAKE + 2) == ALIGN
+    assert fwd(d_in=320, group=128) == INVALID   # group does not divide d_in
+    assert fwd(d_in=320, group=64) == WORKSPACE
     assert fwd() == WORKSPACE
     need = q.qwha_layer_fwd_workspace_bytes(128, 256, 64, 500)
     assert need >= 128 * 64 * 4 + 128 * 256 * 4

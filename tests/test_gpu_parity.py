@@ -1,12 +1,11 @@
 """Parity of the HIP path (through the C-ABI) with the fp64 CPU oracle.
 
-Bars: indices / budgets / permutations bit-exact; floating outputs within the
-normwise relative error max|a-b|/max|b| of 1e-5 for fp32 activations and
-2e-2 for bf16 activations; dW and c always at 1e-5 (they depend only on fp32
-c). Small shapes are compared element by element on every output; the full
-layer configurations (the same launch configuration bench.py times) are
-compared on E/row_ptr/col_ptr/csc_perm in full and on sampled tokens (y, dx)
-and sampled rows of F (dc) that the oracle computes one by one.
+Bars (tests/bars.py): indices / budgets / permutations bit-exact; fp32
+outputs (dW, c, dc, and y / dx with fp32 activations) within 1e-5 of the
+largest reference entry; bf16 outputs element by element within
+2^-8 |b| + 1e-5 max|b| (one bf16 rounding of an fp32 sum). Every output is
+compared whole, at the small shapes and at the full layer configurations
+(the same launch configuration bench.py times).
 """
 
 import numpy as np
@@ -14,6 +13,7 @@ import pytest
 
 import oracle as O
 import synth
+from tests.bars import assert_act_close, assert_f32_close
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +52,6 @@ def to_np(t):
     return t.cpu().numpy().astype(np.float64)
 
 
-def tol(act):
-    return 1e-5 if act == "f32" else 2e-2
-
-
 def init_both(q, dwq, p, m=3, t=1.0):
     ref = O.init_select(dwq, p, m=m, t=t, with_diagnostics=True)
     got = q.qwha_init_select(to_dev(dwq), p, m, t)
@@ -91,8 +87,7 @@ def test_fwht_parity(q, log_n, dts):
     y = q.qwha_fwht(x, scale, out_dtype=out_dt)
     torch.cuda.synchronize()
     ref = synth.act_to_f64(a) @ O.sylvester(n) * scale
-    bound = 1e-5 if dts[1] == "f32" else 2e-2
-    assert O.rel_err(to_np(y), ref) <= bound
+    assert_act_close(to_np(y), ref, dts[1], "fwht")
 
 
 # ------------------------------------------------------------------ init
@@ -141,8 +136,12 @@ def test_init_select_temperature_two(q):
     dwq = _edge_dwq(100, 128, 3)
     say("init t=2")
     ref, got = init_both(q, dwq, 3000, 3, t=2.0)
-    if np.min(ref["budget_margin"]) > 1e-9:
-        assert_init_equal(ref, got)
+    # the seed is chosen so that no share sits within fp64 rounding of an
+    # integer (where a different summation order could move a budget)
+    assert np.min(ref["budget_margin"]) > 1e-9, "ambiguous budget at this seed"
+    gap = ref["boundary_gap"]
+    assert not np.any((gap > 0) & (gap < 1e-9)), "ambiguous selection at this seed"
+    assert_init_equal(ref, got)
 
 
 @pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5"])
@@ -264,14 +263,14 @@ def test_materialize(q, d_out, d_in, p, out_dt):
                              alpha, out_dtype=dt)
     torch.cuda.synchronize()
     ref = O.materialize(r["E"], r["c"], d_out, d_in, alpha)
-    assert O.rel_err(to_np(got), ref) <= (1e-5 if out_dt == "f32" else 2e-2)
+    assert_act_close(to_np(got), ref, out_dt, "dW")
     # accumulate mode: dW += alpha F H^-1
     base = np.random.default_rng(1).standard_normal((d_out, d_in)).astype(np.float32)
     acc = to_dev(base)
     q.qwha_materialize(to_dev(r["row_ptr"]), to_dev(r["E"]), to_dev(r["c"]), d_out, d_in,
                        alpha, out=acc, accumulate=True)
     torch.cuda.synchronize()
-    assert O.rel_err(to_np(acc), base + ref) <= 1e-5
+    assert_f32_close(to_np(acc), base + ref, "dW accumulated")
 
 
 def test_materialize_full_budget_reconstructs(q):
@@ -280,7 +279,7 @@ def test_materialize_full_budget_reconstructs(q):
     r = O.init_select(dwq, d_out * d_in, m=3)
     got = q.qwha_materialize(to_dev(r["row_ptr"]), to_dev(r["E"]), to_dev(r["c"]), d_out, d_in)
     torch.cuda.synchronize()
-    assert O.rel_err(to_np(got), dwq.astype(np.float64)) <= 1e-5
+    assert_f32_close(to_np(got), dwq.astype(np.float64), "dW")
 
 
 # ------------------------------------------------------------------ fwd / bwd small
@@ -321,9 +320,9 @@ def test_fwd_bwd_small(q, d_out, d_in, p, T, act):
     dW = O.materialize(r["E"], r["c"], d_out, d_in, alpha)
     y_ref = O.forward(x64, dW)
     dx_ref, dc_ref = O.backward(x64, dy64, r["E"], r["c"], d_out, d_in, alpha, dW=dW)
-    assert O.rel_err(to_np(y), y_ref) <= tol(act)
-    assert O.rel_err(to_np(dx), dx_ref) <= tol(act)
-    assert O.rel_err(to_np(dc), dc_ref) <= tol(act)
+    assert_act_close(to_np(y), y_ref, act, "y")
+    assert_act_close(to_np(dx), dx_ref, act, "dx")
+    assert_f32_close(to_np(dc), dc_ref, "dc")
 
 
 @pytest.mark.parametrize("d_out,d_in,p,T,act", [(300, 64, 2500, 77, "f32"),
@@ -366,9 +365,9 @@ def test_fwd_bwd_accumulate_and_partial_outputs(q):
     torch.cuda.synchronize()
     dW = O.materialize(r["E"], r["c"], 300, 64, 1.0)
     dx_ref, dc_ref = O.backward(x, dy, r["E"], r["c"], 300, 64, 1.0, dW=dW)
-    assert O.rel_err(to_np(yt), base_y + O.forward(x, dW)) <= 1e-5
-    assert O.rel_err(to_np(dxt), base_dx + dx_ref) <= 1e-5
-    assert O.rel_err(to_np(dc_only), dc_ref) <= 1e-5
+    assert_f32_close(to_np(yt), base_y + O.forward(x, dW), "y accumulated")
+    assert_f32_close(to_np(dxt), base_dx + dx_ref, "dx accumulated")
+    assert_f32_close(to_np(dc_only), dc_ref, "dc")
 
 
 def test_zero_tokens(q):
@@ -412,26 +411,16 @@ def test_autograd_function(q):
     torch.cuda.synchronize()
     dW = O.materialize(r["E"], r["c"], 256, 256, 1.0)
     dx_ref, dc_ref = O.backward(x, dy, r["E"], r["c"], 256, 256, 1.0, dW=dW)
-    assert O.rel_err(to_np(y), O.forward(x, dW)) <= 1e-5
-    assert O.rel_err(to_np(xt.grad), dx_ref) <= 1e-5
-    assert O.rel_err(to_np(ct.grad), dc_ref) <= 1e-5
+    assert_f32_close(to_np(y), O.forward(x, dW), "y")
+    assert_f32_close(to_np(xt.grad), dx_ref, "dx")
+    assert_f32_close(to_np(ct.grad), dc_ref, "dc")
 
 
 # ------------------------------------------------------------------ full configs
-def _sample_tokens(T, k, seed):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(k, T), replace=False).tolist()) | {0, T - 1}
-    return np.array(sorted(s))
-
-
-def _sample_rows(d_out, k, seed):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(d_out, size=min(k, d_out), replace=False).tolist()) | {0, d_out - 1}
-    return np.array(sorted(s))
-
-
 def _check_layer_full(q, spec, layer, x, dy, got_init=None):
-    """Init (bit-exact), materialize, fwd, bwd at full size; sampled checks."""
+    """Init (bit-exact), materialize, fwd and bwd at full size, every output
+    compared whole with the oracle. Returns the GPU adapter, the GPU dc and
+    the oracle's dc."""
     d_out, d_in, T = spec.d_out, spec.d_in, x.shape[0]
     ref = O.init_select(layer.dwq, spec.p, m=3)
     if got_init is None:
@@ -444,19 +433,20 @@ def _check_layer_full(q, spec, layer, x, dy, got_init=None):
     y = q.qwha_fwd(xt, d_out, a["row_ptr"], a["E"], a["c"], 1.0)
     dx, dc = q.qwha_bwd(xt, dyt, a["row_ptr"], a["E"], a["c"], a["col_ptr"], a["csc_perm"], 1.0)
     torch.cuda.synchronize()
+    del xt, dyt
     dW_ref = O.materialize(ref["E"], ref["c"], d_out, d_in, 1.0)
-    rows = _sample_rows(d_out, 64, 1)
-    assert O.rel_err(to_np(dW[rows]), dW_ref[rows]) <= 1e-5
-    toks = _sample_tokens(T, 48, 2)
-    x64 = synth.act_to_f64(x[toks])
-    dy64 = synth.act_to_f64(dy[toks])
-    assert O.rel_err(to_np(y[toks]), O.forward(x64, dW_ref)) <= tol(spec.act)
-    assert O.rel_err(to_np(dx[toks]), dy64 @ dW_ref) <= tol(spec.act)
-    drows = _sample_rows(d_out, 6, 3)
-    ks, vals = O.backward_dc_rows(synth.act_to_f64(x), synth.act_to_f64(dy), ref["E"], drows,
-                                  d_in, 1.0)
-    assert O.rel_err(to_np(dc)[ks], vals) <= tol(spec.act)
-    return a, dc
+    assert_f32_close(to_np(dW), dW_ref, f"{spec.name} dW")
+    del dW
+    x64 = synth.act_to_f64(x)
+    dy64 = synth.act_to_f64(dy)
+    assert_act_close(to_np(y), O.forward(x64, dW_ref), spec.act, f"{spec.name} y")
+    del y
+    dx_ref, dc_ref = O.backward(x64, dy64, ref["E"], ref["c"], d_out, d_in, 1.0, dW=dW_ref)
+    del x64, dy64
+    assert_act_close(to_np(dx), dx_ref, spec.act, f"{spec.name} dx")
+    del dx, dx_ref
+    assert_f32_close(to_np(dc), dc_ref, f"{spec.name} dc")
+    return a, dc, dc_ref
 
 
 @pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
@@ -473,22 +463,26 @@ def test_full_config_attention_block_step(q):
     dW re-materialised. The update is checked bitwise against the GPU's own dc
     (an exactly-zero or near-zero dc would make the sign ambiguous); signs must
     agree with the oracle wherever |dc_ref| exceeds the observed error; the
-    re-materialised dW is checked against the oracle fed the GPU's c'."""
+    whole re-materialised dW is checked against the oracle fed the GPU's c'."""
     specs = synth.config_specs("c5")
     for spec in specs:
         say("c5", spec.name)
         layer = synth.make_layer(spec, seed=0)
         x, dy = synth.make_activations(spec, seed=0, x_stream=synth.C5_X_STREAM[spec.name])
-        a, dc = _check_layer_full(q, spec, layer, x, dy)
+        a, dc, dc_ref = _check_layer_full(q, spec, layer, x, dy)
+        del x, dy
+        dc_np = dc.cpu().numpy()
+        err = float(np.max(np.abs(dc_np.astype(np.float64) - dc_ref)))
+        sure = np.abs(dc_ref) > err
+        assert sure.mean() > 0.99, "too few dc entries with a certain sign"
+        assert np.array_equal(np.sign(dc_np[sure]), np.sign(dc_ref[sure])), "dc sign"
         c_old = a["c"].clone()
         q.qwha_sign_update(a["c"], dc, 1e-3)
         torch.cuda.synchronize()
         c_new = a["c"].cpu().numpy()
-        assert np.array_equal(c_new, O.sign_update(c_old.cpu().numpy(), dc.cpu().numpy()))
+        assert np.array_equal(c_new, O.sign_update(c_old.cpu().numpy(), dc_np))
         dW2 = q.qwha_materialize(a["row_ptr"], a["E"], a["c"], spec.d_out, spec.d_in, 1.0)
         torch.cuda.synchronize()
-        rows = _sample_rows(spec.d_out, 32, 4)
         E_np = a["E"].cpu().numpy()
-        sel = np.isin(E_np[:, 0], rows)
-        ref_rows = O.materialize(E_np[sel], c_new[sel], spec.d_out, spec.d_in, 1.0)[rows]
-        assert O.rel_err(to_np(dW2[rows]), ref_rows) <= 1e-5
+        ref2 = O.materialize(E_np, c_new, spec.d_out, spec.d_in, 1.0)
+        assert_f32_close(to_np(dW2), ref2, f"{spec.name} dW after the update")

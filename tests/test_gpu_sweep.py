@@ -14,6 +14,7 @@ import pytest
 
 import oracle as O
 import synth
+from tests.bars import assert_act_close, assert_f32_close
 
 pytestmark = pytest.mark.gpu
 
@@ -84,23 +85,22 @@ def test_random_shapes_whole_path(q, seed):
     alpha = 0.75
     dW = q.qwha_materialize(got["row_ptr"], got["E"], got["c"], d_out, d_in, alpha)
     dW_ref = O.materialize(ref["E"], ref["c"], d_out, d_in, alpha)
-    assert O.rel_err(to_np(dW), dW_ref) <= 1e-5
+    assert_f32_close(to_np(dW), dW_ref, "dW")
 
     x = rng.standard_normal((T, d_in)).astype(np.float32)
     dy = rng.standard_normal((T, d_out)).astype(np.float32)
     if act == "bf16":
         x, dy = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(dy)
-    bar = 1e-5 if act == "f32" else 2e-2
     xt, dyt = to_dev(x), to_dev(dy)
     y = q.qwha_fwd(xt, d_out, got["row_ptr"], got["E"], got["c"], alpha)
     dx, dc = q.qwha_bwd(xt, dyt, got["row_ptr"], got["E"], got["c"], got["col_ptr"],
                         got["csc_perm"], alpha)
     torch.cuda.synchronize()
     x64, dy64 = synth.act_to_f64(x), synth.act_to_f64(dy)
-    assert O.rel_err(to_np(y), O.forward(x64, dW_ref)) <= bar
+    assert_act_close(to_np(y), O.forward(x64, dW_ref), act, "y")
     dx_ref, dc_ref = O.backward(x64, dy64, ref["E"], ref["c"], d_out, d_in, alpha, dW=dW_ref)
-    assert O.rel_err(to_np(dx), dx_ref) <= bar
-    assert O.rel_err(to_np(dc), dc_ref) <= bar
+    assert_act_close(to_np(dx), dx_ref, act, "dx")
+    assert_f32_close(to_np(dc), dc_ref, "dc")
 
     # the update takes the sign of the GPU's own dc (a sign is a decision)
     c_gpu = got["c"].cpu().numpy()
