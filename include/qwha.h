@@ -163,6 +163,26 @@ qwha_status qwha_bwd(const void* x, const void* dy, qwha_dtype act, int64_t T, i
                      size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * qwha_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels as qwha_fwd, with the workspace taken from a
+ * static device array of 64 MiB (64 << 20 bytes) that the library holds on
+ * each GPU it runs on until the process ends. The call itself allocates
+ * nothing. A call whose qwha_fwd_workspace_bytes(T, d_in, d_out, p) exceeds
+ * 64 MiB is rejected with QWHA_ERR_WORKSPACE (e.g. d_in = d_out = 4096,
+ * p = 524288 takes T up to about 3300 tokens). The stream must belong to
+ * the current device (QWHA_ERR_INVALID_ARG otherwise); the first call on a
+ * device looks up the array's address there. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller. Nothing in the array
+ * needs clearing between calls: each call writes all it reads.
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_fwd_noalloc(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                             int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                             const float* c, float alpha, void* y, int32_t accumulate,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * The same forward and backward with the forward's transform kept, as
  * autograd keeps a saved activation: qwha_fwd_save also writes
  * z = FWHT(x)/d_in to z (fp32 [T][d_in], caller-owned, 16-byte aligned),

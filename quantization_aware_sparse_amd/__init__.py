@@ -22,7 +22,7 @@ __all__ = [
     "QWHA_SELECT_MAGNITUDE", "QWHA_SELECT_RANDOM",
     "qwha_init_select", "qwha_init_select_global", "qwha_hessian",
     "qwha_init_select_calibrated", "qwha_refine_values", "qwha_merge", "qwha_layer_fwd",
-    "qwha_materialize", "qwha_fwd", "qwha_bwd",
+    "qwha_materialize", "qwha_fwd", "qwha_fwd_noalloc", "qwha_bwd",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
@@ -238,6 +238,22 @@ def qwha_fwd(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
     check(lib.qwha_fwd(_ptr(x), _dt(x), T, d_in, d_out, p, _ptr(row_ptr), E.data_ptr(),
                        c.data_ptr(), float(alpha), _ptr(y), int(accumulate), ws.data_ptr(),
                        ws.numel(), _stream()), "qwha_fwd")
+    return y
+
+
+def qwha_fwd_noalloc(x: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
+                     y: Optional[torch.Tensor] = None,
+                     accumulate: bool = False) -> torch.Tensor:
+    """qwha_fwd with the library's static device scratch as its workspace
+    (the call allocates nothing on the device; y is allocated here only when
+    not given)."""
+    T, d_in = x.shape
+    p = int(c.numel())
+    if y is None:
+        y = torch.empty((T, d_out), dtype=x.dtype, device=x.device)
+    check(lib.qwha_fwd_noalloc(_ptr(x), _dt(x), T, d_in, d_out, p, _ptr(row_ptr), E.data_ptr(),
+                               c.data_ptr(), float(alpha), _ptr(y), int(accumulate), _stream()),
+          "qwha_fwd_noalloc")
     return y
 
 

@@ -4,10 +4,21 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/qwha.h"
 #include "launch.h"
 
 using namespace qwha;
+
+// Device memory of qwha_fwd_noalloc, for callers that cannot allocate: the
+// forward's workspace (z and the prepared stream) lives here instead of in a
+// caller buffer. Each GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` is only a stand-in for the symbol;
+// its device address comes from hipGetSymbolAddress (scratch_address).
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 
 namespace {
 
@@ -171,6 +182,40 @@ BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p, bool with_dc) {
 }
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+qwha_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QWHA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QWHA_ERR_HIP, "device %d outside the %d the static scratch serves", dev,
+                kMaxDevices);
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess)
+      return fail(QWHA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(QWHA_ERR_INVALID_ARG,
+                  "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(QWHA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QWHA_OK;
+}
 
 }  // namespace
 
@@ -566,11 +611,12 @@ size_t qwha_fwd_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int64_t 
 namespace {
 
 // qwha_fwd; with z_out, z = FWHT(x)/n goes there (kept for the backward)
-// instead of into the workspace.
+// instead of into the workspace. With use_scratch, the workspace is the
+// static `scratch` array (workspace and workspace_bytes are ignored).
 qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
                      int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
                      float alpha, void* y, int32_t accumulate, float* z_out, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+                     size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
   g_err[0] = 0;
   int log_n;
   int nblk;
@@ -590,6 +636,15 @@ qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
   QWHA_NEED(x, 16);
   QWHA_NEED(y, 16);
   const FwdWs l = fwd_ws(T, d_in, d_out, p);
+  if (use_scratch) {
+    if (l.total > kScratchBytes)
+      return fail(QWHA_ERR_WORKSPACE,
+                  "this forward needs %zu bytes of workspace; the static scratch of "
+                  "qwha_fwd_noalloc holds %zu (use qwha_fwd with a caller workspace)",
+                  l.total, kScratchBytes);
+    QWHA_TRY(scratch_address(stream, &workspace));
+    workspace_bytes = kScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < l.total)
     return fail(QWHA_ERR_WORKSPACE, "fwd workspace needs %zu bytes", l.total);
   QWHA_NEED(workspace, 256);
@@ -624,6 +679,14 @@ qwha_status qwha_fwd(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
                      size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(x, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, nullptr,
                   workspace, workspace_bytes, stream);
+}
+
+qwha_status qwha_fwd_noalloc(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
+                             int32_t d_out, int64_t p, const int32_t* row_ptr, const int32_t* E,
+                             const float* c, float alpha, void* y, int32_t accumulate,
+                             hipStream_t stream) {
+  return fwd_impl(x, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, nullptr,
+                  nullptr, 0, stream, true);
 }
 
 qwha_status qwha_fwd_save(const void* x, qwha_dtype act, int64_t T, int32_t d_in,

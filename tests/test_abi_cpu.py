@@ -95,6 +95,33 @@ def test_fwd_validation(q):
     assert _fwd(q, T=-3) == SHAPE
 
 
+def _fwd_noalloc(q, **kw):
+    a = dict(x=FAKE, act=1, T=16, d_in=256, d_out=256, p=2048, row_ptr=FAKE, E=FAKE, c=FAKE,
+             alpha=1.0, y=FAKE, acc=0, stream=None)
+    a.update(kw)
+    return q.qwha_fwd_noalloc(a["x"], a["act"], a["T"], a["d_in"], a["d_out"], a["p"],
+                              a["row_ptr"], a["E"], a["c"], a["alpha"], a["y"], a["acc"],
+                              a["stream"])
+
+
+def test_fwd_noalloc_validation(q):
+    # the same argument checks as qwha_fwd, all before any HIP call
+    assert _fwd_noalloc(q, d_in=12) == SHAPE
+    assert _fwd_noalloc(q, act=7) == DTYPE
+    assert _fwd_noalloc(q, p=256 * 256 + 1) == BUDGET
+    assert _fwd_noalloc(q, x=None) == INVALID
+    assert _fwd_noalloc(q, y=FAKE + 4) == ALIGN
+    assert _fwd_noalloc(q, T=0) == OK                       # nothing to do, nothing touched
+    # a forward whose workspace exceeds the 64 MiB static scratch is refused
+    # on the host, with the sizes in the message
+    need = q.qwha_fwd_workspace_bytes(8192, 4096, 4096, 524288)
+    assert need > 64 << 20
+    assert _fwd_noalloc(q, T=8192, d_in=4096, d_out=4096, p=524288) == WORKSPACE
+    msg = q.qwha_last_error()
+    assert b"static scratch" in msg and str(need).encode() in msg
+    assert q.qwha_fwd_workspace_bytes(3200, 4096, 4096, 524288) <= 64 << 20
+
+
 def test_stream_position_limit(q):
     # the SpMM stream holds at most 2p + 16 entries at int32 positions: p is
     # capped at (2^31 - 65) // 2 for the calls that build it
