@@ -1,7 +1,8 @@
 """Throughput of the Walsh-Hadamard adapter hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch, every kernel in
-the library's HIP code, on torch's current stream:
+the library's HIP code, on torch's current stream, for every adapter of the
+workload:
   init (row norms, AdaAlloc budgets, fp64 transform + in-row top-k, column
   index) -> materialize dW -> forward (FWHT(x), gather-SpMM; z = FWHT(x)/n
   kept as the saved activation) -> backward (gather-SpMM dz and dc partials
@@ -9,10 +10,16 @@ the library's HIP code, on torch's current stream:
   c += 1e-3 sign(dc) -> re-materialize dW.
 value = tokens per second of that step (T / step time), inputs resident in HBM.
 
-Workload (default): the 4096x4096 q_proj-shaped layer, 4-bit RTN (group 128)
-error with 0.1% x20 outliers, budget p = 524288 (rank-64 LoRA parameter
-count), 8192 bf16 tokens. Four copies of the inputs are rotated so the
-working set exceeds the 256 MB Infinity Cache.
+Workload (default --config c2): the 4096x4096 q_proj-shaped layer, 4-bit
+RTN (group 128) error with 0.1% x20 outliers, budget p = 524288 (rank-64
+LoRA parameter count), 8192 bf16 tokens. The further workloads (--configs,
+default c3, c4, c5) are measured after it in the same run, each with its own
+step, kernel table, dominant-kernel roofline and oracle baseline: the
+14336x4096 up_proj layer (3-bit), the 8192x8192 layer (2-bit, 16384 tokens)
+and the GQA attention block (q/o 4096x4096, k/v 1024x4096, 32768 tokens),
+whose q, k and v adapters share one FWHT(x) in the forward and one
+FWHT(dz_q + dz_k + dz_v) in the backward. Four copies of the inputs are
+rotated so the working set exceeds the 256 MB Infinity Cache.
 
 Per-kernel times come from HIP events recorded by the library around each
 kernel launch (qwha_profile_next), on the launch stream, over the timed steps.
@@ -61,6 +68,11 @@ def parse():
                     help="timed calls of each init selection strategy (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: all of the workload's)")
+    ap.add_argument("--configs", default="c3,c4,c5",
+                    help="further workloads measured after --config, each its own step "
+                         "('' for none)")
+    ap.add_argument("--extra-cpu-tokens", type=int, default=1024,
+                    help="tokens in the oracle's sample for the further workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain fp32 copy kernel of this size (read + write) after the "
                          "warmup, to calibrate HBM byte counters")
@@ -93,6 +105,279 @@ class HipEvents:
         return ms.value
 
 
+# kernel ids of the profiling hook (qwha.h qwha_kernel) by the step's calls
+CALL_KERNELS = {
+    "init": ["INIT_SELECT"],
+    "materialize": ["MATERIALIZE"],
+    "fwd_save": ["FWD_FWHT", "FWD_SPMM"],
+    "fwd_z": ["FWD_SPMM"],
+    "bwd_saved": ["BWD_SPMM", "BWD_FWHT_DX", "BWD_DC_REDUCE"],
+    "bwd_dz": ["BWD_SPMM", "BWD_DC_REDUCE"],
+    "fwht_dx": ["FWHT"],
+}
+KID = dict(K, FWHT=9)
+
+
+class Block:
+    """The device state of one workload: its adapters (one per projection),
+    grouped by the activation they read (q, k, v of the attention block read
+    one x; every other layer is a group of one), with `sets` rotated copies
+    of every input so the working set exceeds the Infinity Cache.
+
+    One step = the whole hot path over one batch: for every adapter the init
+    (row norms, AdaAlloc, fp64 transform + in-row top-k, column index) and
+    the materialisation of dW; per group the forward (one z = FWHT(x)/n for
+    the group, kept, then each adapter's gather-SpMM) and the backward (each
+    adapter's dz and dc against the kept z; one transform of the summed dz for
+    a shared group); then every adapter's c += 1e-3 sign(dc) and
+    re-materialisation."""
+
+    def __init__(self, cfg, nsets, dev, hip):
+        import numpy as np
+        import torch
+        import synth
+        from quantization_aware_sparse_amd import lib
+        self.cfg = cfg
+        self.specs = synth.config_specs(cfg)
+        self.hip = hip
+        self.dev = dev
+        t0 = time.perf_counter()
+        self.layers = [synth.make_layer(sp, seed=0) for sp in self.specs]
+        streams = {}
+        self.host_x, self.host_dy = [], []
+        for sp in self.specs:
+            xs = synth.C5_X_STREAM.get(sp.name) if cfg == "c5" else None
+            x, dy = synth.make_activations(sp, seed=0, x_stream=xs)
+            key = xs if xs is not None else sp.name
+            if key not in streams:
+                streams[key] = (len(streams), x)
+            self.host_x.append(streams[key][0])
+            self.host_dy.append(dy)
+        self.x_host = [None] * len(streams)
+        for key, (g, x) in streams.items():
+            self.x_host[g] = x
+        self.gen_s = time.perf_counter() - t0
+
+        def up(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        sp0 = self.specs[0]
+        self.T = sp0.T
+        self.act = sp0.act
+        self.act_code = 1 if sp0.act == "bf16" else 0
+        adt = torch.bfloat16 if sp0.act == "bf16" else torch.float32
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.groups = []
+        for g, x in enumerate(self.x_host):
+            xd = up(x)
+            members = [i for i, gi in enumerate(self.host_x) if gi == g]
+            d_in = x.shape[1]
+            grp = dict(members=members, d_in=d_in,
+                       x=[xd] + [xd.clone() for _ in range(nsets - 1)],
+                       z=torch.empty((self.T, d_in), dtype=torch.float32, device=dev),
+                       dx=torch.empty((self.T, d_in), dtype=adt, device=dev))
+            if len(members) > 1:
+                grp["dz"] = torch.empty((self.T, d_in), dtype=torch.float32, device=dev)
+            self.groups.append(grp)
+        self.ads = []
+        for i, (sp, L) in enumerate(zip(self.specs, self.layers)):
+            d_out, d_in, p, T = sp.d_out, sp.d_in, sp.p, sp.T
+            dwq = up(L.dwq)
+            dy = up(self.host_dy[i])
+            a = dict(spec=sp, name=sp.name,
+                     dwq=[dwq] + [dwq.clone() for _ in range(nsets - 1)],
+                     dy=[dy] + [dy.clone() for _ in range(nsets - 1)],
+                     row_ptr=torch.empty(d_out + 1, **i32), E=torch.empty((p, 2), **i32),
+                     c=torch.empty(p, dtype=torch.float32, device=dev),
+                     col_ptr=torch.empty(d_in + 1, **i32), perm=torch.empty(p, **i32),
+                     dW=torch.empty((d_out, d_in), dtype=torch.float32, device=dev),
+                     y=torch.empty((T, d_out), dtype=adt, device=dev),
+                     dc=torch.empty(p, dtype=torch.float32, device=dev))
+            a["ws_i"] = torch.empty(lib.qwha_init_workspace_bytes(d_out, d_in),
+                                    dtype=torch.uint8, device=dev)
+            a["ws_f"] = torch.empty(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p),
+                                    dtype=torch.uint8, device=dev)
+            a["ws_b"] = torch.empty(lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p),
+                                    dtype=torch.uint8, device=dev)
+            a["ev"] = {k: (hip.create(), hip.create()) for k in KID}
+            a["times"] = {k: [] for k in KID}
+            self.ads.append(a)
+        self.nsets = nsets
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def _arm(self, a, call, record):
+        from quantization_aware_sparse_amd import check, lib
+        if not record:
+            return
+        for k in CALL_KERNELS[call]:
+            check(lib.qwha_profile_next(KID[k], a["ev"][k][0], a["ev"][k][1]), "profile")
+            a["armed"].append(k)
+
+    def step(self, s, record=False):
+        from quantization_aware_sparse_amd import check, lib
+        st, A = self.stream, self.act_code
+        T = self.T
+        for a in self.ads:
+            a["armed"] = []
+        for a in self.ads:
+            sp = a["spec"]
+            self._arm(a, "init", record)
+            check(lib.qwha_init_select(a["dwq"][s % self.nsets].data_ptr(), sp.d_out, sp.d_in,
+                                       sp.p, 3, 1.0, a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                       a["c"].data_ptr(), a["col_ptr"].data_ptr(),
+                                       a["perm"].data_ptr(), a["ws_i"].data_ptr(),
+                                       a["ws_i"].numel(), st), "init")
+            self._arm(a, "materialize", record)
+            check(lib.qwha_materialize(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                       a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
+                                       a["dW"].data_ptr(), 0, st), "materialize")
+        for g in self.groups:
+            x = g["x"][s % self.nsets]
+            for n, i in enumerate(g["members"]):
+                a, sp = self.ads[i], self.ads[i]["spec"]
+                if n == 0:
+                    self._arm(a, "fwd_save", record)
+                    check(lib.qwha_fwd_save(x.data_ptr(), A, T, sp.d_in, sp.d_out, sp.p,
+                                            a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                            a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
+                                            g["z"].data_ptr(), a["ws_f"].data_ptr(),
+                                            a["ws_f"].numel(), st), "fwd")
+                else:
+                    self._arm(a, "fwd_z", record)
+                    check(lib.qwha_fwd_z(g["z"].data_ptr(), A, T, sp.d_in, sp.d_out, sp.p,
+                                         a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                         a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
+                                         a["ws_f"].data_ptr(), a["ws_f"].numel(), st), "fwd_z")
+        for g in self.groups:
+            if len(g["members"]) == 1:
+                a = self.ads[g["members"][0]]
+                sp = a["spec"]
+                self._arm(a, "bwd_saved", record)
+                check(lib.qwha_bwd_saved(g["z"].data_ptr(), a["dy"][s % self.nsets].data_ptr(),
+                                         A, T, sp.d_in, sp.d_out, sp.p, a["row_ptr"].data_ptr(),
+                                         a["E"].data_ptr(), a["c"].data_ptr(),
+                                         a["col_ptr"].data_ptr(), a["perm"].data_ptr(), 1.0,
+                                         g["dx"].data_ptr(), 0, a["dc"].data_ptr(),
+                                         a["ws_b"].data_ptr(), a["ws_b"].numel(), st), "bwd")
+                continue
+            for n, i in enumerate(g["members"]):
+                a, sp = self.ads[i], self.ads[i]["spec"]
+                self._arm(a, "bwd_dz", record)
+                check(lib.qwha_bwd_dz(g["z"].data_ptr(), a["dy"][s % self.nsets].data_ptr(), A,
+                                      T, sp.d_in, sp.d_out, sp.p, a["E"].data_ptr(),
+                                      a["c"].data_ptr(), a["col_ptr"].data_ptr(),
+                                      a["perm"].data_ptr(), 1.0, g["dz"].data_ptr(),
+                                      int(n > 0), a["dc"].data_ptr(), a["ws_b"].data_ptr(),
+                                      a["ws_b"].numel(), st), "bwd_dz")
+            a0 = self.ads[g["members"][0]]
+            self._arm(a0, "fwht_dx", record)
+            d_in = g["d_in"]
+            b = d_in & -d_in
+            check(lib.qwha_fwht(g["dz"].data_ptr(), 0, g["dx"].data_ptr(), A, T * (d_in // b), b,
+                                1.0 / b, st), "fwht dx")
+        for a in self.ads:
+            sp = a["spec"]
+            check(lib.qwha_sign_update(a["c"].data_ptr(), a["dc"].data_ptr(), sp.p, 1e-3, st),
+                  "update")
+            check(lib.qwha_materialize(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                       a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
+                                       a["dW"].data_ptr(), 0, st), "rematerialize")
+
+    def read_times(self):
+        for a in self.ads:
+            for k in a["armed"]:
+                a["times"][k].append(self.hip.elapsed_ms(*a["ev"][k]))
+
+
+def kernel_rates(sp, esz, times):
+    """Per kernel: average launch time and the achieved rate against its roof
+    (algorithmic bytes or flops per launch; SURVEY-style counts: each
+    activation once, E / c once, dW_Q once)."""
+    import numpy as np
+    d_out, d_in, p, T = sp.d_out, sp.d_in, sp.p, sp.T
+    nbytes = {
+        "FWD_FWHT": T * d_in * (esz + 4),
+        "BWD_FWHT_DX": T * d_in * (4 + esz),
+        "FWHT": T * d_in * (4 + esz),
+        "INIT_SELECT": d_out * d_in * 4 + p * 12 + (d_out + 1) * 4,
+        "MATERIALIZE": p * 12 + (d_out + 1) * 4 + d_out * d_in * 4,
+    }
+    flops = {"FWD_SPMM": 2.0 * T * p, "BWD_SPMM": 4.0 * T * p}
+    kern = {}
+    for k, v in times.items():
+        if not v:
+            continue
+        us = 1e3 * float(np.mean(v))
+        if k in flops:
+            a = flops[k] / (us * 1e-6) / 1e12
+            kern[k] = dict(avg_us=round(us, 2), bound="alu", achieved=round(a, 3),
+                           unit="TFLOP/s", peak=FP32_VECTOR_PEAK_TFLOPS,
+                           frac=round(a / FP32_VECTOR_PEAK_TFLOPS, 4))
+        elif k in nbytes:
+            a = nbytes[k] / (us * 1e-6) / 1e9
+            kern[k] = dict(avg_us=round(us, 2), bound="hbm", achieved=round(a, 1), unit="GB/s",
+                           peak=HBM_PEAK_GBS, frac=round(a / HBM_PEAK_GBS, 4))
+        else:
+            kern[k] = dict(avg_us=round(us, 2))
+    return kern
+
+
+def measure(block, steps, warmup, config_name):
+    """Warm up, time `steps` profiled steps (per-kernel HIP events, one host
+    wait per step) and then `steps` clean steps (no host waits): the clean
+    steps give the throughput."""
+    import torch
+    for s in range(warmup):
+        block.step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        block.step(s, True)
+        torch.cuda.synchronize()     # the next step re-arms the same events
+        block.read_times()
+    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(steps):
+        block.step(s, False)
+    torch.cuda.synchronize()
+    wall_clean = time.perf_counter() - t1
+    ms_step = 1e3 * wall_clean / steps
+    esz = 2 if block.act == "bf16" else 4
+    per = {a["name"]: kernel_rates(a["spec"], esz, a["times"]) for a in block.ads}
+    # the dominant kernel: the longest launch of any adapter
+    best = None
+    for name, kern in per.items():
+        for k, v in kern.items():
+            if best is None or v["avg_us"] > best[2]["avg_us"]:
+                best = (name, k, v)
+    name, k, v = best
+    roof = {kk: vv for kk, vv in v.items() if kk != "avg_us"}
+    roof["kernel"] = k if len(per) == 1 else f"{k} ({name})"
+    roof["avg_us"] = v["avg_us"]
+    roof["traffic"] = measured_traffic(k, config_name) if len(per) == 1 else None
+    return dict(value=round(block.T / (ms_step / 1e3), 1), ms_per_step=round(ms_step, 4),
+                profiled_steps_ms=round(1e3 * wall / steps, 4), roofline=roof,
+                kernels=per[block.ads[0]["name"]] if len(per) == 1 else per)
+
+
+def workload_text(block):
+    sps = block.specs
+    if len(sps) == 1:
+        sp = sps[0]
+        return (f"{sp.name}: {sp.d_out}x{sp.d_in} layer, {sp.bits}-bit RTN g{sp.group} error "
+                f"with {sp.outlier_frac:.1%} x{sp.outlier_mult:g} outliers, p={sp.p}, "
+                f"{sp.T} {sp.act} tokens; step = init + materialize + fwd + bwd + sign update "
+                "+ re-materialize")
+    parts = ", ".join(f"{sp.name.split('.')[-1]} {sp.d_out}x{sp.d_in} p={sp.p}" for sp in sps)
+    return (f"{block.cfg}: GQA attention block ({parts}), {sps[0].bits}-bit RTN "
+            f"g{sps[0].group}, {sps[0].T} {sps[0].act} tokens (16 x 2048); step = for all four "
+            "adapters init + materialize + fwd + bwd + sign update + re-materialize, q/k/v "
+            "sharing one FWHT(x) and one FWHT(dz_q + dz_k + dz_v)")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -104,82 +389,18 @@ def main():
     import numpy as np
     import torch
 
-    import synth
-    import quantization_aware_sparse_amd as q
-    from quantization_aware_sparse_amd import check, lib
+    import quantization_aware_sparse_amd as q  # noqa: F401  (fails loudly without the library)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    spec = synth.config_specs(args.config)[0]
-    d_out, d_in, p, T = spec.d_out, spec.d_in, spec.p, spec.T
-    act = q.QWHA_BF16 if spec.act == "bf16" else q.QWHA_F32
-    adt = torch.bfloat16 if spec.act == "bf16" else torch.float32
-    esz = 2 if spec.act == "bf16" else 4
-
-    t_gen = time.perf_counter()
-    layer = synth.make_layer(spec, seed=0)
-    x_np, dy_np = synth.make_activations(spec, seed=0)
-    gen_s = time.perf_counter() - t_gen
-
-    def up(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    sets = []
-    base = (up(layer.dwq), up(x_np), up(dy_np))
-    for s in range(args.sets):
-        sets.append(tuple(b.clone() for b in base))
-    del base
-
-    i32 = dict(dtype=torch.int32, device=dev)
-    row_ptr = torch.empty(d_out + 1, **i32)
-    E = torch.empty((p, 2), **i32)
-    c = torch.empty(p, dtype=torch.float32, device=dev)
-    col_ptr = torch.empty(d_in + 1, **i32)
-    perm = torch.empty(p, **i32)
-    dW = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
-    y = torch.empty((T, d_out), dtype=adt, device=dev)
-    dx = torch.empty((T, d_in), dtype=adt, device=dev)
-    dc = torch.empty(p, dtype=torch.float32, device=dev)
-    zsave = torch.empty((T, d_in), dtype=torch.float32, device=dev)   # saved activation
-    ws_i = torch.empty(lib.qwha_init_workspace_bytes(d_out, d_in), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
-                       device=dev)
-    ws_b = torch.empty(lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p), dtype=torch.uint8,
-                       device=dev)
-    stream = torch.cuda.current_stream().cuda_stream
-
     hip = HipEvents()
-    ev = {name: (hip.create(), hip.create()) for name in K}
-    times = {name: [] for name in K}
 
-    def step(s, record):
-        dwq, x, dy = sets[s % len(sets)]
-        if record:
-            for name, kid in K.items():
-                check(lib.qwha_profile_next(kid, ev[name][0], ev[name][1]), "profile")
-        check(lib.qwha_init_select(dwq.data_ptr(), d_out, d_in, p, 3, 1.0, row_ptr.data_ptr(),
-                                   E.data_ptr(), c.data_ptr(), col_ptr.data_ptr(),
-                                   perm.data_ptr(), ws_i.data_ptr(), ws_i.numel(), stream),
-              "init")
-        check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
-                                   p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "materialize")
-        check(lib.qwha_fwd_save(x.data_ptr(), act, T, d_in, d_out, p, row_ptr.data_ptr(),
-                                E.data_ptr(), c.data_ptr(), 1.0, y.data_ptr(), 0,
-                                zsave.data_ptr(), ws_f.data_ptr(), ws_f.numel(), stream), "fwd")
-        check(lib.qwha_bwd_saved(zsave.data_ptr(), dy.data_ptr(), act, T, d_in, d_out, p,
-                                 row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(),
-                                 col_ptr.data_ptr(), perm.data_ptr(), 1.0, dx.data_ptr(), 0,
-                                 dc.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream), "bwd")
-        check(lib.qwha_sign_update(c.data_ptr(), dc.data_ptr(), p, 1e-3, stream), "update")
-        check(lib.qwha_materialize(row_ptr.data_ptr(), E.data_ptr(), c.data_ptr(), d_out, d_in,
-                                   p, 1.0, q.QWHA_F32, dW.data_ptr(), 0, stream), "rematerialize")
-
-    for s in range(args.warmup):
-        step(s, False)
-    torch.cuda.synchronize()
+    block = Block(args.config, args.sets, dev, hip)
+    spec = block.specs[0]
     if args.calib_copy_mib > 0:
+        for s in range(args.warmup):
+            block.step(s, False)
+        torch.cuda.synchronize()
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -187,104 +408,77 @@ def main():
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         del a, b
-    print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
-          flush=True)
-
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(s, True)
-        # the next step's requests reuse these events: read them first
-        torch.cuda.synchronize()
-        for name in K:
-            times[name].append(hip.elapsed_ms(*ev[name]))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # clean timing without per-step host waits: the figure `value` reports
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for s in range(args.steps):
-        step(s, False)
-    torch.cuda.synchronize()
-    wall_clean = time.perf_counter() - t1
-    ms_step = 1e3 * wall_clean / args.steps
-    value = T / (ms_step / 1e3)
-
-    avg_us = {k: 1e3 * float(np.mean(v)) for k, v in times.items()}
-    # algorithmic work per launch
-    nbytes = {
-        "FWD_FWHT": T * d_in * (esz + 4),
-        "BWD_FWHT_DX": T * d_in * (4 + esz),
-        "INIT_SELECT": d_out * d_in * 4 + p * 12 + (d_out + 1) * 4,
-        "MATERIALIZE": p * 12 + (d_out + 1) * 4 + d_out * d_in * 4,
-        "BWD_DC_REDUCE": 0,
-    }
-    flops = {"FWD_SPMM": 2.0 * T * p, "BWD_SPMM": 4.0 * T * p}
-    kern = {}
-    for k, us in avg_us.items():
-        if k in flops:
-            a = flops[k] / (us * 1e-6) / 1e12
-            kern[k] = dict(avg_us=round(us, 2), bound="alu", achieved=round(a, 3),
-                           unit="TFLOP/s", peak=FP32_VECTOR_PEAK_TFLOPS,
-                           frac=round(a / FP32_VECTOR_PEAK_TFLOPS, 4))
-        elif nbytes.get(k):
-            a = nbytes[k] / (us * 1e-6) / 1e9
-            kern[k] = dict(avg_us=round(us, 2), bound="hbm", achieved=round(a, 1), unit="GB/s",
-                           peak=HBM_PEAK_GBS, frac=round(a / HBM_PEAK_GBS, 4))
-        else:
-            kern[k] = dict(avg_us=round(us, 2))
-    dom = max(avg_us, key=avg_us.get)
-    roof = dict(kern[dom])
-    roof.pop("avg_us", None)
-    roof["kernel"] = dom
-    roof["avg_us"] = round(avg_us[dom], 2)
-    roof["traffic"] = measured_traffic(dom, args.config)
-
-    fwd_bwd_us = sum(avg_us[k] for k in ("FWD_FWHT", "FWD_SPMM", "BWD_SPMM", "BWD_FWHT_DX",
-                                         "BWD_DC_REDUCE"))
+    print(f"# {args.config}: inputs ready; warmup {args.warmup}, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+    m = measure(block, args.steps, args.warmup, args.config)
+    kern = m["kernels"]
     out = {
         "metric": "adapter fwd+bwd tokens/s per layer; FWHT/gather achieved HBM GB/s vs peak",
-        "value": round(value, 1),
+        "value": m["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": block.act,
         "data": "synthetic",
         "config": {
-            "workload": f"{spec.name}: {d_out}x{d_in} layer, {spec.bits}-bit RTN g{spec.group} "
-                        f"error with {spec.outlier_frac:.1%} x{spec.outlier_mult:g} outliers, "
-                        f"p={p}, {T} {spec.act} tokens; step = init + materialize + fwd + bwd "
-                        "+ sign update + re-materialize",
-            "d_out": d_out, "d_in": d_in, "p": p, "tokens": T, "act": spec.act,
+            "workload": workload_text(block),
+            "d_out": spec.d_out, "d_in": spec.d_in, "p": spec.p, "tokens": spec.T,
+            "act": spec.act, "math": "f32 (fp64 init transform)",
             "input_sets_rotated": args.sets,
         },
-        "roofline": roof,
+        "roofline": m["roofline"],
         "kernels": kern,
-        "fwd_bwd_kernels_us": round(fwd_bwd_us, 2),
-        "fwd_bwd_tokens_per_s": round(T / (fwd_bwd_us * 1e-6), 1),
-        "profiled_steps_ms": round(1e3 * wall / args.steps, 4),
-        "input_gen_s": round(gen_s, 2),
+        "profiled_steps_ms": m["profiled_steps_ms"],
+        "input_gen_s": round(block.gen_s, 2),
     }
+    if len(block.ads) == 1:
+        fb = ("FWD_FWHT", "FWD_SPMM", "BWD_SPMM", "BWD_FWHT_DX", "BWD_DC_REDUCE")
+        fwd_bwd_us = sum(kern[k]["avg_us"] for k in fb if k in kern)
+        out["fwd_bwd_kernels_us"] = round(fwd_bwd_us, 2)
+        out["fwd_bwd_tokens_per_s"] = round(spec.T / (fwd_bwd_us * 1e-6), 1)
 
-    if args.variant_reps > 0:
-        out["init_variants"] = init_variants(args.variant_reps, sets, (d_out, d_in, p),
-                                             (row_ptr, E, c, col_ptr, perm), ws_i, stream, hip)
-
-    if args.base_reps > 0:
-        out["base_layer"] = base_layer_measure(args.base_reps, spec, layer, sets,
-                                               (row_ptr, E, c), stream, hip)
-
-    if args.refine_tokens > 0 and args.refine_reps > 0:
+    a0 = block.ads[0]
+    sets = [(a0["dwq"][s], block.groups[0]["x"][s], a0["dy"][s]) for s in range(args.sets)]
+    stream = block.stream
+    if args.variant_reps > 0 and len(block.ads) == 1:
+        out["init_variants"] = init_variants(args.variant_reps, sets,
+                                             (spec.d_out, spec.d_in, spec.p),
+                                             (a0["row_ptr"], a0["E"], a0["c"], a0["col_ptr"],
+                                              a0["perm"]), a0["ws_i"], stream, hip)
+    if args.base_reps > 0 and len(block.ads) == 1:
+        out["base_layer"] = base_layer_measure(args.base_reps, spec, block.layers[0], sets,
+                                               (a0["row_ptr"], a0["E"], a0["c"]), stream, hip)
+    if args.refine_tokens > 0 and args.refine_reps > 0 and len(block.ads) == 1:
         out["refine"] = refine_measure(args.refine_tokens, args.refine_reps, spec, sets[0][0],
                                        stream, hip)
-
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, layer, x_np, dy_np, args.cpu_tokens or T)
+        out["cpu_baseline"] = cpu_baseline(block, args.cpu_tokens or spec.T)
+
+    # the other workloads of the configuration list, each its own step
+    extra = [c for c in args.configs.split(",") if c and c != args.config]
+    if extra:
+        del block, sets, a0
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        for cfg in extra:
+            blk = Block(cfg, args.sets, dev, hip)
+            print(f"# {cfg}: inputs ready; warmup {args.warmup}, timing {args.steps} steps",
+                  file=sys.stderr, flush=True)
+            mm = measure(blk, args.steps, args.warmup, cfg)
+            entry = dict(workload=workload_text(blk), unit="tokens/s", value=mm["value"],
+                         ms_per_step=mm["ms_per_step"], dtype=blk.act, roofline=mm["roofline"],
+                         kernels=mm["kernels"], input_gen_s=round(blk.gen_s, 2))
+            if not args.no_cpu_baseline:
+                entry["cpu_baseline"] = cpu_baseline(blk, min(args.extra_cpu_tokens, blk.T),
+                                                     min_seconds=1.0)
+            out["configs"][cfg] = entry
+            del blk
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
@@ -504,7 +698,8 @@ def refine_measure(N, reps, spec, dwq, stream, hip):
 # and the launch layer, which every kernel depends on)
 KERNEL_SOURCES = {
     "FWD_FWHT": ["fwht.hip", "fwht_core.h"], "BWD_FWHT_X": ["fwht.hip", "fwht_core.h"],
-    "BWD_FWHT_DX": ["fwht.hip", "fwht_core.h"], "FWD_SPMM": ["spmm.hip"],
+    "BWD_FWHT_DX": ["fwht.hip", "fwht_core.h"], "FWHT": ["fwht.hip", "fwht_core.h"],
+    "FWD_SPMM": ["spmm.hip"],
     "BWD_SPMM": ["spmm.hip"], "BWD_DC_REDUCE": ["spmm.hip"],
     "INIT_SELECT": ["init.hip", "fwht_core.h"], "MATERIALIZE": ["materialize.hip", "fwht_core.h"],
     "GLOBAL_THRESHOLD": ["select_global.hip", "fwht_core.h"],
@@ -569,13 +764,12 @@ def measured_traffic(kernel, config):
     return None
 
 
-def cpu_baseline(spec, layer, x_np, dy_np, n_tok, min_seconds=10.0):
+def cpu_baseline(block, n_tok, min_seconds=10.0):
     """The fp64 oracle (as it stands) on the host cores: whole steps of the
-    same path (init, materialize, fwd, bwd, update, re-materialize) on the
-    full layer with n_tok of the workload's tokens, repeated until at least
-    min_seconds have passed. With n_tok < T the fwd+bwd share is scaled
-    linearly to T tokens."""
-    import numpy as np
+    same path for every adapter of the workload (init, materialize, fwd, bwd,
+    update, re-materialize) on the full layers with n_tok of the workload's
+    tokens, repeated until at least min_seconds have passed. With n_tok < T
+    the fwd+bwd share is scaled linearly to T tokens."""
     import oracle as O
     import synth
     cores = len(os.sched_getaffinity(0))
@@ -584,39 +778,44 @@ def cpu_baseline(spec, layer, x_np, dy_np, n_tok, min_seconds=10.0):
         limiter = threadpool_limits(limits=cores)
     except Exception:  # noqa: BLE001
         threadpool_info = limiter = None
-    n_tok = min(n_tok, spec.T)
-    x = synth.act_to_f64(x_np[:n_tok])
-    dy = synth.act_to_f64(dy_np[:n_tok])
+    T = block.T
+    n_tok = min(n_tok, T)
+    xs = [synth.act_to_f64(x[:n_tok]) for x in block.x_host]
+    dys = [synth.act_to_f64(dy[:n_tok]) for dy in block.host_dy]
     fixed, tok, reps = 0.0, 0.0, 0
     t_start = time.perf_counter()
     while reps == 0 or time.perf_counter() - t_start < min_seconds:
-        t0 = time.perf_counter()
-        r = O.init_select(layer.dwq, spec.p, m=3)
-        dW = O.materialize(r["E"], r["c"], spec.d_out, spec.d_in, 1.0)
-        t1 = time.perf_counter()
-        O.forward(x, dW)
-        _, dc = O.backward(x, dy, r["E"], r["c"], spec.d_out, spec.d_in, 1.0, dW=dW)
-        t2 = time.perf_counter()
-        c2 = O.sign_update(r["c"], dc)
-        O.materialize(r["E"], c2, spec.d_out, spec.d_in, 1.0)
-        t3 = time.perf_counter()
-        fixed += (t1 - t0) + (t3 - t2)
-        tok += t2 - t1
+        for i, (sp, L) in enumerate(zip(block.specs, block.layers)):
+            x, dy = xs[block.host_x[i]], dys[i]
+            t0 = time.perf_counter()
+            r = O.init_select(L.dwq, sp.p, m=3)
+            dW = O.materialize(r["E"], r["c"], sp.d_out, sp.d_in, 1.0)
+            t1 = time.perf_counter()
+            O.forward(x, dW)
+            _, dc = O.backward(x, dy, r["E"], r["c"], sp.d_out, sp.d_in, 1.0, dW=dW)
+            t2 = time.perf_counter()
+            c2 = O.sign_update(r["c"], dc)
+            O.materialize(r["E"], c2, sp.d_out, sp.d_in, 1.0)
+            t3 = time.perf_counter()
+            fixed += (t1 - t0) + (t3 - t2)
+            tok += t2 - t1
         reps += 1
     sec = time.perf_counter() - t_start
     fixed /= reps
     tok /= reps
-    step_s = fixed + tok * spec.T / n_tok
+    step_s = fixed + tok * T / n_tok
     threads = cores
     if threadpool_info is not None:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
     del limiter
-    scaled = "" if n_tok == spec.T else f", scaled to {spec.T} tokens"
-    return {"value": round(spec.T / step_s, 2), "unit": "tokens/s", "cores": int(threads),
+    scaled = "" if n_tok == T else f", scaled to {T} tokens"
+    what = (f"the full {block.specs[0].d_out}x{block.specs[0].d_in} layer"
+            if len(block.specs) == 1 else f"all {len(block.specs)} full layers")
+    return {"value": round(T / step_s, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{reps} oracle step(s) on the full {spec.d_out}x{spec.d_in} layer with "
-                      f"{n_tok} of {spec.T} tokens ({sec:.1f} s): init + materialize + update + "
-                      f"re-materialize {fixed:.2f} s, fwd + bwd {tok:.2f} s per step{scaled}"}
+            "sample": f"{reps} oracle step(s) on {what} with {n_tok} of {T} tokens "
+                      f"({sec:.1f} s): init + materialize + update + re-materialize "
+                      f"{fixed:.2f} s, fwd + bwd {tok:.2f} s per step{scaled}"}
 
 
 if __name__ == "__main__":

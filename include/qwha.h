@@ -202,6 +202,34 @@ qwha_status qwha_bwd_saved(const float* z, const void* dy, qwha_dtype act, int64
                            size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Adapters that read the same input (the q, k and v projections of an
+ * attention block read the same x): the transform is linear and acts along
+ * d_in only (papernotes.org, 方法详解 › 整体框架; gist.science §2.1), so
+ * one z = FWHT(x)/d_in serves every adapter's forward and dc, and one
+ * transform of the summed dz gives the summed dx:
+ *   dx_q + dx_k + dx_v = FWHT(alpha_q dy_q F_q + alpha_k dy_k F_k
+ *                             + alpha_v dy_v F_v) / d_in.
+ * qwha_fwd_z:  y (+)= alpha z F^T from a z kept by qwha_fwd_save (fp32
+ *   [T][d_in]); y in `act`. Workspace: qwha_fwd_workspace_bytes(...) bytes
+ *   suffice (only the prepared stream is used).
+ * qwha_bwd_dz: dz (+)= alpha dy F into the caller's fp32 dz [T][d_in]
+ *   (accumulate_dz = 1 adds to it), and, when dc is not NULL, dc as in
+ *   qwha_bwd from the kept z. No transform runs: dx = FWHT(dz)/d_in is then
+ *   one qwha_fwht call with scale 1/d_in (rows T*m and n = b for a
+ *   block-diagonal width). Workspace: qwha_bwd_workspace_bytes(...) bytes
+ *   suffice (the prepared stream and the dc partials only are used).
+ * --------------------------------------------------------------------------- */
+qwha_status qwha_fwd_z(const float* z, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+                       int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
+                       float alpha, void* y, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                        int32_t d_in, int32_t d_out, int64_t p, const int32_t* E, const float* c,
+                        const int32_t* col_ptr, const int32_t* csc_perm, float alpha, float* dz,
+                        int32_t accumulate_dz, float* dc, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Coefficient update of the attention-block training step:
  *   c[k] += step * sign(dc[k])   (sign(0) = 0), fp32, in place.
  * --------------------------------------------------------------------------- */

@@ -22,7 +22,8 @@ __all__ = [
     "QWHA_SELECT_MAGNITUDE", "QWHA_SELECT_RANDOM",
     "qwha_init_select", "qwha_init_select_global", "qwha_hessian",
     "qwha_init_select_calibrated", "qwha_refine_values", "qwha_merge", "qwha_layer_fwd",
-    "qwha_materialize", "qwha_fwd", "qwha_fwd_noalloc", "qwha_bwd",
+    "qwha_materialize", "qwha_fwd", "qwha_fwd_noalloc", "qwha_fwd_z", "qwha_bwd",
+    "qwha_bwd_dz",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
@@ -291,6 +292,49 @@ def qwha_bwd(x: Optional[torch.Tensor], dy: torch.Tensor, row_ptr, E, c, col_ptr
                        dc.data_ptr() if dc is not None else None,
                        ws.data_ptr(), ws.numel(), _stream()), "qwha_bwd")
     return dx, dc
+
+
+def qwha_fwd_z(z: torch.Tensor, d_out: int, row_ptr, E, c, alpha: float = 1.0,
+               act=torch.bfloat16, y: Optional[torch.Tensor] = None, accumulate: bool = False,
+               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y (+)= alpha z F^T from a kept z = FWHT(x)/n (fp32 [T][d_in]), y in `act`."""
+    T, d_in = z.shape
+    p = int(c.numel())
+    if y is None:
+        y = torch.empty((T, d_out), dtype=act, device=z.device)
+    if ws is None:
+        ws = workspace(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p), z.device)
+    check(lib.qwha_fwd_z(_ptr(z), _dt(y), T, d_in, d_out, p, _ptr(row_ptr), E.data_ptr(),
+                         c.data_ptr(), float(alpha), _ptr(y), int(accumulate), ws.data_ptr(),
+                         ws.numel(), _stream()), "qwha_fwd_z")
+    return y
+
+
+def qwha_bwd_dz(z: Optional[torch.Tensor], dy: torch.Tensor, E, c, col_ptr, csc_perm,
+                alpha: float = 1.0, dz: Optional[torch.Tensor] = None,
+                accumulate_dz: bool = False, need_dc: bool = True,
+                dc: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                d_in: Optional[int] = None):
+    """dz (+)= alpha dy F (fp32 [T][d_in]) and dc from the kept z; no transform
+    (dx = FWHT(dz)/n is a qwha_fwht call)."""
+    T, d_out = dy.shape
+    if d_in is None:
+        d_in = (z if z is not None else dz).shape[1]
+    p = int(c.numel())
+    if dz is None:
+        dz = torch.empty((T, d_in), dtype=torch.float32, device=dy.device)
+    if need_dc and dc is None:
+        dc = torch.empty(max(p, 1), dtype=torch.float32, device=dy.device)[:p]
+    if not need_dc:
+        dc = None
+    if ws is None:
+        ws = workspace(lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p), dy.device)
+    check(lib.qwha_bwd_dz(_ptr(z), _ptr(dy), _dt(dy), T, d_in, d_out, p, E.data_ptr(),
+                          c.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(), float(alpha),
+                          _ptr(dz), int(accumulate_dz),
+                          dc.data_ptr() if dc is not None else None, ws.data_ptr(), ws.numel(),
+                          _stream()), "qwha_bwd_dz")
+    return dz, dc
 
 
 # ---------------------------------------------------------------- update, fwht

@@ -61,6 +61,12 @@ SIGNATURES = {
     "qwha_fwd_noalloc": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
                                    c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
                                    c_void_p]),
+    "qwha_fwd_z": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
+                             c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
+                             c_void_p, c_size_t, c_void_p]),
+    "qwha_bwd_dz": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                              c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "qwha_fwd_save": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
                                 c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),

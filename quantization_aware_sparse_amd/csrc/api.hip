@@ -19,7 +19,6 @@ using namespace qwha;
 constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-
 namespace {
 
 thread_local char g_err[512] = {0};
@@ -613,10 +612,13 @@ namespace {
 // qwha_fwd; with z_out, z = FWHT(x)/n goes there (kept for the backward)
 // instead of into the workspace. With use_scratch, the workspace is the
 // static `scratch` array (workspace and workspace_bytes are ignored).
+// With z_in (a transform kept by an earlier forward), x is not read and no
+// transform runs.
 qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
                      int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
                      float alpha, void* y, int32_t accumulate, float* z_out, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
+                     size_t workspace_bytes, hipStream_t stream, bool use_scratch = false,
+                     const float* z_in = nullptr) {
   g_err[0] = 0;
   int log_n;
   int nblk;
@@ -633,9 +635,16 @@ qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
     QWHA_NEED(c, 4);
   }
   if (T == 0) return QWHA_OK;
-  QWHA_NEED(x, 16);
+  if (z_in != nullptr)
+    QWHA_NEED(z_in, 16);
+  else
+    QWHA_NEED(x, 16);
   QWHA_NEED(y, 16);
-  const FwdWs l = fwd_ws(T, d_in, d_out, p);
+  FwdWs l = fwd_ws(T, d_in, d_out, p);
+  if (z_in != nullptr) {   // no transform: the workspace holds the prepared stream only
+    l.total -= l.prep;
+    l.prep = 0;
+  }
   if (use_scratch) {
     if (l.total > kScratchBytes)
       return fail(QWHA_ERR_WORKSPACE,
@@ -650,15 +659,20 @@ qwha_status fwd_impl(const void* x, qwha_dtype act, int64_t T, int32_t d_in, int
   QWHA_NEED(workspace, 256);
 
   if (z_out != nullptr) QWHA_NEED(z_out, 16);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(at(workspace, l.z));
+  const float* z = z_in;
   void* prep = at(workspace, l.prep);
   const Dt adt = static_cast<Dt>(act);
-  QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
-                           [&] {
-                             return launch_fwht(x, adt, z, Dt::F32, T * nblk, log_n,
-                                                1.0f / static_cast<float>(1 << log_n), 0, stream);
-                           }),
-                     "fwd fwht"));
+  if (z_in == nullptr) {
+    float* zw = z_out ? z_out : reinterpret_cast<float*>(at(workspace, l.z));
+    z = zw;
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
+                             [&] {
+                               return launch_fwht(x, adt, zw, Dt::F32, T * nblk, log_n,
+                                                  1.0f / static_cast<float>(1 << log_n), 0,
+                                                  stream);
+                             }),
+                       "fwd fwht"));
+  }
   QWHA_TRY(hip_check(launch_prep_csr(row_ptr, E, c, d_out, p, l.plan, prep, stream), "fwd prep"));
   QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_SPMM, stream,
                            [&] {
@@ -687,6 +701,16 @@ qwha_status qwha_fwd_noalloc(const void* x, qwha_dtype act, int64_t T, int32_t d
                              hipStream_t stream) {
   return fwd_impl(x, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, nullptr,
                   nullptr, 0, stream, true);
+}
+
+qwha_status qwha_fwd_z(const float* z, qwha_dtype act, int64_t T, int32_t d_in, int32_t d_out,
+                       int64_t p, const int32_t* row_ptr, const int32_t* E, const float* c,
+                       float alpha, void* y, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (z == nullptr && T > 0) return fail(QWHA_ERR_INVALID_ARG, "z is NULL");
+  return fwd_impl(nullptr, act, T, d_in, d_out, p, row_ptr, E, c, alpha, y, accumulate, nullptr,
+                  workspace, workspace_bytes, stream, false, z);
 }
 
 qwha_status qwha_fwd_save(const void* x, qwha_dtype act, int64_t T, int32_t d_in,
@@ -823,6 +847,71 @@ qwha_status qwha_bwd_saved(const float* z, const void* dy, qwha_dtype act, int64
   if (z == nullptr && T > 0 && dc != nullptr) return fail(QWHA_ERR_INVALID_ARG, "z is NULL");
   return bwd_impl(nullptr, z, dy, act, T, d_in, d_out, p, row_ptr, E, c, col_ptr, csc_perm,
                   alpha, dx, accumulate_dx, dc, workspace, workspace_bytes, stream);
+}
+
+qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                        int32_t d_in, int32_t d_out, int64_t p, const int32_t* E, const float* c,
+                        const int32_t* col_ptr, const int32_t* csc_perm, float alpha, float* dz,
+                        int32_t accumulate_dz, float* dc, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
+  QWHA_TRY(check_dt(act, "act"));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate_dz != 0 && accumulate_dz != 1)
+    return fail(QWHA_ERR_INVALID_ARG, "accumulate_dz must be 0/1");
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(c, 4);
+    QWHA_NEED(csc_perm, 4);
+  }
+  QWHA_NEED(col_ptr, 4);
+  if (dz == nullptr) return fail(QWHA_ERR_INVALID_ARG, "dz is NULL");
+  if (dc != nullptr && !aligned(dc, 4)) return fail(QWHA_ERR_ALIGN, "dc is not 4-byte aligned");
+  if (T == 0) {
+    if (dc != nullptr && p > 0)
+      return hip_check(launch_dc_reduce(nullptr, 0, p, csc_perm, alpha, dc, stream), "dc zero");
+    return QWHA_OK;
+  }
+  QWHA_NEED(dz, 16);
+  QWHA_NEED(dy, 16);
+  if (dc != nullptr) QWHA_NEED(z, 16);
+  // z and dz belong to the caller: the workspace holds the prepared stream
+  // and the dc partials only
+  BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr);
+  l.total -= l.prep;
+  l.partial -= l.prep;
+  l.prep = 0;
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", l.total);
+  QWHA_NEED(workspace, 256);
+
+  void* prep = at(workspace, l.prep);
+  float* partial = dc ? reinterpret_cast<float*>(at(workspace, l.partial)) : nullptr;
+  const Dt adt = static_cast<Dt>(act);
+  QWHA_TRY(hip_check(launch_prep_csc(col_ptr, csc_perm, E, c, d_in, p, l.plan, prep, stream),
+                     "bwd prep"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_SPMM, stream,
+                           [&] {
+                             return launch_spmm(dy, adt, T, d_out, prep, p, d_in, l.plan, alpha,
+                                                dz, Dt::F32, accumulate_dz, dc ? z : nullptr,
+                                                partial, stream);
+                           }),
+                     "bwd spmm"));
+  if (dc)
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_DC_REDUCE, stream,
+                             [&] {
+                               return launch_dc_reduce(partial, l.plan.ntiles, p,
+                                                       spmm_prep_korig(prep, p, d_in, l.plan),
+                                                       alpha, dc, stream);
+                             }),
+                       "dc reduce"));
+  return QWHA_OK;
 }
 
 // ------------------------------------------------------------------ update

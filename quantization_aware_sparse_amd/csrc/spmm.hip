@@ -755,7 +755,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     const SrcT* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
     int ptr_stride, int nblk, float* __restrict__ out, const float* __restrict__ zsrc,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, float alpha, int accumulate) {
   __shared__ float stage[2][kRJB * kRT];
   __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + the entries read past the end
   __shared__ int segs[2][kRW * kRRdc + 1];
@@ -853,8 +853,14 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
         const int tt = task / (kRW * kRRdc / 4);
         const int c4 = task % (kRW * kRRdc / 4);
         const float* e = ep + tt * kEp + 4 * c4;
-        *reinterpret_cast<float4*>(out + (t0 + (kRT / 2) * h + tt) * n_out + rg0 + 4 * c4) =
-            make_float4(e[0], e[1], e[2], e[3]);
+        float4* d = reinterpret_cast<float4*>(out + (t0 + (kRT / 2) * h + tt) * n_out + rg0 +
+                                              4 * c4);
+        float4 v = make_float4(alpha * e[0], alpha * e[1], alpha * e[2], alpha * e[3]);
+        if (accumulate) {
+          const float4 a = *d;
+          v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+        }
+        *d = v;
       }
     }
     return;
@@ -867,12 +873,21 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     float* dst = out + t * n_out;
     if (vec) {
       float4* d = reinterpret_cast<float4*>(dst + row0);
-      d[0] = make_float4(acc[0][q], acc[1][q], acc[2][q], acc[3][q]);
-      d[1] = make_float4(acc[4][q], acc[5][q], acc[6][q], acc[7][q]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float4 v = make_float4(alpha * acc[4 * h][q], alpha * acc[4 * h + 1][q],
+                               alpha * acc[4 * h + 2][q], alpha * acc[4 * h + 3][q]);
+        if (accumulate) {
+          const float4 a = d[h];
+          v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+        }
+        d[h] = v;
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < kRRdc; ++r)
-        if (row0 + r < n_out) dst[row0 + r] = acc[r][q];
+        if (row0 + r < n_out)
+          dst[row0 + r] = alpha * acc[r][q] + (accumulate ? dst[row0 + r] : 0.f);
     }
   }
 }
@@ -880,7 +895,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
 template <typename SrcT>
 static hipError_t rows_dc_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                             int n_out, const SpmmPlan& pl, void* out, const float* zsrc,
-                            float* partial, hipStream_t s) {
+                            float* partial, float alpha, int accumulate, hipStream_t s) {
   const int gy = (n_out + pl.rows_wg - 1) / pl.rows_wg;
   void* pp = const_cast<void*>(prep);
   const PrepLayout l = prep_layout(nnz, n_out, pl);
@@ -891,12 +906,14 @@ static hipError_t rows_dc_t(const void* src, int64_t T, int n_src, const void* p
     hipLaunchKernelGGL((rows_dc_kernel<SrcT, true>), grid, dim3(kRW * 64), 0, s,
                        static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
                        at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
-                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial);
+                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial, alpha,
+                       accumulate);
   else
     hipLaunchKernelGGL((rows_dc_kernel<SrcT, false>), grid, dim3(kRW * 64), 0, s,
                        static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),
                        at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
-                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial);
+                       pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial, alpha,
+                       accumulate);
   return hipGetLastError();
 }
 
@@ -929,13 +946,13 @@ hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const v
                        hipStream_t s) {
   if (pl.ntiles == 0) return hipSuccess;
   if (pl.kind == 2) {
-    // dz (unscaled, overwritten) and the dc partials
-    if (partial == nullptr || zsrc == nullptr || out_dt != Dt::F32 || accumulate ||
-        alpha != 1.0f)
-      return hipErrorInvalidValue;
+    // dz = alpha dy F (+ dz when accumulate, fp32) and the dc partials
+    if (partial == nullptr || zsrc == nullptr || out_dt != Dt::F32) return hipErrorInvalidValue;
     return src_dt == Dt::F32
-               ? rows_dc_t<float>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s)
-               : rows_dc_t<uint16_t>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, s);
+               ? rows_dc_t<float>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial, alpha,
+                                  accumulate, s)
+               : rows_dc_t<uint16_t>(src, T, n_src, prep, nnz, n_out, pl, out, zsrc, partial,
+                                     alpha, accumulate, s);
   }
   if (partial != nullptr) return hipErrorInvalidValue;
   if (src_dt == Dt::F32 && out_dt == Dt::F32)

@@ -122,6 +122,41 @@ def test_fwd_noalloc_validation(q):
     assert q.qwha_fwd_workspace_bytes(3200, 4096, 4096, 524288) <= 64 << 20
 
 
+def test_shared_transform_validation(q):
+    # qwha_fwd_z: the forward from a kept z
+    def fz(**kw):
+        a = dict(z=FAKE, act=1, T=16, d_in=256, d_out=256, p=2048, row_ptr=FAKE, E=FAKE,
+                 c=FAKE, alpha=1.0, y=FAKE, acc=0, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_fwd_z(a["z"], a["act"], a["T"], a["d_in"], a["d_out"], a["p"],
+                            a["row_ptr"], a["E"], a["c"], a["alpha"], a["y"], a["acc"], a["ws"],
+                            a["wsb"], None)
+    assert fz(z=None) == INVALID
+    assert fz(z=FAKE + 4) == ALIGN
+    assert fz(d_in=12) == SHAPE
+    assert fz() == WORKSPACE
+    assert fz(T=0, z=None) == OK
+    # only the prepared stream is needed: less than qwha_fwd's workspace
+    need_fwd = q.qwha_fwd_workspace_bytes(16, 256, 256, 2048)
+    assert fz(wsb=need_fwd - 16 * 256 * 4, ws=FAKE, y=FAKE + 8) == ALIGN  # passes the size check
+
+    # qwha_bwd_dz: dz (+)= alpha dy F and dc, no transform
+    def bd(**kw):
+        a = dict(z=FAKE, dy=FAKE, act=1, T=16, d_in=256, d_out=256, p=2048, E=FAKE, c=FAKE,
+                 col_ptr=FAKE, perm=FAKE, alpha=1.0, dz=FAKE, acc=0, dc=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_bwd_dz(a["z"], a["dy"], a["act"], a["T"], a["d_in"], a["d_out"], a["p"],
+                             a["E"], a["c"], a["col_ptr"], a["perm"], a["alpha"], a["dz"],
+                             a["acc"], a["dc"], a["ws"], a["wsb"], None)
+    assert bd(dz=None) == INVALID
+    assert bd(acc=2) == INVALID
+    assert bd(dz=FAKE + 4) == ALIGN
+    assert bd(z=None) == INVALID            # dc needs the kept z
+    assert bd(z=None, dc=None) == WORKSPACE  # dz alone does not
+    assert bd() == WORKSPACE
+    assert bd(alpha=float("nan")) == INVALID
+
+
 def test_stream_position_limit(q):
     # the SpMM stream holds at most 2p + 16 entries at int32 positions: p is
     # capped at (2^31 - 65) // 2 for the calls that build it
