@@ -270,6 +270,110 @@ hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ radix select
+// Needs a block of whole waves: every wave scans the whole histogram with
+// its 64 lanes (4 bins each) and takes the same decisions.
+// The k-th largest of the block's keys (non-negative IEEE doubles as bit
+// patterns, so integer order is value order), MSB first:
+//  level 0: a 256-bin histogram of bins relative to the largest key, 16
+//           per octave: bin = 16 (e_max - e) + 15 - m4 (e the exponent, m4
+//           the top four mantissa bits), bin 0 holding the largest keys;
+//  levels 1..6: 8-bit digits of the remaining 48 mantissa bits, counted
+//           only for the keys in the bucket found so far.
+// Each level finds the bin where the count from the top reaches k, keeps
+// the keys above it and narrows to it; it stops when the bucket holds
+// exactly the keys still needed or the bits run out (a tie). Returns false
+// (tau unset) when the k-th key lies 16 octaves or more below the largest.
+// On success tau is the smallest key the bucket can hold: every key above
+// the bucket exceeds it, every key below is smaller, and the keys equal to
+// it are all in the bucket.
+__device__ __forceinline__ int wave_first_ge(int incl, int k) {
+  const unsigned long long b = __ballot(incl >= k);
+  return b == 0 ? 64 : __ffsll(static_cast<long long>(b)) - 1;
+}
+
+// Every wave reads the whole histogram h[256] (the top of the order at
+// bin 0) and finds, uniformly, the bin b where the running count reaches k
+// (k >= 1 and the total >= k), the count above it and the count in it.
+__device__ __forceinline__ void hist_cross(const int* h, int k, int& b, int& above, int& in) {
+  const int lane = threadIdx.x & 63;
+  const int4 c = reinterpret_cast<const int4*>(h)[lane];
+  const int s4 = c.x + c.y + c.z + c.w;
+  const int incl = wave_incl_scan_i32(s4);
+  const int L = wave_first_ge(incl, k);
+  const int before = __shfl(incl - s4, L);
+  const int x = __shfl(c.x, L), y = __shfl(c.y, L), z = __shfl(c.z, L), w = __shfl(c.w, L);
+  int q, cnt;
+  if (before + x >= k) { q = 0; cnt = x; }
+  else if (before + x + y >= k) { q = 1; cnt = y; }
+  else if (before + x + y + z >= k) { q = 2; cnt = z; }
+  else { q = 3; cnt = w; }
+  b = uniform(4 * L + q);
+  above = uniform(before + (q > 0 ? x : 0) + (q > 1 ? y : 0) + (q > 2 ? z : 0));
+  in = uniform(cnt);
+}
+
+template <int EPT>
+__device__ __forceinline__ bool radix_kth_largest(const unsigned long long (&key)[EPT],
+                                                  bool active, int k, int* hist,
+                                                  unsigned long long* red64,
+                                                  unsigned long long* tau) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  unsigned long long m = 0;
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) m = key[r] > m ? key[r] : m;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(m, off, 64);
+    m = o > m ? o : m;
+  }
+  if (lane == 0) red64[wid] = m;
+  for (int i = tid; i < 512; i += nth) hist[i] = 0;    // levels 0 and 1
+  __syncthreads();
+  unsigned long long kmax = 0;
+  for (int i = 0; i < nw; ++i) kmax = red64[i] > kmax ? red64[i] : kmax;
+  const int emax = static_cast<int>(kmax >> 52);
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int e = static_cast<int>(key[r] >> 52);
+      const int d = (emax - e) * 16 + 15 - static_cast<int>((key[r] >> 48) & 15);
+      atomicAdd(&hist[d > 255 ? 255 : d], 1);
+    }
+  }
+  __syncthreads();
+  int b, above, in;
+  hist_cross(hist, k, b, above, in);
+  if (b == 255) return false;
+  int need = k - above;
+  unsigned long long P = (static_cast<unsigned long long>(emax - b / 16) << 4) |
+                         static_cast<unsigned long long>(15 - b % 16);     // bits 48..62
+  int sh = 48;
+  int lev = 1;
+  while (sh > 0 && in != need) {
+    int* h = hist + 256 * (lev % 3);
+    int* hz = hist + 256 * ((lev + 1) % 3);   // the next level's, read two levels ago
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < EPT; ++r)
+        if ((key[r] >> sh) == P) atomicAdd(&h[255 - static_cast<int>((key[r] >> (sh - 8)) & 255)], 1);
+    }
+    for (int i = tid; i < 256; i += nth) hz[i] = 0;
+    __syncthreads();
+    hist_cross(h, need, b, above, in);
+    need -= above;
+    P = (P << 8) | static_cast<unsigned long long>(255 - b);
+    sh -= 8;
+    ++lev;
+  }
+  *tau = P << sh;
+  return true;
+}
+
 // ------------------------------------------------------------ selection
 // One workgroup per row i: C = dWq[i] H in fp64 (LDS-staged FWHT), then the
 // k = p_i columns first in the order (-|C_j|, j) are emitted ascending as
@@ -305,6 +409,8 @@ __global__ __launch_bounds__(BLOCKED ? 1024 : SelCfg<LOG_N>::BLOCK) void init_se
   __shared__ double lds_row[BLOCKED ? 1 : F::LDS];
   __shared__ int red[32];
   __shared__ int scan_tmp[16];
+  __shared__ int hist[3 * 256];
+  __shared__ unsigned long long red64[16];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int u = BLOCKED ? t % F::TPR : t;
@@ -367,6 +473,16 @@ __global__ __launch_bounds__(BLOCKED ? 1024 : SelCfg<LOG_N>::BLOCK) void init_se
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) gt += __popcll(__ballot(active && key[r] > tau));
     gt = block_total_i32(gt, red, parity);
+    parity ^= 1;
+    need = k - gt;
+  } else if (!all && !none &&
+             radix_kth_largest<F::EPT>(key, active, k, hist, red64, &tau)) {
+    const int gt = [&] {
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) cnt += __popcll(__ballot(active && key[r] > tau));
+      return block_total_i32(cnt, red, parity);
+    }();
     parity ^= 1;
     need = k - gt;
   } else if (!all && !none) {
@@ -456,7 +572,9 @@ hipError_t launch_select_mode(const float* dWq, int d_out, const int32_t* row_pt
   int threads = SelCfg<L>::BLOCK;
   size_t lds = 0;
   if (BLOCKED) {
-    threads = nblk * F::TPR < 64 ? 64 : nblk * F::TPR;
+    // whole waves: the radix select scans its histogram with every lane of
+    // every wave (threads past nblk * TPR hold no columns)
+    threads = (nblk * F::TPR + 63) / 64 * 64;
     lds = static_cast<size_t>(nblk) * F::LDS * sizeof(double);
   }
   const dim3 block(threads);

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(MatCfg<LOG_N>::BLOCK) void materialize_kernel(
     int accumulate) {
   using F = Fwht<LOG_N>;
   constexpr int RPW = MatCfg<LOG_N>::RPW;
-  __shared__ float lds_all[RPW * F::LDS];
+  __shared__ __align__(16) float lds_all[RPW * F::LDS];
   const int slot = threadIdx.x / F::TPR;
   const int u = threadIdx.x % F::TPR;
   // virtual row r of the [d_out * nblk][N] view: block blk of row i
@@ -33,7 +33,12 @@ __global__ __launch_bounds__(MatCfg<LOG_N>::BLOCK) void materialize_kernel(
   const int row = vrow / nblk, blk = vrow - row * nblk;
   float* lds = lds_all + slot * F::LDS;
 
-  for (int j = u; j < F::LDS; j += F::TPR) lds[j] = 0.f;
+  if constexpr (F::LDS % 4 == 0) {   // 16-byte stores (the row offset is a multiple of 16 B)
+    float4* z4 = reinterpret_cast<float4*>(lds);
+    for (int j = u; j < F::LDS / 4; j += F::TPR) z4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int j = u; j < F::LDS; j += F::TPR) lds[j] = 0.f;
+  }
   __syncthreads();
   if (live) {
     const int k1 = row_ptr[row + 1];
