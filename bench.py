@@ -285,6 +285,60 @@ class Block:
                                        a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
                                        a["dW"].data_ptr(), 0, st), "rematerialize")
 
+    def build_plans(self):
+        """The SpMM streams of every adapter from its current E (after an init)."""
+        from quantization_aware_sparse_amd import check, lib
+        import torch
+        for a in self.ads:
+            sp = a["spec"]
+            nb = lib.qwha_plan_bytes(sp.d_in, sp.d_out, sp.p)
+            a["plan"] = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+            check(lib.qwha_plan_build(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                      a["col_ptr"].data_ptr(), a["perm"].data_ptr(), sp.d_in,
+                                      sp.d_out, sp.p, a["plan"].data_ptr(), nb, self.stream),
+                  "plan")
+
+    def train_step(self, s):
+        """One fine-tuning step once the init has run (E frozen, plans built):
+        per group the forward (one kept z) and backward (dz summed over a
+        shared group, one transform), then every adapter's sign update and
+        re-materialisation of dW."""
+        from quantization_aware_sparse_amd import check, lib
+        st, A, T = self.stream, self.act_code, self.T
+        for g in self.groups:
+            x = g["x"][s % self.nsets]
+            for n, i in enumerate(g["members"]):
+                a, sp = self.ads[i], self.ads[i]["spec"]
+                check(lib.qwha_fwd_plan(x.data_ptr() if n == 0 else None,
+                                        None if n == 0 else g["z"].data_ptr(), A, T, sp.d_in,
+                                        sp.d_out, sp.p, a["plan"].data_ptr(), a["c"].data_ptr(),
+                                        1.0, a["y"].data_ptr(), 0,
+                                        g["z"].data_ptr() if n == 0 else None,
+                                        a["ws_f"].data_ptr(), a["ws_f"].numel(), st), "fwd_plan")
+        for g in self.groups:
+            shared = len(g["members"]) > 1
+            for n, i in enumerate(g["members"]):
+                a, sp = self.ads[i], self.ads[i]["spec"]
+                check(lib.qwha_bwd_plan(g["z"].data_ptr(), a["dy"][s % self.nsets].data_ptr(), A,
+                                        T, sp.d_in, sp.d_out, sp.p, a["plan"].data_ptr(),
+                                        a["c"].data_ptr(), 1.0,
+                                        None if shared else g["dx"].data_ptr(), 0,
+                                        g["dz"].data_ptr() if shared else None, int(n > 0),
+                                        a["dc"].data_ptr(), a["ws_b"].data_ptr(),
+                                        a["ws_b"].numel(), st), "bwd_plan")
+            if shared:
+                d_in = g["d_in"]
+                b = d_in & -d_in
+                check(lib.qwha_fwht(g["dz"].data_ptr(), 0, g["dx"].data_ptr(), A,
+                                    T * (d_in // b), b, 1.0 / b, st), "fwht dx")
+        for a in self.ads:
+            sp = a["spec"]
+            check(lib.qwha_sign_update(a["c"].data_ptr(), a["dc"].data_ptr(), sp.p, 1e-3, st),
+                  "update")
+            check(lib.qwha_materialize(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                       a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
+                                       a["dW"].data_ptr(), 0, st), "rematerialize")
+
     def read_times(self):
         for a in self.ads:
             for k in a["armed"]:
@@ -361,6 +415,25 @@ def measure(block, steps, warmup, config_name):
     return dict(value=round(block.T / (ms_step / 1e3), 1), ms_per_step=round(ms_step, 4),
                 profiled_steps_ms=round(1e3 * wall / steps, 4), roofline=roof,
                 kernels=per[block.ads[0]["name"]] if len(per) == 1 else per)
+
+
+def measure_train(block, steps, warmup):
+    """The fine-tuning step after a one-time init (plans built once): what a
+    training loop repeats. Reported beside the whole-path step, not as it."""
+    import torch
+    block.step(0, False)
+    block.build_plans()
+    for s in range(warmup):
+        block.train_step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        block.train_step(s)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    return dict(what="fwd + bwd + sign update + re-materialize per step after one init, "
+                     "SpMM streams planned once from E (values gathered from c per call)",
+                tokens_per_s=round(block.T / (ms / 1e3), 1), ms_per_step=round(ms, 4))
 
 
 def workload_text(block):
@@ -456,6 +529,7 @@ def main():
     if args.refine_tokens > 0 and args.refine_reps > 0 and len(block.ads) == 1:
         out["refine"] = refine_measure(args.refine_tokens, args.refine_reps, spec, sets[0][0],
                                        stream, hip)
+    out["train_step"] = measure_train(block, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(block, args.cpu_tokens or spec.T)
 
@@ -472,7 +546,8 @@ def main():
             mm = measure(blk, args.steps, args.warmup, cfg)
             entry = dict(workload=workload_text(blk), unit="tokens/s", value=mm["value"],
                          ms_per_step=mm["ms_per_step"], dtype=blk.act, roofline=mm["roofline"],
-                         kernels=mm["kernels"], input_gen_s=round(blk.gen_s, 2))
+                         kernels=mm["kernels"], input_gen_s=round(blk.gen_s, 2),
+                         train_step=measure_train(blk, args.steps, args.warmup))
             if not args.no_cpu_baseline:
                 entry["cpu_baseline"] = cpu_baseline(blk, min(args.extra_cpu_tokens, blk.T),
                                                      min_seconds=1.0)

@@ -230,6 +230,47 @@ qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t 
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Plans: the structure of F that the gather-SpMMs walk, built once. E is
+ * frozen after the init and only c trains (papernotes.org, 损失函数 / 训练策略),
+ * so the streams qwha_fwd / qwha_bwd prepare on every call (the nonzeros in
+ * column-block order, for the rows of F and for its columns) depend on E
+ * alone; a plan keeps them, and each planned call only gathers the current
+ * c into them (one small kernel per direction).
+ *
+ * qwha_plan_bytes: the plan's size for (d_in, d_out, p); 0 when out of range.
+ * qwha_plan_build: builds the plan from row_ptr, E, col_ptr, csc_perm into
+ *   `plan` (device, 256-byte aligned, at least qwha_plan_bytes). Rebuild it
+ *   whenever E changes.
+ * qwha_fwd_plan: qwha_fwd on a plan: y (+)= alpha z F^T with z = FWHT(x)/d_in
+ *   computed from x, or taken from z_in (a kept transform; x is then not
+ *   read); z_out (optional, exclusive with z_in) keeps the transform as
+ *   qwha_fwd_save does. Workspace: T * d_in * 4 bytes rounded up to 256 when
+ *   neither z_in nor z_out is given, else none (qwha_fwd_workspace_bytes
+ *   suffices).
+ * qwha_bwd_plan: qwha_bwd_saved on a plan, from the kept z: dc as qwha_bwd
+ *   (required), and either dx (+)= alpha FWHT(dy F)/d_in (dx not NULL) or,
+ *   with dz not NULL, dz (+)= alpha dy F without the transform, as
+ *   qwha_bwd_dz (dx and dz are exclusive; both NULL forms dc only).
+ *   Workspace: qwha_bwd_workspace_bytes suffices.
+ * The plan's values are rewritten by every planned call: calls that share a
+ * plan must not overlap. The shapes, p and c must be those of the plan's
+ * adapter (not checked: the plan lives on the device).
+ * --------------------------------------------------------------------------- */
+size_t qwha_plan_bytes(int32_t d_in, int32_t d_out, int64_t p);
+qwha_status qwha_plan_build(const int32_t* row_ptr, const int32_t* E, const int32_t* col_ptr,
+                            const int32_t* csc_perm, int32_t d_in, int32_t d_out, int64_t p,
+                            void* plan, size_t plan_bytes, hipStream_t stream);
+qwha_status qwha_fwd_plan(const void* x, const float* z_in, qwha_dtype act, int64_t T,
+                          int32_t d_in, int32_t d_out, int64_t p, void* plan, const float* c,
+                          float alpha, void* y, int32_t accumulate, float* z_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+qwha_status qwha_bwd_plan(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                          int32_t d_in, int32_t d_out, int64_t p, void* plan, const float* c,
+                          float alpha, void* dx, int32_t accumulate_dx, float* dz,
+                          int32_t accumulate_dz, float* dc, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Coefficient update of the attention-block training step:
  *   c[k] += step * sign(dc[k])   (sign(0) = 0), fp32, in place.
  * --------------------------------------------------------------------------- */

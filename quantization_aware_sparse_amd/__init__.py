@@ -23,7 +23,7 @@ __all__ = [
     "qwha_init_select", "qwha_init_select_global", "qwha_hessian",
     "qwha_init_select_calibrated", "qwha_refine_values", "qwha_merge", "qwha_layer_fwd",
     "qwha_materialize", "qwha_fwd", "qwha_fwd_noalloc", "qwha_fwd_z", "qwha_bwd",
-    "qwha_bwd_dz",
+    "qwha_bwd_dz", "qwha_plan_build", "qwha_fwd_plan", "qwha_bwd_plan",
     "qwha_sign_update", "qwha_fwht", "workspace", "WHAFunction",
 ]
 
@@ -335,6 +335,67 @@ def qwha_bwd_dz(z: Optional[torch.Tensor], dy: torch.Tensor, E, c, col_ptr, csc_
                           dc.data_ptr() if dc is not None else None, ws.data_ptr(), ws.numel(),
                           _stream()), "qwha_bwd_dz")
     return dz, dc
+
+
+# ---------------------------------------------------------------- plans
+def qwha_plan_build(row_ptr, E, col_ptr, csc_perm, d_in: int, d_out: int,
+                    plan: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Both SpMM streams of the adapter, built once from its frozen E (int32
+    [p][2]) with the init's row_ptr, col_ptr and csc_perm; returns the plan."""
+    p = int(E.shape[0])
+    need = lib.qwha_plan_bytes(d_in, d_out, p)
+    if plan is None:
+        plan = workspace(need, E.device)
+    check(lib.qwha_plan_build(_ptr(row_ptr), E.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(),
+                              d_in, d_out, p, plan.data_ptr(), plan.numel(), _stream()),
+          "qwha_plan_build")
+    return plan
+
+
+def qwha_fwd_plan(x: Optional[torch.Tensor], plan: torch.Tensor, c, d_out: int,
+                  alpha: float = 1.0, y: Optional[torch.Tensor] = None,
+                  accumulate: bool = False, z_in: Optional[torch.Tensor] = None,
+                  z_out: Optional[torch.Tensor] = None, act=None,
+                  ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y (+)= alpha z F^T on a plan; z from x, or z_in (kept); z_out keeps it."""
+    src = z_in if z_in is not None else x
+    T, d_in = src.shape
+    p = int(c.numel())
+    adt = act if act is not None else (x.dtype if x is not None else torch.bfloat16)
+    if y is None:
+        y = torch.empty((T, d_out), dtype=adt, device=src.device)
+    if ws is None:
+        ws = workspace(lib.qwha_fwd_workspace_bytes(T, d_in, d_out, p), src.device)
+    check(lib.qwha_fwd_plan(_ptr(x), _ptr(z_in), _dt(y), T, d_in, d_out, p, plan.data_ptr(),
+                            c.data_ptr(), float(alpha), _ptr(y), int(accumulate), _ptr(z_out),
+                            ws.data_ptr(), ws.numel(), _stream()), "qwha_fwd_plan")
+    return y
+
+
+def qwha_bwd_plan(z: torch.Tensor, dy: torch.Tensor, plan: torch.Tensor, c,
+                  alpha: float = 1.0, need_dx: bool = True, dx: Optional[torch.Tensor] = None,
+                  accumulate_dx: bool = False, dz: Optional[torch.Tensor] = None,
+                  accumulate_dz: bool = False, dc: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None):
+    """dc and dx (or dz with no transform) from the kept z on a plan."""
+    T, d_in = z.shape
+    d_out = dy.shape[1]
+    p = int(c.numel())
+    if dz is not None:
+        need_dx = False
+    if need_dx and dx is None:
+        dx = torch.empty((T, d_in), dtype=dy.dtype, device=dy.device)
+    if not need_dx:
+        dx = None
+    if dc is None:
+        dc = torch.empty(max(p, 1), dtype=torch.float32, device=dy.device)[:p]
+    if ws is None:
+        ws = workspace(lib.qwha_bwd_workspace_bytes(T, d_in, d_out, p), dy.device)
+    check(lib.qwha_bwd_plan(_ptr(z), _ptr(dy), _dt(dy), T, d_in, d_out, p, plan.data_ptr(),
+                            c.data_ptr(), float(alpha), _ptr(dx), int(accumulate_dx), _ptr(dz),
+                            int(accumulate_dz), dc.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream()), "qwha_bwd_plan")
+    return (dz if dz is not None else dx), dc
 
 
 # ---------------------------------------------------------------- update, fwht

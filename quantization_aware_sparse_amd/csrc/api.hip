@@ -182,6 +182,22 @@ BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p, bool with_dc) {
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// A plan: the forward's stream (rows of F, entry pairs) and the backward's
+// (columns of F, single entries with the dc partials), both with korig.
+struct PlanLayout {
+  size_t fwd, bwd, total;
+  SpmmPlan pf, pb;   // ntiles is per call
+};
+PlanLayout plan_layout(int32_t d_in, int32_t d_out, int64_t p) {
+  PlanLayout l;
+  l.pf = spmm_plan(0, d_in, d_out, p, false);
+  l.pb = spmm_plan(0, d_out, d_in, p, true);
+  l.fwd = 0;
+  l.bwd = align256(spmm_prep_bytes(p, d_out, l.pf));
+  l.total = l.bwd + align256(spmm_prep_bytes(p, d_in, l.pb));
+  return l;
+}
+
 // Device address of `scratch` on the current device, looked up once per
 // device (with that device current) and kept.
 constexpr int kMaxDevices = 64;
@@ -912,6 +928,172 @@ qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t 
                              }),
                        "dc reduce"));
   return QWHA_OK;
+}
+
+// ------------------------------------------------------------------ plans
+size_t qwha_plan_bytes(int32_t d_in, int32_t d_out, int64_t p) {
+  if (d_in < 1 || d_out < 1 || p < 0 || p > kMaxStreamP) return 0;
+  return plan_layout(d_in, d_out, p).total;
+}
+
+qwha_status qwha_plan_build(const int32_t* row_ptr, const int32_t* E, const int32_t* col_ptr,
+                            const int32_t* csc_perm, int32_t d_in, int32_t d_out, int64_t p,
+                            void* plan, size_t plan_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
+  QWHA_NEED(row_ptr, 4);
+  QWHA_NEED(col_ptr, 4);
+  if (p > 0) {
+    QWHA_NEED(E, 4);
+    QWHA_NEED(csc_perm, 4);
+  }
+  const PlanLayout l = plan_layout(d_in, d_out, p);
+  if (plan == nullptr || plan_bytes < l.total)
+    return fail(QWHA_ERR_WORKSPACE, "the plan needs %zu bytes", l.total);
+  QWHA_NEED(plan, 256);
+  QWHA_TRY(hip_check(launch_prep_structure(row_ptr, E, nullptr, d_out, p, l.pf,
+                                           at(plan, l.fwd), stream),
+                     "plan (rows of F)"));
+  return hip_check(launch_prep_structure(col_ptr, E, csc_perm, d_in, p, l.pb, at(plan, l.bwd),
+                                         stream),
+                   "plan (columns of F)");
+}
+
+qwha_status qwha_fwd_plan(const void* x, const float* z_in, qwha_dtype act, int64_t T,
+                          int32_t d_in, int32_t d_out, int64_t p, void* plan, const float* c,
+                          float alpha, void* y, int32_t accumulate, float* z_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
+  QWHA_TRY(check_dt(act, "act"));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(QWHA_ERR_INVALID_ARG, "accumulate must be 0/1");
+  if (z_in != nullptr && z_out != nullptr)
+    return fail(QWHA_ERR_INVALID_ARG, "z_in and z_out are exclusive");
+  QWHA_NEED(plan, 256);
+  if (p > 0) QWHA_NEED(c, 4);
+  if (T == 0) return QWHA_OK;
+  if (z_in != nullptr)
+    QWHA_NEED(z_in, 16);
+  else
+    QWHA_NEED(x, 16);
+  if (z_out != nullptr) QWHA_NEED(z_out, 16);
+  QWHA_NEED(y, 16);
+  const bool own_z = z_in == nullptr && z_out == nullptr;
+  const size_t need = own_z ? align256(static_cast<size_t>(T) * d_in * 4) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(QWHA_ERR_WORKSPACE, "fwd workspace needs %zu bytes", need);
+  if (need > 0) QWHA_NEED(workspace, 256);
+
+  PlanLayout l = plan_layout(d_in, d_out, p);
+  l.pf = spmm_plan(T, d_in, d_out, p, false);
+  void* prep = at(plan, l.fwd);
+  const Dt adt = static_cast<Dt>(act);
+  QWHA_TRY(hip_check(launch_prep_refresh(c, p, d_out, l.pf, prep, stream), "fwd values"));
+  const float* z = z_in;
+  if (z_in == nullptr) {
+    float* zw = z_out ? z_out : reinterpret_cast<float*>(workspace);
+    z = zw;
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_FWD_FWHT, stream,
+                             [&] {
+                               return launch_fwht(x, adt, zw, Dt::F32, T * nblk, log_n,
+                                                  1.0f / static_cast<float>(1 << log_n), 0,
+                                                  stream);
+                             }),
+                       "fwd fwht"));
+  }
+  return hip_check(timed(QWHA_KERNEL_FWD_SPMM, stream,
+                         [&] {
+                           return launch_spmm(z, Dt::F32, T, d_in, prep, p, d_out, l.pf, alpha,
+                                              y, adt, accumulate, nullptr, nullptr, stream);
+                         }),
+                   "fwd spmm");
+}
+
+qwha_status qwha_bwd_plan(const float* z, const void* dy, qwha_dtype act, int64_t T,
+                          int32_t d_in, int32_t d_out, int64_t p, void* plan, const float* c,
+                          float alpha, void* dx, int32_t accumulate_dx, float* dz,
+                          int32_t accumulate_dz, float* dc, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  int log_n;
+  int nblk;
+  QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
+  QWHA_TRY(check_p(p, d_out, d_in));
+  QWHA_TRY(check_stream_p(p));
+  QWHA_TRY(check_dt(act, "act"));
+  if (T < 0 || T > (static_cast<int64_t>(1) << 31)) return fail(QWHA_ERR_SHAPE, "T out of range");
+  if (!isfinite(alpha)) return fail(QWHA_ERR_INVALID_ARG, "alpha must be finite");
+  if (accumulate_dx != 0 && accumulate_dx != 1)
+    return fail(QWHA_ERR_INVALID_ARG, "accumulate_dx must be 0/1");
+  if (accumulate_dz != 0 && accumulate_dz != 1)
+    return fail(QWHA_ERR_INVALID_ARG, "accumulate_dz must be 0/1");
+  if (dz != nullptr && dx != nullptr)
+    return fail(QWHA_ERR_INVALID_ARG, "dx and dz are exclusive (dz skips the transform)");
+  if (dc == nullptr)
+    return fail(QWHA_ERR_INVALID_ARG, "dc is NULL (the plan's backward forms dc)");
+  if (!aligned(dc, 4)) return fail(QWHA_ERR_ALIGN, "dc is not 4-byte aligned");
+  QWHA_NEED(plan, 256);
+  if (p > 0) QWHA_NEED(c, 4);
+  const PlanLayout l0 = plan_layout(d_in, d_out, p);
+  const void* prep_b = at(plan, l0.bwd);
+  if (T == 0) {
+    if (p > 0)
+      return hip_check(launch_dc_reduce(nullptr, 0, p,
+                                        spmm_prep_korig(prep_b, p, d_in, l0.pb), alpha, dc,
+                                        stream),
+                       "dc zero");
+    return QWHA_OK;
+  }
+  QWHA_NEED(z, 16);
+  QWHA_NEED(dy, 16);
+  if (dx != nullptr) QWHA_NEED(dx, 16);
+  if (dz != nullptr) QWHA_NEED(dz, 16);
+  const SpmmPlan pb = spmm_plan(T, d_out, d_in, p, true);
+  const size_t zb = dz ? 0 : align256(static_cast<size_t>(T) * d_in * 4);
+  const size_t total = zb + align256(static_cast<size_t>(pb.ntiles) * static_cast<size_t>(p) * 4);
+  if (workspace == nullptr || workspace_bytes < total)
+    return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", total);
+  QWHA_NEED(workspace, 256);
+
+  void* prep = at(plan, l0.bwd);
+  float* dzw = dz ? dz : reinterpret_cast<float*>(workspace);
+  float* partial = reinterpret_cast<float*>(at(workspace, zb));
+  const Dt adt = static_cast<Dt>(act);
+  // with a caller dz the SpMM applies alpha; otherwise the transform does
+  const float a_spmm = dz ? alpha : 1.0f;
+  QWHA_TRY(hip_check(launch_prep_refresh(c, p, d_in, pb, prep, stream), "bwd values"));
+  QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_SPMM, stream,
+                           [&] {
+                             return launch_spmm(dy, adt, T, d_out, prep, p, d_in, pb, a_spmm,
+                                                dzw, Dt::F32, dz ? accumulate_dz : 0, z,
+                                                partial, stream);
+                           }),
+                     "bwd spmm"));
+  if (dx != nullptr)
+    QWHA_TRY(hip_check(timed(QWHA_KERNEL_BWD_FWHT_DX, stream,
+                             [&] {
+                               return launch_fwht(dzw, Dt::F32, dx, adt, T * nblk, log_n,
+                                                  alpha / static_cast<float>(1 << log_n),
+                                                  accumulate_dx, stream);
+                             }),
+                       "bwd fwht(dz)"));
+  return hip_check(timed(QWHA_KERNEL_BWD_DC_REDUCE, stream,
+                         [&] {
+                           return launch_dc_reduce(partial, pb.ntiles, p,
+                                                   spmm_prep_korig(prep, p, d_in, pb), alpha, dc,
+                                                   stream);
+                         }),
+                   "dc reduce");
 }
 
 // ------------------------------------------------------------------ update

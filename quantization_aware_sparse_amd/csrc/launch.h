@@ -111,6 +111,14 @@ hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* csc_perm, cons
                            const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
                            hipStream_t s);
 
+// The same streams built from E alone (values 0, korig kept in both
+// directions), and the per-call gather of the values from c.
+hipError_t launch_prep_structure(const int32_t* seg_ptr, const int32_t* E, const int32_t* perm,
+                                 int n_out, int64_t nnz, const SpmmPlan& pl, void* prep,
+                                 hipStream_t s);
+hipError_t launch_prep_refresh(const float* c, int64_t nnz, int n_out, const SpmmPlan& pl,
+                               void* prep, hipStream_t s);
+
 // out[t][o] (+)= alpha * sum_k val_k * src[t][col_k]; with zsrc, also
 // partial[tile][q] = sum_{t in tile} src[t][col_q] * zsrc[t][o] per stream entry q.
 hipError_t launch_spmm(const void* src, Dt src_dt, int64_t T, int n_src, const void* prep,

@@ -240,7 +240,7 @@ __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __res
   const int first = bptr[r];
   const int64_t pos = static_cast<int64_t>(base[b]) +
                       ptr[static_cast<int64_t>(b) * stride + o] + (q - first);
-  stream[pos] = make_int2((col - b * jb) * tt * 4, __float_as_int(c[k]));
+  stream[pos] = make_int2((col - b * jb) * tt * 4, c ? __float_as_int(c[k]) : 0);
   if (korig) korig[pos] = static_cast<int32_t>(k);
   if (mult > 1) {
     const int last = bptr[r + 1] - 1;
@@ -285,6 +285,36 @@ hipError_t launch_prep_csc(const int32_t* col_ptr, const int32_t* perm, const in
                            const float* c, int d_in, int64_t nnz, const SpmmPlan& pl, void* prep,
                            hipStream_t s) {
   return prep_common(col_ptr, E, c, perm, d_in, nnz, pl, true, prep, s);
+}
+
+// ------------------------------------------------------------ cached structure
+// A prepared stream whose positions depend only on E (frozen after the init):
+// the structure is built once, with korig kept in both directions, and each
+// call only gathers the current values, stream[q].value = c[korig[q]] (0 for
+// the padding entries). The stream's length is base[nblk], read on the device.
+hipError_t launch_prep_structure(const int32_t* seg_ptr, const int32_t* E, const int32_t* perm,
+                                 int n_out, int64_t nnz, const SpmmPlan& pl, void* prep,
+                                 hipStream_t s) {
+  return prep_common(seg_ptr, E, nullptr, perm, n_out, nnz, pl, true, prep, s);
+}
+
+__global__ void refresh_values_kernel(int2* __restrict__ stream, const int32_t* __restrict__ korig,
+                                      const float* __restrict__ c,
+                                      const int32_t* __restrict__ end, int64_t cap) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= cap || q >= static_cast<int64_t>(*end)) return;
+  const int k = korig[q];
+  stream[q].y = k >= 0 ? __float_as_int(c[k]) : 0;
+}
+
+hipError_t launch_prep_refresh(const float* c, int64_t nnz, int n_out, const SpmmPlan& pl,
+                               void* prep, hipStream_t s) {
+  const PrepLayout l = prep_layout(nnz, n_out, pl);
+  if (l.cap == 0) return hipSuccess;
+  hipLaunchKernelGGL(refresh_values_kernel, dim3(static_cast<unsigned>((l.cap + 255) / 256)),
+                     dim3(256), 0, s, at<int2>(prep, l.stream), at<int32_t>(prep, l.korig), c,
+                     at<int32_t>(prep, l.base) + pl.nblk, l.cap);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ helpers

@@ -157,6 +157,70 @@ def test_shared_transform_validation(q):
     assert bd(alpha=float("nan")) == INVALID
 
 
+def test_plan_validation(q):
+    # the plan holds both prepared streams: the forward's (padded pairs) and
+    # the backward's, each with its index map, sized independently of T
+    pb = q.qwha_plan_bytes(4096, 4096, 524288)
+    assert pb >= 524288 * (8 + 4) * 2
+    assert q.qwha_plan_bytes(0, 4096, 100) == 0
+    assert q.qwha_plan_bytes(4096, 4096, -1) == 0
+    assert q.qwha_plan_bytes(16384, 65536, 2**31) == 0
+
+    def build(**kw):
+        a = dict(row_ptr=FAKE, E=FAKE, col_ptr=FAKE, perm=FAKE, d_in=256, d_out=256, p=2048,
+                 plan=FAKE, nb=0)
+        a.update(kw)
+        return q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["perm"], a["d_in"],
+                                 a["d_out"], a["p"], a["plan"], a["nb"], None)
+    assert build(d_in=12) == SHAPE
+    assert build(p=256 * 256 + 1) == BUDGET
+    assert build(E=None) == INVALID
+    assert build() == WORKSPACE
+    assert b"plan needs" in q.qwha_last_error()
+    need = q.qwha_plan_bytes(256, 256, 2048)
+    assert build(nb=need, plan=FAKE + 64) == ALIGN
+
+    def fp(**kw):
+        a = dict(x=FAKE, z_in=None, act=1, T=16, d_in=256, d_out=256, p=2048, plan=FAKE,
+                 c=FAKE, alpha=1.0, y=FAKE, acc=0, z_out=None, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_fwd_plan(a["x"], a["z_in"], a["act"], a["T"], a["d_in"], a["d_out"],
+                               a["p"], a["plan"], a["c"], a["alpha"], a["y"], a["acc"],
+                               a["z_out"], a["ws"], a["wsb"], None)
+    assert fp(d_in=12) == SHAPE
+    assert fp(act=7) == DTYPE
+    assert fp(z_in=FAKE, z_out=FAKE) == INVALID
+    assert fp(plan=None) == INVALID
+    assert fp(x=None) == INVALID                         # neither x nor z_in
+    assert fp(acc=2) == INVALID
+    assert fp() == WORKSPACE                             # z needs room
+    assert fp(T=0, x=None) == OK
+    # with z kept by the caller no workspace is needed: the next check is y's
+    assert fp(z_out=FAKE, y=FAKE + 8) == ALIGN
+    assert fp(z_in=FAKE, x=None, y=FAKE + 8) == ALIGN
+
+    def bp(**kw):
+        a = dict(z=FAKE, dy=FAKE, act=1, T=16, d_in=256, d_out=256, p=2048, plan=FAKE, c=FAKE,
+                 alpha=1.0, dx=FAKE, accx=0, dz=None, accz=0, dc=FAKE, ws=FAKE, wsb=0)
+        a.update(kw)
+        return q.qwha_bwd_plan(a["z"], a["dy"], a["act"], a["T"], a["d_in"], a["d_out"],
+                               a["p"], a["plan"], a["c"], a["alpha"], a["dx"], a["accx"],
+                               a["dz"], a["accz"], a["dc"], a["ws"], a["wsb"], None)
+    assert bp(dz=FAKE) == INVALID                        # dx and dz are exclusive
+    assert bp(dc=None) == INVALID
+    assert bp(dc=FAKE + 2) == ALIGN
+    assert bp(accx=2) == INVALID
+    assert bp(accz=3, dx=None, dz=FAKE) == INVALID
+    assert bp(alpha=float("inf")) == INVALID
+    assert bp(z=None) == INVALID
+    assert bp() == WORKSPACE
+    assert b"bwd workspace" in q.qwha_last_error()
+    # qwha_bwd_workspace_bytes suffices for every form
+    wb = q.qwha_bwd_workspace_bytes(16, 256, 256, 2048)
+    assert bp(wsb=wb, ws=FAKE + 64) == ALIGN
+    assert bp(wsb=wb, ws=FAKE + 64, dx=None, dz=FAKE) == ALIGN
+
+
 def test_stream_position_limit(q):
     # the SpMM stream holds at most 2p + 16 entries at int32 positions: p is
     # capped at (2^31 - 65) // 2 for the calls that build it
