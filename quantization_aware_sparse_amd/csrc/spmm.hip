@@ -51,6 +51,12 @@ constexpr int kRJB = 64;          // source columns per staged block (64 KiB fp3
 constexpr int kRW = 16;           // waves per workgroup
 constexpr int kRR = 16;           // output rows per wave
 constexpr int kRRdc = 8;          // output rows per wave with dc partials
+// The row after which a wave stores the first half of the next block and
+// issues the loads of its second half (forward, backward; measured at the
+// 4096x4096 layer). The first half's loads go out before the block's opening
+// barrier, so they have the barrier wait and the first rows to land.
+constexpr int kMidF = 8;
+constexpr int kMidB = 2;
 constexpr int kEntCap = 1536;     // stream entries staged in LDS per block
 constexpr int kMaxBlk = 256;      // blocks held in a workgroup's run table
 
@@ -494,7 +500,7 @@ __device__ __forceinline__ void rows_pairs(float (&acc)[kRR][4], const int (&sg)
       fma4(acc[r], __int_as_float(cur.w), z1);
       cur = nx;
     }
-    if (r == kRR / 2 - 1) mid();
+    if (r == kMidF - 1) mid();
   }
 }
 
@@ -505,7 +511,8 @@ __device__ __forceinline__ void rows_pairs(float (&acc)[kRR][4], const int (&sg)
 // an array of values (kEntCap + 2 each). Longer runs are restaged in chunks.
 template <int ROWS, bool SPLIT>
 struct RowsMeta {
-  int seg;     // thread tid <= ROWS: bound of row tid
+  int seg;     // thread tid <= ROWS: bound of row tid, before subtracting p0
+  int p0;      // the run's block-local start
   int4 pair;   // thread tid <= kEntCap / 2: pair tid of the run
   int k0;      // uniform
   // Run table of a workgroup, one int4 per block: (k0, the block-local
@@ -527,7 +534,7 @@ struct RowsMeta {
                                        const int32_t* __restrict__ base, const int4* runs,
                                        bool with_table, int ptr_stride, int rg0, int b) {
     const int32_t* pb = ptr + static_cast<int64_t>(b) * ptr_stride + rg0;
-    int p0, cnt;
+    int cnt;
     if (with_table) {
       const int4 rb = runs[b];
       k0 = uniform(rb.x);
@@ -539,7 +546,9 @@ struct RowsMeta {
       cnt = pb[ROWS] - p0;
     }
     const int tid = threadIdx.x;
-    seg = tid <= ROWS ? pb[tid] - p0 : 0;
+    // raw: subtracting p0 here would make the compiler wait for this load
+    // (and every load issued before it) at once; store() does it instead
+    seg = tid <= ROWS ? pb[tid] : 0;
     // the stream is padded past its end, so a pair may straddle the run's
     // end; pair kEntCap / 2 (read past the staged run, never used) is zero
     pair = 2 * tid < cnt && tid < kEntCap / 2
@@ -548,7 +557,7 @@ struct RowsMeta {
   }
   __device__ __forceinline__ void store(int* segs, int4* pairs) const {
     const int tid = threadIdx.x;
-    if (tid <= ROWS) segs[tid] = seg;
+    if (tid <= ROWS) segs[tid] = seg - p0;
     if (tid < kEntCap / 2 + 1) store_pair(pairs, tid, pair);
   }
   static __device__ __forceinline__ void store_pair(int4* pairs, int t, const int4& e) {
@@ -596,16 +605,17 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
     pf.store(stage[0], T, n_src, t0, 0, h);
   }
   meta.store(segs[0], pairs[0]);
+  int k0n = meta.k0;   // k0 of the block staged next
+  if (nblk > 1) {
+    pf.load(src, T, n_src, t0, 1, 0);
+    meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 1);
+  }
   for (int b = 0; b < nblk; ++b) {
     __syncthreads();
-    const int k0 = meta.k0;
+    const int k0 = k0n;
     const bool more = b + 1 < nblk;
     const int nb = b + 1;
     float* nst = stage[nb & 1];
-    if (more) {
-      pf.load(src, T, n_src, t0, nb, 0);
-      meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb);
-    }
     const int buf = b & 1;
     int sg[kRR + 1];
 #pragma unroll
@@ -635,6 +645,11 @@ __global__ __launch_bounds__(kRW * 64) void rows_kernel(
     if (more) {
       pf.store(nst, T, n_src, t0, nb, 1);
       meta.store(segs[nb & 1], pairs[nb & 1]);
+      k0n = meta.k0;
+      if (nb + 1 < nblk) {   // registers only: nothing in LDS is touched
+        pf.load(src, T, n_src, t0, nb + 1, 0);
+        meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb + 1);
+      }
     }
   }
 
@@ -776,7 +791,7 @@ __device__ __forceinline__ void rows_entries_dc(float (&acc)[kRRdc][4],
         i += 1;
       }
     }
-    if (r == kRRdc / 2 - 1) mid();
+    if (r == kMidB - 1) mid();
   });
 }
 
@@ -820,16 +835,17 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     pf.store(stage[0], T, n_src, t0, 0, h);
   }
   meta.store(segs[0], pairs[0]);
+  int k0n = meta.k0;   // k0 of the block staged next
+  if (nblk > 1) {
+    pf.load(src, T, n_src, t0, 1, 0);
+    meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 1);
+  }
   for (int b = 0; b < nblk; ++b) {
     __syncthreads();
-    const int k0 = meta.k0;
+    const int k0 = k0n;
     const bool more = b + 1 < nblk;
     const int nb = b + 1;
     float* nst = stage[nb & 1];
-    if (more) {
-      pf.load(src, T, n_src, t0, nb, 0);
-      meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb);
-    }
     const int buf = b & 1;
     int sg[kRRdc + 1];
 #pragma unroll
@@ -859,6 +875,11 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
     if (more) {
       pf.store(nst, T, n_src, t0, nb, 1);
       meta.store(segs[nb & 1], pairs[nb & 1]);
+      k0n = meta.k0;
+      if (nb + 1 < nblk) {   // registers only: nothing in LDS is touched
+        pf.load(src, T, n_src, t0, nb + 1, 0);
+        meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb + 1);
+      }
     }
   }
 
