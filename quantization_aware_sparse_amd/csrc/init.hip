@@ -259,12 +259,194 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
   }
 }
 
+// The same passes with every row's state in registers: thread tid owns the
+// contiguous rows [tid * rpt, (tid+1) * rpt) (rpt <= kAllocRegRows), so a
+// pass is register work plus one block reduction, with no global memory
+// between passes. The sums over rows are taken in this order (per thread,
+// then across threads); the leftover and the row_ptr scan are as above.
+constexpr int kAllocRegRows = 16;
+
+__global__ __launch_bounds__(kAllocThreads) void adaalloc_reg_kernel(
+    const double* __restrict__ w, int d_out, int d_in, int64_t p, int m, double t,
+    int32_t* __restrict__ row_ptr) {
+  __shared__ double red_d[2][16];
+  __shared__ long long red_l[2][16];
+  __shared__ int red_i[2][16];
+  __shared__ int red_f[2][16];
+  __shared__ int hist[16385 + 1];
+  __shared__ int scan_tmp[16];
+  __shared__ int vstar;
+  __shared__ int below_star;
+  constexpr int R = kAllocRegRows;
+  constexpr int NW = kAllocThreads / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int rpt = (d_out + kAllocThreads - 1) / kAllocThreads;
+  const int r0 = tid * rpt;
+
+  double s[R];
+  int bud[R];
+  int fx[R];   // 0 free, 1 held at the floor m, 2 held at the cap d_in, -1 / -2 tentative
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r0 + r;
+    const bool own = r < rpt && i < d_out;
+    s[r] = own ? ((t == 1.0) ? w[i] : pow(w[i], 1.0 / t)) : 0.0;
+    bud[r] = 0;
+    fx[r] = own ? 0 : 3;   // 3: not a row
+  }
+
+  int parity = 0;
+  for (;;) {
+    double ps = 0.0;
+    long long pf = 0;
+    int nu = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (fx[r] == 0) { ps += s[r]; ++nu; }
+      else if (fx[r] == 1 || fx[r] == 2) pf += bud[r];
+    }
+    ps = wave_sum_f64(ps);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) pf += __shfl_xor(pf, off, 64);
+    nu = wave_sum_i32(nu);
+    if (lane == 0) { red_d[parity][wid] = ps; red_l[parity][wid] = pf; red_i[parity][wid] = nu; }
+    __syncthreads();
+    double S = 0.0;
+    long long F = 0;
+    int NU = 0;
+    for (int i = 0; i < NW; ++i) { S += red_d[parity][i]; F += red_l[parity][i]; NU += red_i[parity][i]; }
+    const int pp = parity;   // the next pass (or the leftover) posts to the other slots
+    parity ^= 1;
+    if (NU == 0) break;
+    const long long P = p - F;
+    int low = 0, high = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (fx[r] != 0) continue;
+      const double qi = (S > 0.0) ? (static_cast<double>(P) * s[r]) / S
+                                  : static_cast<double>(P / NU);
+      bud[r] = static_cast<int>(floor(qi));
+      if (qi < static_cast<double>(m)) { low = 1; fx[r] = -1; }
+      else if (qi > static_cast<double>(d_in)) { high = 1; fx[r] = -2; }
+    }
+    low = __any(low);
+    high = __any(high);
+    if (lane == 0) red_f[pp][wid] = (low ? 1 : 0) | (high ? 2 : 0);
+    __syncthreads();
+    int fl = 0;
+    for (int i = 0; i < NW; ++i) fl |= red_f[pp][i];
+    if (fl & 1) {
+      // rows below the floor are held at m; tentative caps are dropped
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (fx[r] == -1) { bud[r] = m; fx[r] = 1; }
+        else if (fx[r] == -2) fx[r] = 0;
+      }
+      continue;
+    }
+    if (fl & 2) {
+      // rows above the cap are held at d_in and rows at the floor released
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (fx[r] == -2) { bud[r] = d_in; fx[r] = 2; }
+        else if (fx[r] == 1) fx[r] = 0;
+      }
+      continue;
+    }
+    break;
+  }
+
+  // leftover: as adaalloc_kernel, with budget values [tid * vpt, (tid+1) * vpt)
+  const int vpt = (d_in + 1 + kAllocThreads - 1) / kAllocThreads;
+  const int v0 = tid * vpt, v1 = min(v0 + vpt, d_in + 1);
+  for (;;) {
+    long long tot = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (fx[r] != 3) tot += bud[r];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    if (lane == 0) red_l[parity][wid] = tot;
+    for (int v = tid; v <= d_in; v += kAllocThreads) hist[v] = 0;
+    if (tid == 0) vstar = -1;
+    __syncthreads();
+    long long TOT = 0;
+    for (int i = 0; i < NW; ++i) TOT += red_l[parity][i];
+    parity ^= 1;
+    const long long rem = p - TOT;
+    if (rem <= 0) break;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (fx[r] != 3 && bud[r] < d_in) atomicAdd(&hist[bud[r]], 1);
+    __syncthreads();
+    {
+      int h = 0;
+      for (int v = v0; v < v1; ++v) h += hist[v];
+      int all_h;
+      int before = block_excl_scan_i32(h, scan_tmp, &all_h);
+      for (int v = v0; v < v1; ++v) {
+        const int hv = hist[v];
+        if (hv > 0 && before < rem && before + hv >= rem) { vstar = v; below_star = before; }
+        before += hv;
+      }
+    }
+    __syncthreads();
+    const int vs = vstar;
+    if (vs < 0) {
+      // fewer eligible rows than the leftover: every eligible row gets one
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (fx[r] != 3 && bud[r] < d_in) bud[r] += 1;
+      __syncthreads();   // hist and vstar are read before the next pass resets them
+      continue;
+    }
+    const long long need = rem - below_star;   // rows at vs that get a unit
+    int eq = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) eq += (fx[r] != 3 && bud[r] == vs) ? 1 : 0;
+    int all_eq;
+    int rank = block_excl_scan_i32(eq, scan_tmp, &all_eq);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (fx[r] == 3) continue;
+      if (bud[r] < vs) {
+        bud[r] += 1;
+      } else if (bud[r] == vs) {
+        if (rank < need) bud[r] += 1;
+        ++rank;
+      }
+    }
+    __syncthreads();   // vstar / below_star are read before the next pass resets them
+  }
+
+  // row_ptr = exclusive scan of budgets
+  int sum = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (fx[r] != 3) sum += bud[r];
+  int total;
+  int pos = block_excl_scan_i32(sum, scan_tmp, &total);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (fx[r] == 3) continue;
+    row_ptr[r0 + r] = pos;
+    pos += bud[r];
+  }
+  if (tid == 0) row_ptr[d_out] = total;
+}
+
 hipError_t launch_adaalloc(const double* w, int d_out, int d_in, int64_t p, int m, double t,
                            int32_t* row_ptr, void* scratch, hipStream_t st) {
   char* base = static_cast<char*>(scratch);
   double* s = reinterpret_cast<double*>(base);
   int64_t* budget = reinterpret_cast<int64_t*>(base + static_cast<size_t>(d_out) * 8);
   int32_t* fixed = reinterpret_cast<int32_t*>(base + static_cast<size_t>(d_out) * 16);
+  if (d_out <= kAllocThreads * kAllocRegRows) {
+    hipLaunchKernelGGL(adaalloc_reg_kernel, dim3(1), dim3(kAllocThreads), 0, st, w, d_out, d_in,
+                       p, m, t, row_ptr);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(adaalloc_kernel, dim3(1), dim3(kAllocThreads), 0, st, w, d_out, d_in, p, m, t,
                      row_ptr, s, budget, fixed);
   return hipGetLastError();

@@ -108,3 +108,23 @@ def test_random_shapes_whole_path(q, seed):
     torch.cuda.synchronize()
     c_ref = O.sign_update(c_gpu, dc.cpu().numpy(), 1e-3)
     assert np.array_equal(c_new.cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("d_out,d_in,p", [
+    (16384, 16, 16384 * 5 + 777),     # the most rows the register allocator holds
+    (16385, 16, 16385 * 5 + 777),     # one more: the allocator that keeps rows in memory
+    (20000, 8, 20000 * 7 - 3),        # near the cap of 8 per row
+    (16384, 8, 16384 * 3 + 1)])       # near the floor of 3 per row
+def test_allocator_row_counts(q, d_out, d_in, p):
+    """Budgets and the whole index at the row counts where the allocator
+    switches from rows in registers to rows in memory."""
+    print("allocator", d_out, d_in, p, flush=True)
+    rng = np.random.default_rng(d_out + p)
+    dwq = (0.01 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    dwq[rng.choice(d_out, size=d_out // 50, replace=False)] *= 4.0
+    ref = O.init_select(dwq, p, m=3, with_diagnostics=True)
+    assert np.min(ref["budget_margin"]) > 1e-9, "ambiguous budget at this seed"
+    got = q.qwha_init_select(to_dev(dwq), p, 3, 1.0)
+    torch.cuda.synchronize()
+    for key in ("row_ptr", "E", "col_ptr", "csc_perm"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
