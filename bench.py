@@ -295,7 +295,8 @@ class Block:
             a["plan"] = torch.empty(nb, dtype=torch.uint8, device=self.dev)
             check(lib.qwha_plan_build(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
                                       a["col_ptr"].data_ptr(), a["perm"].data_ptr(), sp.d_in,
-                                      sp.d_out, sp.p, a["plan"].data_ptr(), nb, self.stream),
+                                      sp.d_out, sp.p, self.act_code, a["plan"].data_ptr(), nb,
+                                      self.stream),
                   "plan")
 
     def train_step(self, s):

@@ -239,7 +239,9 @@ qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t 
  *
  * qwha_plan_bytes: the plan's size for (d_in, d_out, p); 0 when out of range.
  * qwha_plan_build: builds the plan from row_ptr, E, col_ptr, csc_perm into
- *   `plan` (device, 256-byte aligned, at least qwha_plan_bytes). Rebuild it
+ *   `plan` (device, 256-byte aligned, at least qwha_plan_bytes) for
+ *   activations of type `act` (the backward stages bf16 dy as bf16, in its
+ *   own layout): the planned calls must pass the same act. Rebuild it
  *   whenever E changes.
  * qwha_fwd_plan: qwha_fwd on a plan: y (+)= alpha z F^T with z = FWHT(x)/d_in
  *   computed from x, or taken from z_in (a kept transform; x is then not
@@ -259,7 +261,7 @@ qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t 
 size_t qwha_plan_bytes(int32_t d_in, int32_t d_out, int64_t p);
 qwha_status qwha_plan_build(const int32_t* row_ptr, const int32_t* E, const int32_t* col_ptr,
                             const int32_t* csc_perm, int32_t d_in, int32_t d_out, int64_t p,
-                            void* plan, size_t plan_bytes, hipStream_t stream);
+                            qwha_dtype act, void* plan, size_t plan_bytes, hipStream_t stream);
 qwha_status qwha_fwd_plan(const void* x, const float* z_in, qwha_dtype act, int64_t T,
                           int32_t d_in, int32_t d_out, int64_t p, void* plan, const float* c,
                           float alpha, void* y, int32_t accumulate, float* z_out,

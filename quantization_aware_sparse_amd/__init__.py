@@ -339,15 +339,17 @@ def qwha_bwd_dz(z: Optional[torch.Tensor], dy: torch.Tensor, E, c, col_ptr, csc_
 
 # ---------------------------------------------------------------- plans
 def qwha_plan_build(row_ptr, E, col_ptr, csc_perm, d_in: int, d_out: int,
-                    plan: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    act=torch.bfloat16, plan: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Both SpMM streams of the adapter, built once from its frozen E (int32
-    [p][2]) with the init's row_ptr, col_ptr and csc_perm; returns the plan."""
+    [p][2]) with the init's row_ptr, col_ptr and csc_perm, for activations
+    of dtype `act` (the planned calls must use the same); returns the plan."""
     p = int(E.shape[0])
     need = lib.qwha_plan_bytes(d_in, d_out, p)
     if plan is None:
         plan = workspace(need, E.device)
+    code = 1 if act == torch.bfloat16 else 0
     check(lib.qwha_plan_build(_ptr(row_ptr), E.data_ptr(), _ptr(col_ptr), csc_perm.data_ptr(),
-                              d_in, d_out, p, plan.data_ptr(), plan.numel(), _stream()),
+                              d_in, d_out, p, code, plan.data_ptr(), plan.numel(), _stream()),
           "qwha_plan_build")
     return plan
 

@@ -69,7 +69,7 @@ SIGNATURES = {
                               c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "qwha_plan_bytes": (c_size_t, [c_int32, c_int32, c_int64]),
     "qwha_plan_build": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
-                                  c_int64, c_void_p, c_size_t, c_void_p]),
+                                  c_int64, c_int32, c_void_p, c_size_t, c_void_p]),
     "qwha_fwd_plan": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32, c_int64,
                                 c_void_p, c_void_p, c_float, c_void_p, c_int32, c_void_p,
                                 c_void_p, c_size_t, c_void_p]),

@@ -166,9 +166,13 @@ struct BwdWs {
 };
 // with_dc: the dz pass also forms the dc partials (one fp32 per nonzero and
 // token tile); without, it is the plain gather over entry pairs.
-BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p, bool with_dc) {
+// stage16: dy is bf16 and the dc pass keeps it as bf16 in LDS (blocks of 128
+// columns); its prepared stream is no larger than the fp32 layout's, which
+// the size queries use.
+BwdWs bwd_ws(int64_t T, int32_t d_in, int32_t d_out, int64_t p, bool with_dc,
+             bool stage16 = false) {
   BwdWs l;
-  l.plan = spmm_plan(T, d_out, d_in, p, with_dc);
+  l.plan = spmm_plan(T, d_out, d_in, p, with_dc, with_dc && stage16);
   const size_t zb = align256(static_cast<size_t>(T) * d_in * 4);
   l.z = 0;
   l.dz = zb;
@@ -793,7 +797,7 @@ qwha_status bwd_impl(const void* x, const float* z_in, const void* dy, qwha_dtyp
     else
       QWHA_NEED(x, 16);
   }
-  const BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr);
+  const BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr, act == QWHA_BF16);
   if (workspace == nullptr || workspace_bytes < l.total)
     return fail(QWHA_ERR_WORKSPACE, "bwd workspace needs %zu bytes", l.total);
   QWHA_NEED(workspace, 256);
@@ -899,7 +903,7 @@ qwha_status qwha_bwd_dz(const float* z, const void* dy, qwha_dtype act, int64_t 
   if (dc != nullptr) QWHA_NEED(z, 16);
   // z and dz belong to the caller: the workspace holds the prepared stream
   // and the dc partials only
-  BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr);
+  BwdWs l = bwd_ws(T, d_in, d_out, p, dc != nullptr, act == QWHA_BF16);
   l.total -= l.prep;
   l.partial -= l.prep;
   l.prep = 0;
@@ -938,13 +942,14 @@ size_t qwha_plan_bytes(int32_t d_in, int32_t d_out, int64_t p) {
 
 qwha_status qwha_plan_build(const int32_t* row_ptr, const int32_t* E, const int32_t* col_ptr,
                             const int32_t* csc_perm, int32_t d_in, int32_t d_out, int64_t p,
-                            void* plan, size_t plan_bytes, hipStream_t stream) {
+                            qwha_dtype act, void* plan, size_t plan_bytes, hipStream_t stream) {
   g_err[0] = 0;
   int log_n;
   int nblk;
   QWHA_TRY(check_width(d_out, d_in, &log_n, &nblk));
   QWHA_TRY(check_p(p, d_out, d_in));
   QWHA_TRY(check_stream_p(p));
+  QWHA_TRY(check_dt(act, "act"));
   QWHA_NEED(row_ptr, 4);
   QWHA_NEED(col_ptr, 4);
   if (p > 0) {
@@ -958,7 +963,9 @@ qwha_status qwha_plan_build(const int32_t* row_ptr, const int32_t* E, const int3
   QWHA_TRY(hip_check(launch_prep_structure(row_ptr, E, nullptr, d_out, p, l.pf,
                                            at(plan, l.fwd), stream),
                      "plan (rows of F)"));
-  return hip_check(launch_prep_structure(col_ptr, E, csc_perm, d_in, p, l.pb, at(plan, l.bwd),
+  // the backward's layout follows the activations' type (bf16 dy staged as bf16)
+  const SpmmPlan pb = spmm_plan(0, d_out, d_in, p, true, act == QWHA_BF16);
+  return hip_check(launch_prep_structure(col_ptr, E, csc_perm, d_in, p, pb, at(plan, l.bwd),
                                          stream),
                    "plan (columns of F)");
 }
@@ -1046,11 +1053,13 @@ qwha_status qwha_bwd_plan(const float* z, const void* dy, qwha_dtype act, int64_
   if (p > 0) QWHA_NEED(c, 4);
   const PlanLayout l0 = plan_layout(d_in, d_out, p);
   const void* prep_b = at(plan, l0.bwd);
+  const bool b16 = act == QWHA_BF16;
   if (T == 0) {
     if (p > 0)
       return hip_check(launch_dc_reduce(nullptr, 0, p,
-                                        spmm_prep_korig(prep_b, p, d_in, l0.pb), alpha, dc,
-                                        stream),
+                                        spmm_prep_korig(prep_b, p, d_in,
+                                                        spmm_plan(0, d_out, d_in, p, true, b16)),
+                                        alpha, dc, stream),
                        "dc zero");
     return QWHA_OK;
   }
@@ -1058,7 +1067,7 @@ qwha_status qwha_bwd_plan(const float* z, const void* dy, qwha_dtype act, int64_
   QWHA_NEED(dy, 16);
   if (dx != nullptr) QWHA_NEED(dx, 16);
   if (dz != nullptr) QWHA_NEED(dz, 16);
-  const SpmmPlan pb = spmm_plan(T, d_out, d_in, p, true);
+  const SpmmPlan pb = spmm_plan(T, d_out, d_in, p, true, b16);
   const size_t zb = dz ? 0 : align256(static_cast<size_t>(T) * d_in * 4);
   const size_t total = zb + align256(static_cast<size_t>(pb.ntiles) * static_cast<size_t>(p) * 4);
   if (workspace == nullptr || workspace_bytes < total)

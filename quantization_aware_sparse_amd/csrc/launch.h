@@ -96,8 +96,11 @@ struct SpmmPlan {
   int64_t ntiles;
   int seg_mult;  // (row, block) segments padded with zero entries to a multiple of this
   int ptr_stride;  // per-block segment table stride (>= n_out + 1)
+  int esz;       // bytes per staged source element (4: fp32, 2: bf16 kept as bf16)
 };
-SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc);
+// stage16: the product with dc partials on a bf16 source, staged as bf16 in
+// blocks of 128 columns (same LDS bytes as 64 fp32 columns)
+SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc, bool stage16 = false);
 size_t spmm_prep_bytes(int64_t nnz, int n_out, const SpmmPlan& pl);
 // index k in E of each entry of the prepared stream (stream order)
 const int32_t* spmm_prep_korig(const void* prep, int64_t nnz, int n_out, const SpmmPlan& pl);

@@ -48,6 +48,7 @@ constexpr int kPad = 16;          // padding entries after the stream
 // wave-uniform rows (plain SpMM)
 constexpr int kRT = 256;          // tokens per tile: 64 lanes x 4
 constexpr int kRJB = 64;          // source columns per staged block (64 KiB fp32)
+constexpr int kRJB16 = 128;       // the same for a bf16 source kept as bf16 (64 KiB)
 constexpr int kRW = 16;           // waves per workgroup
 constexpr int kRR = 16;           // output rows per wave
 constexpr int kRRdc = 8;          // output rows per wave with dc partials
@@ -62,7 +63,7 @@ constexpr int kMaxBlk = 256;      // blocks held in a workgroup's run table
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
+SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc, bool stage16) {
   (void)nnz;
   SpmmPlan pl;
   // wave-uniform rows: 256-token tiles, 64-column blocks; the plain product
@@ -70,7 +71,8 @@ SpmmPlan spmm_plan(int64_t T, int n_src, int n_out, int64_t nnz, bool dc) {
   // partials single entries (one partial per real entry)
   pl.kind = dc ? 2 : 1;
   pl.tt = kRT;
-  pl.jb = kRJB;
+  pl.jb = dc && stage16 ? kRJB16 : kRJB;
+  pl.esz = dc && stage16 ? 2 : 4;
   pl.rows_wg = dc ? kRW * kRRdc : kRW * kRR;
   pl.seg_mult = dc ? 1 : 2;
   pl.nblk = (n_src + pl.jb - 1) / pl.jb;
@@ -229,7 +231,8 @@ __global__ __launch_bounds__(1024) void blk_base_kernel(int32_t* __restrict__ ba
 // past the stream's end.
 __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __restrict__ c,
                                const int32_t* __restrict__ perm, int64_t nnz, int stride,
-                               int nblk, int jb, int tt, int mult, const int32_t* __restrict__ bptr,
+                               int nblk, int jb, int tt, int esz, int mult,
+                               const int32_t* __restrict__ bptr,
                                const int32_t* __restrict__ ptr, const int32_t* __restrict__ base,
                                int2* __restrict__ stream, int32_t* __restrict__ korig) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -246,7 +249,7 @@ __global__ void scatter_kernel(const int32_t* __restrict__ E, const float* __res
   const int first = bptr[r];
   const int64_t pos = static_cast<int64_t>(base[b]) +
                       ptr[static_cast<int64_t>(b) * stride + o] + (q - first);
-  stream[pos] = make_int2((col - b * jb) * tt * 4, c ? __float_as_int(c[k]) : 0);
+  stream[pos] = make_int2((col - b * jb) * tt * esz, c ? __float_as_int(c[k]) : 0);
   if (korig) korig[pos] = static_cast<int32_t>(k);
   if (mult > 1) {
     const int last = bptr[r + 1] - 1;
@@ -276,7 +279,7 @@ static hipError_t prep_common(const int32_t* seg_ptr, const int32_t* E, const fl
   hipLaunchKernelGGL(blk_base_kernel, dim3(1), dim3(1024), 0, s, base, pl.nblk);
   const int64_t nthreads = nnz > 0 ? nnz : 1;
   hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
-                     0, s, E, c, perm, nnz, pl.ptr_stride, pl.nblk, pl.jb, pl.tt,
+                     0, s, E, c, perm, nnz, pl.ptr_stride, pl.nblk, pl.jb, pl.tt, pl.esz,
                      pl.seg_mult, bptr, ptr, base, at<int2>(prep, l.stream),
                      with_korig ? at<int32_t>(prep, l.korig) : nullptr);
   return hipGetLastError();
@@ -704,18 +707,31 @@ __device__ __forceinline__ float wave_total_lane63(float v) {
   return v;   // lane 63: the sum over all 64 lanes
 }
 
+// The 4 tokens of a lane from a staged row: fp32 (16 bytes) or bf16 kept as
+// bf16 (8 bytes, widened exactly: a bf16 is the top half of its fp32).
+template <bool B16>
+__device__ __forceinline__ float4 lds_tok4(const char* sb, int off) {
+  if constexpr (B16) {
+    const uint2 q = *reinterpret_cast<const uint2*>(sb + off);
+    return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
+                       __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(sb + off);
+  }
+}
+
 // Entries are taken two at a time in stream order: a pair inside row RA, or
 // straddling from RA into the next row RB (RA's last entry and RB's first).
 // (off, val) hold the pair's offsets and values; the next pair's offsets are
 // read while this pair's LDS reads are in flight and its values after the
 // FMAs. Lane 63 stores the two dc partials.
-template <int RA, int RB>
+template <int RA, int RB, bool B16>
 __device__ __forceinline__ void dc_pair(float (&acc)[kRRdc][4], const float (&zr)[kRRdc][4],
                                         const char* sb, const int* offs, const int* vals, int j,
                                         int2& off, int2& val, float* __restrict__ prow, int i,
                                         int lane) {
-  const float4 z0 = lds4(sb, off.x);
-  const float4 z1 = lds4(sb, off.y);
+  const float4 z0 = lds_tok4<B16>(sb, off.x);
+  const float4 z1 = lds_tok4<B16>(sb, off.y);
   off = make_int2(offs[j + 2], offs[j + 3]);
   asm volatile("" ::: "memory");
   fma4(acc[RA], __int_as_float(val.x), z0);
@@ -738,12 +754,12 @@ __device__ __forceinline__ void dc_pair(float (&acc)[kRRdc][4], const float (&zr
 }
 
 // One entry of row RA (its row's last, with no next row to pair with).
-template <int RA>
+template <int RA, bool B16>
 __device__ __forceinline__ void dc_single(float (&acc)[kRRdc][4], const float (&zr)[kRRdc][4],
                                           const char* sb, const int* offs, const int* vals, int j,
                                           int2& off, int2& val, float* __restrict__ prow, int i,
                                           int lane) {
-  const float4 z0 = lds4(sb, off.x);
+  const float4 z0 = lds_tok4<B16>(sb, off.x);
   off = make_int2(offs[j + 1], offs[j + 2]);
   asm volatile("" ::: "memory");
   fma4(acc[RA], __int_as_float(val.x), z0);
@@ -759,7 +775,7 @@ __device__ __forceinline__ void dc_single(float (&acc)[kRRdc][4], const float (&
 
 // The wave's rows in one block: row r owns entries [sg[r], sg[r+1]) of the
 // workgroup's run, of which [c0, c0 + kEntCap) are staged (offs, vals).
-template <typename Mid>
+template <bool B16, typename Mid>
 __device__ __forceinline__ void rows_entries_dc(float (&acc)[kRRdc][4],
                                                 const float (&zr)[kRRdc][4],
                                                 const int (&sg)[kRRdc + 1], int c0,
@@ -776,18 +792,19 @@ __device__ __forceinline__ void rows_entries_dc(float (&acc)[kRRdc][4],
   static_for<0, kRRdc>([&](auto rc) {
     constexpr int r = decltype(rc)::value;
     const int hi = clampc(sg[r + 1]);
-    for (; i + 1 < hi; i += 2) dc_pair<r, r>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+    for (; i + 1 < hi; i += 2)
+      dc_pair<r, r, B16>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
     if (i < hi) {
       bool paired = false;
       if constexpr (r + 1 < kRRdc) {
         if (i + 1 < clampc(sg[r + 2])) {   // row r+1 is not empty: pair across
-          dc_pair<r, r + 1>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+          dc_pair<r, r + 1, B16>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
           i += 2;
           paired = true;
         }
       }
       if (!paired) {
-        dc_single<r>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
+        dc_single<r, B16>(acc, zr, sb, offs, vals, i, off, val, prow, i, lane);
         i += 1;
       }
     }
@@ -859,7 +876,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
       }
     };
     const int run = uniform(segs[buf][kRW * kRRdc]);
-    rows_entries_dc(acc, zr, sg, 0, sb, pairs[buf], prow, lane, mid);
+    rows_entries_dc<false>(acc, zr, sg, 0, sb, pairs[buf], prow, lane, mid);
     for (int c0 = kEntCap; c0 < run; c0 += kEntCap) {
       __syncthreads();
       const int t = threadIdx.x;
@@ -870,7 +887,7 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
         RowsMeta<kRW * kRRdc, true>::store_pair(pairs[buf], t, e);
       }
       __syncthreads();
-      rows_entries_dc(acc, zr, sg, c0, sb, pairs[buf], prow, lane, [] {});
+      rows_entries_dc<false>(acc, zr, sg, c0, sb, pairs[buf], prow, lane, [] {});
     }
     if (more) {
       pf.store(nst, T, n_src, t0, nb, 1);
@@ -943,6 +960,231 @@ __global__ __launch_bounds__(kRW * 64) void rows_dc_kernel(
   }
 }
 
+// Staging of a 128-column block of a bf16 source kept as bf16: row jj of the
+// block holds the 256 tokens of column jj as 128 dwords (tokens 2i and 2i+1
+// in dword i), 512 bytes. Thread tid takes the token pair tp = tid % 128 and
+// columns 16g .. 16g+15 (g = tid / 128) in two parts of 8: per part one
+// 16-byte load per token and one dword store per column (a wave writes 256
+// contiguous bytes of a row).
+template <bool VEC_OK>
+struct StageB16 {
+  uint4 ra, rb;   // the part's 8 columns of tokens 2tp and 2tp+1
+
+  static __device__ __forceinline__ bool whole(int64_t T, int n_src, int64_t t0, int b) {
+    return VEC_OK && t0 + kRT <= T && (b + 1) * kRJB16 <= n_src;
+  }
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t T, int n_src,
+                                       int64_t t0, int b, int h) {
+    const int tp = threadIdx.x & 127, g = threadIdx.x >> 7;
+    const int col = b * kRJB16 + g * 16 + h * 8;
+    const int64_t ta = t0 + 2 * tp;
+    if (whole(T, n_src, t0, b)) {
+      ra = *reinterpret_cast<const uint4*>(src + ta * n_src + col);
+      rb = *reinterpret_cast<const uint4*>(src + (ta + 1) * n_src + col);
+      return;
+    }
+    const int64_t tA = ta < T ? ta : T - 1, tB = ta + 1 < T ? ta + 1 : T - 1;
+    if constexpr (VEC_OK) {
+      // n_src is a multiple of 8: the part is wholly inside or wholly past it
+      const int cc = col + 8 <= n_src ? col : n_src - 8;
+      ra = *reinterpret_cast<const uint4*>(src + tA * n_src + cc);
+      rb = *reinterpret_cast<const uint4*>(src + tB * n_src + cc);
+    } else {
+      uint32_t wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cc = col + e < n_src ? col + e : n_src - 1;
+        wa[e >> 1] |= static_cast<uint32_t>(src[tA * n_src + cc]) << (16 * (e & 1));
+        wb[e >> 1] |= static_cast<uint32_t>(src[tB * n_src + cc]) << (16 * (e & 1));
+      }
+      ra = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+      rb = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    }
+  }
+
+  __device__ __forceinline__ void store(uint32_t* __restrict__ st, int64_t T, int n_src, int64_t t0,
+                                        int b, int h) const {
+    const int tp = threadIdx.x & 127, g = threadIdx.x >> 7;
+    const int cl = g * 16 + h * 8;
+    const uint32_t a[4] = {ra.x, ra.y, ra.z, ra.w};
+    const uint32_t c[4] = {rb.x, rb.y, rb.z, rb.w};
+    if (whole(T, n_src, t0, b)) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st[(cl + 2 * k) * (kRT / 2) + tp] = (a[k] & 0xFFFFu) | (c[k] << 16);
+        st[(cl + 2 * k + 1) * (kRT / 2) + tp] = (a[k] >> 16) | (c[k] & 0xFFFF0000u);
+      }
+      return;
+    }
+    const uint32_t mA = t0 + 2 * tp < T ? 0xFFFFu : 0u;
+    const uint32_t mB = t0 + 2 * tp + 1 < T ? 0xFFFF0000u : 0u;
+    const int col = b * kRJB16 + cl;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = VEC_OK ? (col + 8 <= n_src) : (col + 2 * k + e < n_src);
+        const uint32_t lo = e ? (a[k] >> 16) : (a[k] & 0xFFFFu);
+        const uint32_t hi = e ? (c[k] & 0xFFFF0000u) : (c[k] << 16);
+        st[(cl + 2 * k + e) * (kRT / 2) + tp] = ok ? ((lo & mA) | (hi & mB)) : 0u;
+      }
+    }
+  }
+};
+
+// The backward with dc partials on a bf16 source, staged as bf16 in blocks
+// of 128 columns (the same LDS bytes as 64 fp32 columns, twice the entries
+// per row and block to walk between barriers); dy widens to fp32 exactly, so
+// every product and sum is the same as rows_dc_kernel's.
+template <bool VEC_OK>
+__global__ __launch_bounds__(kRW * 64) void rows_dc16_kernel(
+    const uint16_t* __restrict__ src, int64_t T, int n_src, const int2* __restrict__ stream,
+    const int32_t* __restrict__ ptr, const int32_t* __restrict__ base, int64_t nnz, int n_out,
+    int ptr_stride, int nblk, float* __restrict__ out, const float* __restrict__ zsrc,
+    float* __restrict__ partial, float alpha, int accumulate) {
+  __shared__ __align__(16) uint32_t stage[2][kRJB16 * kRT / 2];
+  __shared__ int4 pairs[2][kEntCap / 2 + 1];   // + the entries read past the end
+  __shared__ int segs[2][kRW * kRRdc + 1];
+  __shared__ int4 runs[kMaxBlk];
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kRT;
+  const int rg0 = static_cast<int>(blockIdx.y) * (kRW * kRRdc);
+  const int row0 = rg0 + w * kRRdc;
+
+  float acc[kRRdc][4], zr[kRRdc][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * lane + q;
+#pragma unroll
+    for (int r = 0; r < kRRdc; ++r) {
+      acc[r][q] = 0.f;
+      zr[r][q] = (t < T && row0 + r < n_out) ? zsrc[t * n_out + row0 + r] : 0.f;
+    }
+  }
+
+  StageB16<VEC_OK> pf;
+  RowsMeta<kRW * kRRdc, true> meta;
+  const bool tab = nblk <= kMaxBlk;
+  if (tab) RowsMeta<kRW * kRRdc, true>::build_runs(runs, ptr, base, ptr_stride, rg0, nblk);
+  __syncthreads();
+  meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pf.load(src, T, n_src, t0, 0, h);
+    pf.store(stage[0], T, n_src, t0, 0, h);
+  }
+  meta.store(segs[0], pairs[0]);
+  int k0n = meta.k0;   // k0 of the block staged next
+  if (nblk > 1) {
+    pf.load(src, T, n_src, t0, 1, 0);
+    meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, 1);
+  }
+  for (int b = 0; b < nblk; ++b) {
+    __syncthreads();
+    const int k0 = k0n;
+    const bool more = b + 1 < nblk;
+    const int nb = b + 1;
+    uint32_t* nst = stage[nb & 1];
+    const int buf = b & 1;
+    int sg[kRRdc + 1];
+#pragma unroll
+    for (int r = 0; r <= kRRdc; ++r) sg[r] = uniform(segs[buf][w * kRRdc + r]);
+    const char* sb = reinterpret_cast<const char*>(stage[buf]) + lane * 8;
+    float* prow = partial + tile * nnz + k0;
+    auto mid = [&]() {
+      if (more) {
+        pf.store(nst, T, n_src, t0, nb, 0);
+        pf.load(src, T, n_src, t0, nb, 1);
+      }
+    };
+    const int run = uniform(segs[buf][kRW * kRRdc]);
+    rows_entries_dc<true>(acc, zr, sg, 0, sb, pairs[buf], prow, lane, mid);
+    for (int c0 = kEntCap; c0 < run; c0 += kEntCap) {
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < kEntCap / 2 + 1) {
+        const int4 e = t < kEntCap / 2 && c0 + 2 * t < run
+                           ? *reinterpret_cast<const int4*>(stream + k0 + c0 + 2 * t)
+                           : make_int4(0, 0, 0, 0);
+        RowsMeta<kRW * kRRdc, true>::store_pair(pairs[buf], t, e);
+      }
+      __syncthreads();
+      rows_entries_dc<true>(acc, zr, sg, c0, sb, pairs[buf], prow, lane, [] {});
+    }
+    if (more) {
+      pf.store(nst, T, n_src, t0, nb, 1);
+      meta.store(segs[nb & 1], pairs[nb & 1]);
+      k0n = meta.k0;
+      if (nb + 1 < nblk) {   // registers only: nothing in LDS is touched
+        pf.load(src, T, n_src, t0, nb + 1, 0);
+        meta.load(stream, ptr, base, runs, tab, ptr_stride, rg0, nb + 1);
+      }
+    }
+  }
+
+  // epilogue. A whole tile goes through LDS, 128 tokens at a time, laid out
+  // [token][row] (stride 129 floats), so that each token's 128 outputs leave
+  // as 512 contiguous bytes; otherwise each lane writes its own 8 rows.
+  if (t0 + kRT <= T && rg0 + kRW * kRRdc <= n_out && n_out % 4 == 0) {
+    constexpr int kEp = kRW * kRRdc + 1;
+    float* ep = reinterpret_cast<float*>(&stage[0][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // the staging buffers (or the previous half) are free
+      if ((lane >> 5) == h) {
+        const int lt = 4 * (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < kRRdc; ++r) ep[(lt + q) * kEp + w * kRRdc + r] = acc[r][q];
+      }
+      __syncthreads();
+      for (int task = threadIdx.x; task < (kRT / 2) * (kRW * kRRdc / 4); task += kRW * 64) {
+        const int tt = task / (kRW * kRRdc / 4);
+        const int c4 = task % (kRW * kRRdc / 4);
+        const float* e = ep + tt * kEp + 4 * c4;
+        float4* d = reinterpret_cast<float4*>(out + (t0 + (kRT / 2) * h + tt) * n_out + rg0 +
+                                              4 * c4);
+        float4 v = make_float4(alpha * e[0], alpha * e[1], alpha * e[2], alpha * e[3]);
+        if (accumulate) {
+          const float4 a = *d;
+          v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+        }
+        *d = v;
+      }
+    }
+    return;
+  }
+  const bool vec = row0 + kRRdc <= n_out && n_out % 4 == 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * lane + q;
+    if (t >= T) continue;
+    float* dst = out + t * n_out;
+    if (vec) {
+      float4* d = reinterpret_cast<float4*>(dst + row0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float4 v = make_float4(alpha * acc[4 * h][q], alpha * acc[4 * h + 1][q],
+                               alpha * acc[4 * h + 2][q], alpha * acc[4 * h + 3][q]);
+        if (accumulate) {
+          const float4 a = d[h];
+          v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+        }
+        d[h] = v;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kRRdc; ++r)
+        if (row0 + r < n_out)
+          dst[row0 + r] = alpha * acc[r][q] + (accumulate ? dst[row0 + r] : 0.f);
+    }
+  }
+}
+
 template <typename SrcT>
 static hipError_t rows_dc_t(const void* src, int64_t T, int n_src, const void* prep, int64_t nnz,
                             int n_out, const SpmmPlan& pl, void* out, const float* zsrc,
@@ -953,6 +1195,24 @@ static hipError_t rows_dc_t(const void* src, int64_t T, int n_src, const void* p
   const dim3 grid(static_cast<unsigned>(pl.ntiles), gy);
   constexpr int VEC = 16 / static_cast<int>(sizeof(SrcT));
   const bool vec_ok = (n_src % VEC) == 0 && n_src >= VEC;
+  if constexpr (sizeof(SrcT) == 2) {
+    if (pl.jb == kRJB16) {
+      if (vec_ok)
+        hipLaunchKernelGGL((rows_dc16_kernel<true>), grid, dim3(kRW * 64), 0, s,
+                           static_cast<const uint16_t*>(src), T, n_src, at<int2>(pp, l.stream),
+                           at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
+                           pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial,
+                           alpha, accumulate);
+      else
+        hipLaunchKernelGGL((rows_dc16_kernel<false>), grid, dim3(kRW * 64), 0, s,
+                           static_cast<const uint16_t*>(src), T, n_src, at<int2>(pp, l.stream),
+                           at<int32_t>(pp, l.ptr), at<int32_t>(pp, l.base), nnz, n_out,
+                           pl.ptr_stride, pl.nblk, static_cast<float*>(out), zsrc, partial,
+                           alpha, accumulate);
+      return hipGetLastError();
+    }
+  }
+  if (pl.jb != kRJB || pl.esz != 4) return hipErrorInvalidValue;
   if (vec_ok)
     hipLaunchKernelGGL((rows_dc_kernel<SrcT, true>), grid, dim3(kRW * 64), 0, s,
                        static_cast<const SrcT*>(src), T, n_src, at<int2>(pp, l.stream),

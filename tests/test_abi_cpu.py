@@ -168,11 +168,12 @@ def test_plan_validation(q):
 
     def build(**kw):
         a = dict(row_ptr=FAKE, E=FAKE, col_ptr=FAKE, perm=FAKE, d_in=256, d_out=256, p=2048,
-                 plan=FAKE, nb=0)
+                 act=1, plan=FAKE, nb=0)
         a.update(kw)
         return q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["perm"], a["d_in"],
-                                 a["d_out"], a["p"], a["plan"], a["nb"], None)
+                                 a["d_out"], a["p"], a["act"], a["plan"], a["nb"], None)
     assert build(d_in=12) == SHAPE
+    assert build(act=5) == DTYPE
     assert build(p=256 * 256 + 1) == BUDGET
     assert build(E=None) == INVALID
     assert build() == WORKSPACE

@@ -96,7 +96,8 @@ def test_plan_matches_unplanned_calls(q, d_out, d_in, p, T, act, alpha):
     print("plan", d_out, d_in, p, T, act, alpha, flush=True)
     r, a = adapter(d_out, d_in, p, d_out + d_in + T)
     x, dy = dev(acts(T, d_in, act, 1)), dev(acts(T, d_out, act, 2))
-    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out)
+    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out,
+                             act=x.dtype)
     assert_same(unplanned(q, a, x, dy, d_out, alpha), planned(q, plan, a, x, dy, d_out, alpha))
     # c moves, E does not: the same plan serves the next step
     for step in range(2):
@@ -113,7 +114,8 @@ def test_plan_accumulates(q):
     print("plan accumulate", flush=True)
     r, a = adapter(d_out, d_in, p, 11)
     x, dy = dev(acts(T, d_in, "bf16", 3)), dev(acts(T, d_out, "bf16", 4))
-    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out)
+    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out,
+                             act=x.dtype)
     y0 = dev(acts(T, d_out, "bf16", 5))
     dx0 = dev(acts(T, d_in, "bf16", 6))
     dz0 = torch.from_numpy(np.random.default_rng(7).standard_normal((T, d_in))
@@ -143,7 +145,8 @@ def test_plan_against_oracle(q, act):
     r, a = adapter(d_out, d_in, p, 21)
     xa, dya = acts(T, d_in, act, 8), acts(T, d_out, act, 9)
     x, dy = dev(xa), dev(dya)
-    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out)
+    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out,
+                             act=x.dtype)
     z = torch.empty((T, d_in), dtype=torch.float32, device=DEV)
     q.qwha_fwd_plan(x, plan, a["c"], d_out, alpha, z_out=z)
     _, dc = q.qwha_bwd_plan(z, dy, plan, a["c"], alpha, need_dx=False)
@@ -160,13 +163,16 @@ def test_plan_against_oracle(q, act):
     assert_f32_close(host(dc), dc_ref, "dc")
 
 
-def test_plan_zero_tokens(q):
+@pytest.mark.parametrize("adt", ["f32", "bf16"])
+def test_plan_zero_tokens(q, adt):
     """T = 0: no output rows; dc is all zeros, written through the plan's map."""
     d_out, d_in, p = 300, 256, 2500
+    act = torch.bfloat16 if adt == "bf16" else torch.float32
     r, a = adapter(d_out, d_in, p, 31)
-    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out)
+    plan = q.qwha_plan_build(a["row_ptr"], a["E"], a["col_ptr"], a["csc_perm"], d_in, d_out,
+                             act=act)
     z = torch.empty((0, d_in), dtype=torch.float32, device=DEV)
-    dy = torch.empty((0, d_out), dtype=torch.float32, device=DEV)
+    dy = torch.empty((0, d_out), dtype=act, device=DEV)
     dc = torch.full((p,), 7.0, dtype=torch.float32, device=DEV)
     q.qwha_bwd_plan(z, dy, plan, a["c"], 1.0, dc=dc)
     torch.cuda.synchronize()

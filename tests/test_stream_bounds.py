@@ -29,15 +29,15 @@ RW, RR, RRDC = 16, 16, 8          # waves per workgroup, rows per wave (plain / 
 ENT_CAP, PAD = 1536, 16           # staged entries per block, zero entries past the stream
 
 
-def plan(n_src, n_out, nnz, dc):
+def plan(n_src, n_out, nnz, dc, jb=JB):
     rows_wg = RW * (RRDC if dc else RR)
-    nblk = -(-n_src // JB)
+    nblk = -(-n_src // jb)
     n_out_pad = -(-n_out // rows_wg) * rows_wg
     mult = 1 if dc else 2
     segs = n_out * nblk
     cap = nnz + (mult - 1) * min(segs, nnz)
     return dict(rows_wg=rows_wg, nblk=nblk, stride=n_out_pad + 1, mult=mult, cap=cap,
-                n_out=n_out)
+                n_out=n_out, jb=jb)
 
 
 def prep(seg_ptr, keys, pl):
@@ -49,7 +49,7 @@ def prep(seg_ptr, keys, pl):
         lo, hi = int(seg_ptr[o]), int(seg_ptr[o + 1])
         seg = keys[lo:hi]
         assert np.all(np.diff(seg) > 0), "columns ascend within a segment"
-        bptr[o] = lo + np.searchsorted(seg, np.arange(nblk + 1) * JB, side="left")
+        bptr[o] = lo + np.searchsorted(seg, np.arange(nblk + 1) * pl["jb"], side="left")
     cnt = np.diff(bptr, axis=1).T                      # [nblk][n_out]
     cnt = -(-cnt // mult) * mult
     ptr = np.zeros((nblk, stride), dtype=np.int64)
@@ -61,15 +61,15 @@ def prep(seg_ptr, keys, pl):
     for o in range(n_out):
         lo, hi = int(seg_ptr[o]), int(seg_ptr[o + 1])
         q = np.arange(lo, hi)
-        b = keys[lo:hi] // JB
+        b = keys[lo:hi] // pl["jb"]
         pos[lo:hi] = base[b] + ptr[b, o] + (q - bptr[o, b])
     return bptr, ptr, base, pos
 
 
-def check_stream(seg_ptr, keys, n_src, dc, prep_fn=prep):
+def check_stream(seg_ptr, keys, n_src, dc, prep_fn=prep, jb=JB):
     n_out = len(seg_ptr) - 1
     nnz = len(keys)
-    pl = plan(n_src, n_out, nnz, dc)
+    pl = plan(n_src, n_out, nnz, dc, jb)
     bptr, ptr, base, pos = prep_fn(seg_ptr, keys, pl)
     nblk, stride, cap = pl["nblk"], pl["stride"], pl["cap"]
     # the scatter: every entry at its own position inside the stream, the
@@ -116,7 +116,9 @@ def csc_keys(E, perm):
 
 def both_directions(row_ptr, E, col_ptr, perm, d_out, d_in):
     check_stream(row_ptr.astype(np.int64), csr_keys(E), d_in, dc=False)
+    # the backward with dc: fp32 dy in 64-column blocks, bf16 dy in 128
     check_stream(col_ptr.astype(np.int64), csc_keys(E, perm), d_out, dc=True)
+    check_stream(col_ptr.astype(np.int64), csc_keys(E, perm), d_out, dc=True, jb=128)
 
 
 @pytest.mark.parametrize("d_out,d_in,p", [
