@@ -63,27 +63,92 @@ __device__ __forceinline__ void load16(const uint16_t* p, Acc* v) {
 }
 
 // ------------------------------------------------------- wave reductions
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Scans and sums go through DPP (register moves between lanes of a row of
+// 16, or from the last lane of a row to the rows after it), not through
+// LDS permutes: row_shr 1, 2, 4, 8 scan each row; row_bcast:15 into rows 1
+// and 3 and row_bcast:31 into rows 2 and 3 carry the rows' totals. Lanes a
+// shift moves in from outside their row read 0. The active lanes must be a
+// prefix of the wave (a whole wave, or the first k lanes of a workgroup's
+// last wave); sums are read from the last active lane.
+__device__ __forceinline__ int last_active_lane() {
+  return 63 - __builtin_clzll(__builtin_amdgcn_read_exec());
 }
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = true>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, BOUND);
+}
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = true>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROW_MASK, BOUND>(static_cast<int>(b));
+  const int hi = dpp_i32<CTRL, ROW_MASK, BOUND>(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
 }
 
 // Inclusive prefix sum across the wave (lane order).
 __device__ __forceinline__ int wave_incl_scan_i32(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v += dpp_i32<0x111>(v);
+  v += dpp_i32<0x112>(v);
+  v += dpp_i32<0x114>(v);
+  v += dpp_i32<0x118>(v);
+  v += dpp_i32<0x142, 0xA, false>(v);
+  v += dpp_i32<0x143, 0xC, false>(v);
   return v;
+}
+
+// Sum over the wave, the same value in every lane.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_i32(v), last_active_lane());
+}
+
+// fp64 sum over the wave (the scan's order: within rows of 16, then rows),
+// the same value in every lane.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0x111>(v);
+  v += dpp_f64<0x112>(v);
+  v += dpp_f64<0x114>(v);
+  v += dpp_f64<0x118>(v);
+  v += dpp_f64<0x142, 0xA, false>(v);
+  v += dpp_f64<0x143, 0xC, false>(v);
+  const long long b = __double_as_longlong(v);
+  const int last = last_active_lane();
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), last);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), last);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+// int64 sum over the wave, the same value in every lane.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = true>
+__device__ __forceinline__ long long dpp_i64(long long v) {
+  const int lo = dpp_i32<CTRL, ROW_MASK, BOUND>(static_cast<int>(v));
+  const int hi = dpp_i32<CTRL, ROW_MASK, BOUND>(static_cast<int>(v >> 32));
+  return (static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo);
+}
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+  v += dpp_i64<0x111>(v);
+  v += dpp_i64<0x112>(v);
+  v += dpp_i64<0x114>(v);
+  v += dpp_i64<0x118>(v);
+  v += dpp_i64<0x142, 0xA, false>(v);
+  v += dpp_i64<0x143, 0xC, false>(v);
+  const int last = last_active_lane();
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), last);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), last);
+  return (static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo);
+}
+
+// Largest unsigned 32-bit value over the wave, the same in every lane.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+  auto mx = [](unsigned a, int b) { return a > static_cast<unsigned>(b) ? a : static_cast<unsigned>(b); };
+  v = mx(v, dpp_i32<0x111>(static_cast<int>(v)));
+  v = mx(v, dpp_i32<0x112>(static_cast<int>(v)));
+  v = mx(v, dpp_i32<0x114>(static_cast<int>(v)));
+  v = mx(v, dpp_i32<0x118>(static_cast<int>(v)));
+  v = mx(v, dpp_i32<0x142, 0xA, false>(static_cast<int>(v)));
+  v = mx(v, dpp_i32<0x143, 0xC, false>(static_cast<int>(v)));
+  return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(v), last_active_lane()));
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

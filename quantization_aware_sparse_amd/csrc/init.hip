@@ -129,8 +129,7 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
       else { ps += s[i]; ++nu; }
     }
     ps = wave_sum_f64(ps);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) pf += __shfl_xor(pf, off, 64);
+    pf = wave_sum_i64(pf);
     nu = wave_sum_i32(nu);
     if (lane == 0) { red_d[wid] = ps; red_l[parity][wid] = pf; red_i[parity][wid] = nu; }
     if (tid < 4) flags[tid] = 0;
@@ -190,8 +189,7 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_kernel(
   for (;;) {
     long long tot = 0;
     for (int i = tid; i < d_out; i += kAllocThreads) tot += budget[i];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    tot = wave_sum_i64(tot);
     if (lane == 0) red_l[parity][wid] = tot;
     for (int v = tid; v <= d_in; v += kAllocThreads) hist[v] = 0;
     if (tid == 0) vstar = -1;
@@ -307,8 +305,7 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_reg_kernel(
       else if (fx[r] == 1 || fx[r] == 2) pf += bud[r];
     }
     ps = wave_sum_f64(ps);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) pf += __shfl_xor(pf, off, 64);
+    pf = wave_sum_i64(pf);
     nu = wave_sum_i32(nu);
     if (lane == 0) { red_d[parity][wid] = ps; red_l[parity][wid] = pf; red_i[parity][wid] = nu; }
     __syncthreads();
@@ -365,8 +362,7 @@ __global__ __launch_bounds__(kAllocThreads) void adaalloc_reg_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (fx[r] != 3) tot += bud[r];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    tot = wave_sum_i64(tot);
     if (lane == 0) red_l[parity][wid] = tot;
     for (int v = tid; v <= d_in; v += kAllocThreads) hist[v] = 0;
     if (tid == 0) vstar = -1;
@@ -483,8 +479,9 @@ __device__ __forceinline__ void hist_cross(const int* h, int k, int& b, int& abo
   const int s4 = c.x + c.y + c.z + c.w;
   const int incl = wave_incl_scan_i32(s4);
   const int L = wave_first_ge(incl, k);
-  const int before = __shfl(incl - s4, L);
-  const int x = __shfl(c.x, L), y = __shfl(c.y, L), z = __shfl(c.z, L), w = __shfl(c.w, L);
+  const int before = __builtin_amdgcn_readlane(incl - s4, L);
+  const int x = __builtin_amdgcn_readlane(c.x, L), y = __builtin_amdgcn_readlane(c.y, L);
+  const int z = __builtin_amdgcn_readlane(c.z, L), w = __builtin_amdgcn_readlane(c.w, L);
   int q, cnt;
   if (before + x >= k) { q = 0; cnt = x; }
   else if (before + x + y >= k) { q = 1; cnt = y; }
@@ -503,22 +500,22 @@ __device__ __forceinline__ bool radix_kth_largest(const unsigned long long (&key
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = (blockDim.x + 63) >> 6;
   const int tid = threadIdx.x, nth = blockDim.x;
-  unsigned long long m = 0;
+  // the largest exponent: the high 32 bits of the keys carry it (bits 20..30)
+  unsigned m = 0;
   if (active) {
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) m = key[r] > m ? key[r] : m;
+    for (int r = 0; r < EPT; ++r) {
+      const unsigned h = static_cast<unsigned>(key[r] >> 32);
+      m = h > m ? h : m;
+    }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(m, off, 64);
-    m = o > m ? o : m;
-  }
+  m = wave_max_u32(m);
   if (lane == 0) red64[wid] = m;
   for (int i = tid; i < 512; i += nth) hist[i] = 0;    // levels 0 and 1
   __syncthreads();
   unsigned long long kmax = 0;
   for (int i = 0; i < nw; ++i) kmax = red64[i] > kmax ? red64[i] : kmax;
-  const int emax = static_cast<int>(kmax >> 52);
+  const int emax = static_cast<int>(kmax >> 20);
   if (active) {
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {

@@ -708,7 +708,9 @@ hipError_t calib_rows_t(const double* M, const float* dWq, const double* delta, 
     return hipGetLastError();
   }
   if constexpr (L >= 6 && L <= 12) {
-    const int threads = nblk * F::TPR < 64 ? 64 : nblk * F::TPR;
+    // whole waves (the wave sums take every lane of a wave; threads past
+    // nblk * TPR hold no columns)
+    const int threads = (nblk * F::TPR + 63) / 64 * 64;
     const size_t lds = static_cast<size_t>(nblk) * F::LDS * sizeof(double);
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&calib_rows_kernel<L, true>),
