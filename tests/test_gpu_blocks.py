@@ -49,7 +49,9 @@ def test_init_select_block_widths(q, d_out, d_in, p):
     assert_init_equal(ref, got)
 
 
-@pytest.mark.parametrize("d_out,d_in,p", WIDTHS[:4])
+# (800, 6144, 60000): 2400 blocks of 2048 columns, more than the row kernel's
+# 2048 workgroups, so workgroups take several blocks of different rows
+@pytest.mark.parametrize("d_out,d_in,p", WIDTHS[:4] + [(800, 6144, 60000)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_materialize_block_widths(q, d_out, d_in, p, out):
     say("materialize block width", d_out, d_in, p, out)

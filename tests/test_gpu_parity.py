@@ -251,7 +251,12 @@ def test_init_global_configs(q, strategy, cfg):
 
 # ------------------------------------------------------------------ materialize
 @pytest.mark.parametrize("d_out,d_in,p", [(37, 2, 40), (300, 64, 2500), (17, 1024, 2000),
-                                          (3, 8192, 900), (2, 16384, 1000), (256, 256, 2048)])
+                                          (3, 8192, 900), (2, 16384, 1000), (256, 256, 2048),
+                                          # more nonzeros per row than the row kernel holds
+                                          # in registers (128 at 1024 columns)
+                                          (8, 1024, 4000),
+                                          # more rows than workgroups (1024 at 4096 columns)
+                                          (1500, 4096, 60000)])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_materialize(q, d_out, d_in, p, out_dt):
     say("materialize", d_out, d_in, p, out_dt)
