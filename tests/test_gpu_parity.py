@@ -132,6 +132,44 @@ def test_init_select_ties_zero_rows_and_bounds(q):
     assert_init_equal(ref, got)
 
 
+@pytest.mark.parametrize("d_in", [64, 1024, 3072])
+def test_init_select_wide_range_ties_and_cap(q, d_in):
+    """Selection edge rows in both selection orders (rows below 1024 columns
+    go back to natural order; from 1024 columns, and for the three blocks of
+    1024 of a 3072-wide row, the selection runs on the transform's order):
+    rows 5 and 6 have three large |C| and the rest about 20 octaves below, so
+    the k-th key lies past the radix select's first-level bins and the
+    bisection decides; row 3 is a spike (|C| flat: the boundary inside a run
+    of ties, lowest columns first); rows 11 and 12 are zero (the floor); row
+    20 dominates (the cap: every column taken)."""
+    d_out = 40
+    N = O.block_size(d_in)
+    dwq = _edge_dwq(d_out, d_in, 7 + d_in) * 0.01
+    n0 = float(np.median(np.linalg.norm(dwq, axis=1)))
+    for i in (5, 6):
+        L = 4 * n0 * np.sqrt(N / 3) * (1 + 0.1 * i)
+        C = L * 1e-6 * (1.0 + np.arange(d_in) / d_in)
+        C[[3, d_in // 2, d_in - 1]] = L
+        dwq[i] = (O.wht(C[None, :], d_in)[0] / N).astype(np.float32)
+    dwq[3] = 0.0
+    dwq[3, 9] = 4 * n0
+    dwq[11] = 0.0
+    dwq[12] = 0.0
+    dwq[20] = 50.0 * np.sign(dwq[20] + 1e-9)
+    p = d_in + d_out * d_in // 8
+    say("init wide/ties/cap", d_in, p)
+    ref, got = init_both(q, dwq, p, 3)
+    b = ref["budgets"]
+    assert b[20] == d_in and b[11] >= 3 and b[12] >= 3
+    for i in (5, 6):   # the k-th key sits more than 16 octaves below the largest
+        a = np.sort(np.abs(ref["C"][i]))[::-1]
+        assert 3 < b[i] < d_in and np.log2(a[0] / a[b[i] - 1]) > 16
+    assert np.min(ref["budget_margin"]) > 1e-9
+    gap = ref["boundary_gap"]
+    assert not np.any((gap > 0) & (gap < 1e-9))
+    assert_init_equal(ref, got)
+
+
 def test_init_select_temperature_two(q):
     dwq = _edge_dwq(100, 128, 3)
     say("init t=2")
