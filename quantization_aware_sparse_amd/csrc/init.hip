@@ -553,131 +553,13 @@ __device__ __forceinline__ bool radix_kth_largest(const unsigned long long (&key
   return true;
 }
 
-// tau for a row: the given global threshold (MODE 1, 2) or the k-th largest
-// key (MODE 0): the radix select, or, when its first level cannot place the
-// k-th key (the boundary lies 16 octaves below the largest key), a bisection
-// first on the top 32 bits of the keys (32-bit compares), then on the full
-// keys within that 2^32-wide range, stopping as soon as the keys >= lo are
-// exactly k. 0 < k < the row's length.
-template <int EPT, int MODE>
-__device__ __forceinline__ unsigned long long row_threshold(
-    const unsigned long long (&key)[EPT], bool active, int k,
-    const unsigned long long* __restrict__ gtau, int* hist, unsigned long long* red64, int* red,
-    int& parity) {
-  if (MODE != 0) return *gtau;
-  unsigned long long tau = 0;
-  if (radix_kth_largest<EPT>(key, active, k, hist, red64, &tau)) return tau;
-  auto count_ge32 = [&](unsigned m) {
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < EPT; ++r) cnt += __popcll(__ballot(static_cast<unsigned>(key[r] >> 32) >= m));
-    const int t = block_total_i32(cnt, red, parity);
-    parity ^= 1;
-    return t;
-  };
-  auto count_ge64 = [&](unsigned long long m) {
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < EPT; ++r) cnt += __popcll(__ballot(key[r] >= m));
-    const int t = block_total_i32(cnt, red, parity);
-    parity ^= 1;
-    return t;
-  };
-  // count(top32 >= lo32) >= k > count(top32 >= hi32); keys are < 2^63 and
-  // the keys of inactive threads are 0 (below every probe)
-  unsigned lo32 = 0, hi32 = 1u << 31;
-  int cnt_lo = -1;
-  while (hi32 - lo32 > 1 && cnt_lo != k) {
-    const unsigned mid = lo32 + ((hi32 - lo32) >> 1);
-    const int cnt = count_ge32(mid);
-    if (cnt >= k) { lo32 = mid; cnt_lo = cnt; } else { hi32 = mid; }
-  }
-  unsigned long long lo = static_cast<unsigned long long>(lo32) << 32;
-  unsigned long long hi = static_cast<unsigned long long>(hi32) << 32;
-  while (hi - lo > 1 && cnt_lo != k) {
-    const unsigned long long mid = lo + ((hi - lo) >> 1);
-    const int cnt = count_ge64(mid);
-    if (cnt >= k) { lo = mid; cnt_lo = cnt; } else { hi = mid; }
-  }
-  return lo;
-}
-
-// Ordered write of a row held in the transform's order: thread t = blk * TPR
-// + u (TPR a multiple of 64) holds columns c0 + r * TPR with c0 = blk * N + u,
-// so columns ascend with (blk, r, wave of the block, lane). Keys above tau are
-// taken, and of the keys equal to tau the first need = k - #(above) in column
-// order. Per register r a wave counts its keys above and equal to tau by
-// ballot; one scan over the (blk, r, wave) counts, packed as above | equal <<
-// 16 (both below 2^16: at most 16384 columns), gives every key the numbers
-// above and equal before it, and with them its output position
-// #(above before) + min(#(equal before), need).
-template <int EPT, int TPR>
-__device__ __forceinline__ void write_selection_strided(
-    const unsigned long long (&key)[EPT], const double (&v)[EPT], bool active, bool all,
-    bool none, unsigned long long tau, int k, int row, int base, int d_in, int c0,
-    int32_t* __restrict__ E, float* __restrict__ c) {
-  __shared__ int cnt[256];   // (blk * 16 + r) * waves_per_blk + wave: packed counts
-  __shared__ int total;
-  constexpr int kWpb = TPR / 64;
-  const int t = threadIdx.x, lane = t & 63;
-  const int blk = t / TPR, wb = (t % TPR) >> 6;
-  const int n = static_cast<int>(blockDim.x >> 6) * EPT;   // (blk, r, wave) entries
-  const unsigned long long below = (1ull << lane) - 1;
-  int pre[EPT];   // this lane's keys above | equal << 16 among lower lanes of its wave
-  unsigned gm = 0, em = 0;
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    const bool g = active && !all && !none && key[r] > tau;
-    const bool e = active && !all && !none && key[r] == tau;
-    const unsigned long long bg = __ballot(g), be = __ballot(e);
-    pre[r] = __popcll(bg & below) | (__popcll(be & below) << 16);
-    if (lane == 0) cnt[(blk * EPT + r) * kWpb + wb] = __popcll(bg) | (__popcll(be) << 16);
-    gm |= static_cast<unsigned>(g) << r;
-    em |= static_cast<unsigned>(e) << r;
-  }
-  __syncthreads();
-  if (t < 64) {   // wave 0: exclusive scan of the counts in place
-    int carry = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      const int x = i < n ? cnt[i] : 0;
-      const int incl = wave_incl_scan_i32(x);
-      if (i < n) cnt[i] = carry + incl - x;
-      carry += __builtin_amdgcn_readlane(incl, 63);
-    }
-    if (lane == 0) total = carry;
-  }
-  __syncthreads();
-  const int need = k - (total & 0xFFFF);
-  if (!active || none) return;
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    const int col = c0 + r * TPR;
-    int pos;
-    if (all) {
-      pos = col;
-    } else {
-      const int pr = cnt[(blk * EPT + r) * kWpb + wb];
-      const int gb = (pr & 0xFFFF) + (pre[r] & 0xFFFF);
-      const int eb = (pr >> 16) + (pre[r] >> 16);
-      if ((gm >> r) & 1u) pos = gb + (eb < need ? eb : need);
-      else if (((em >> r) & 1u) && eb < need) pos = gb + eb;
-      else continue;
-    }
-    E[2 * static_cast<int64_t>(base + pos)] = row;      // E needs only 4-byte alignment
-    E[2 * static_cast<int64_t>(base + pos) + 1] = col;
-    c[base + pos] = __double2float_rn(v[r]);
-  }
-  (void)d_in;
-}
-
 // ------------------------------------------------------------ selection
 // One workgroup per row i: C = dWq[i] H in fp64 (LDS-staged FWHT), then the
 // k = p_i columns first in the order (-|C_j|, j) are emitted ascending as
 // E rows (i, j) with c = fp32_RNE(C_j). The k-th largest magnitude tau is
-// found on the IEEE bit pattern of |C| (monotone for non-negative doubles;
-// +0 and -0 share the pattern 0); every |C| > tau is taken and the
-// lowest-index columns with |C| == tau fill the rest.
+// found by bisection on the IEEE bit pattern of |C| (monotone for
+// non-negative doubles; +0 and -0 share the pattern 0); every |C| > tau is
+// taken and the lowest-index columns with |C| == tau fill the rest.
 template <int LOG_N>
 struct SelCfg {
   using F = Fwht<LOG_N>;
@@ -694,9 +576,8 @@ struct SelCfg {
 // BLOCKED: a row of nblk * N columns under the block-diagonal transform (nblk
 // Sylvester blocks of order N): thread t = blk * TPR + u transforms its part
 // of block blk in that block's slice of the dynamic LDS; the selection runs
-// over the whole row. With N >= 1024 the selection works on the transform's
-// output order (write_selection_strided); below that the row goes back to
-// natural order through LDS and thread t holds columns t*EPT .. t*EPT + EPT - 1.
+// over the whole row, and thread t holds columns t*EPT .. t*EPT + EPT - 1 in
+// both cases.
 template <int LOG_N, int MODE, bool BLOCKED>
 __global__ __launch_bounds__(BLOCKED ? 1024 : SelCfg<LOG_N>::BLOCK) void init_select_kernel(
     const float* __restrict__ dWq, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ E,
@@ -733,100 +614,129 @@ __global__ __launch_bounds__(BLOCKED ? 1024 : SelCfg<LOG_N>::BLOCK) void init_se
     for (int r = 0; r < F::EPT; ++r) v[r] = 0.0;
   }
   F::run(v, lds, u, active);
-  const bool all = (k >= d_in), none = (k <= 0);
-  int parity = 0;
-
-  if constexpr (F::TPR >= 64) {
-    // Rows of 1024 or more columns: select in the transform's own order,
-    // thread t = blk * TPR + u holding columns blk * N + u + r * TPR (whole
-    // waves per block), with no pass back to natural order.
-    const int blk = t / F::TPR;
-    unsigned long long key[F::EPT];
+  // back to natural order, then to "EPT consecutive columns per thread"
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) lds[F::pad(F::out_index(u, r))] = v[r];
+  }
+  __syncthreads();
+  unsigned long long key[F::EPT];
+  if (active) {
 #pragma unroll
     for (int r = 0; r < F::EPT; ++r) {
-      const int col = blk * F::N + u + r * F::TPR;
-      key[r] = !active ? 0ull
-               : MODE == 2
-                   ? ~splitmix64(seed, static_cast<unsigned long long>(row) * d_in + col)
+      v[r] = lds[F::pad(u * F::EPT + r)];
+      key[r] = MODE == 2
+                   ? ~splitmix64(seed, static_cast<unsigned long long>(row) * d_in + col0 + r)
                    : static_cast<unsigned long long>(__double_as_longlong(v[r])) &
                          0x7FFFFFFFFFFFFFFFull;
     }
-    const unsigned long long tau =
-        all || none ? 0ull : row_threshold<F::EPT, MODE>(key, active, k, gtau, hist, red64, red,
-                                                          parity);
-    write_selection_strided<F::EPT, F::TPR>(key, v, active, all, none, tau, k, row, base, d_in,
-                                            blk * F::N + u, E, c);
   } else {
-    // back to natural order, then to "EPT consecutive columns per thread"
-    __syncthreads();
-    if (active) {
 #pragma unroll
-      for (int r = 0; r < F::EPT; ++r) lds[F::pad(F::out_index(u, r))] = v[r];
-    }
-    __syncthreads();
-    unsigned long long key[F::EPT];
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < F::EPT; ++r) {
-        v[r] = lds[F::pad(u * F::EPT + r)];
-        key[r] = MODE == 2
-                     ? ~splitmix64(seed, static_cast<unsigned long long>(row) * d_in + col0 + r)
-                     : static_cast<unsigned long long>(__double_as_longlong(v[r])) &
-                           0x7FFFFFFFFFFFFFFFull;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < F::EPT; ++r) key[r] = 0;
-    }
-    unsigned long long tau = 0;
-    int need = 0;      // how many |C| == tau are taken (lowest index first)
-    if (!all && !none) {
-      tau = row_threshold<F::EPT, MODE>(key, active, k, gtau, hist, red64, red, parity);
-      int gt = 0;
-#pragma unroll
-      for (int r = 0; r < F::EPT; ++r) gt += __popcll(__ballot(active && key[r] > tau));
-      gt = block_total_i32(gt, red, parity);
-      parity ^= 1;
-      need = k - gt;
-    }
+    for (int r = 0; r < F::EPT; ++r) key[r] = 0;
+  }
 
-    // selection flags in column order
-    unsigned sel = 0;
-    int nsel = 0;
-    {
-      int neq = 0;
-      if (active && !all && !none) {
+  // tau = the k-th largest key: the largest t with count(key >= t) >= k,
+  // found by bisection, first on the top 32 bits of the keys (32-bit
+  // compares), then, only if the top bits leave more than k keys at the
+  // threshold, on the full keys within that 2^32-wide range. Counts go by
+  // wave ballots (one barrier per step); the search stops as soon as the
+  // keys >= lo are exactly k.
+  unsigned long long tau = 0;
+  int need = 0;      // how many |C| == tau are taken (lowest index first)
+  bool all = (k >= d_in), none = (k <= 0);
+  int parity = 0;
+  if (!all && !none && MODE != 0) {
+    tau = *gtau;
+    int gt = 0;
 #pragma unroll
-        for (int r = 0; r < F::EPT; ++r) neq += (key[r] == tau) ? 1 : 0;
-      }
-      int tot;
-      const int eq_before = block_excl_scan_i32(neq, scan_tmp, &tot);
-      if (active) {
-        int e = eq_before;
+    for (int r = 0; r < F::EPT; ++r) gt += __popcll(__ballot(active && key[r] > tau));
+    gt = block_total_i32(gt, red, parity);
+    parity ^= 1;
+    need = k - gt;
+  } else if (!all && !none &&
+             radix_kth_largest<F::EPT>(key, active, k, hist, red64, &tau)) {
+    const int gt = [&] {
+      int cnt = 0;
 #pragma unroll
-        for (int r = 0; r < F::EPT; ++r) {
-          bool take;
-          if (all) take = true;
-          else if (none) take = false;
-          else if (key[r] > tau) take = true;
-          else if (key[r] == tau) { take = e < need; ++e; }
-          else take = false;
-          if (take) { sel |= 1u << r; ++nsel; }
-        }
-      }
+      for (int r = 0; r < F::EPT; ++r) cnt += __popcll(__ballot(active && key[r] > tau));
+      return block_total_i32(cnt, red, parity);
+    }();
+    parity ^= 1;
+    need = k - gt;
+  } else if (!all && !none) {
+    auto count_ge32 = [&](unsigned m) {
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r)
+        cnt += __popcll(__ballot(static_cast<unsigned>(key[r] >> 32) >= m));
+      return block_total_i32(cnt, red, parity);
+    };
+    auto count_ge64 = [&](unsigned long long m) {
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) cnt += __popcll(__ballot(key[r] >= m));
+      return block_total_i32(cnt, red, parity);
+    };
+    // count(top32 >= lo32) >= k > count(top32 >= hi32); keys are < 2^63
+    unsigned lo32 = 0, hi32 = 1u << 31;
+    int cnt_lo = d_in;
+    while (hi32 - lo32 > 1 && cnt_lo != k) {
+      const unsigned mid = lo32 + ((hi32 - lo32) >> 1);
+      const int cnt = count_ge32(mid);
+      parity ^= 1;
+      if (cnt >= k) { lo32 = mid; cnt_lo = cnt; } else { hi32 = mid; }
+    }
+    unsigned long long lo = static_cast<unsigned long long>(lo32) << 32;
+    unsigned long long hi = static_cast<unsigned long long>(hi32) << 32;
+    while (hi - lo > 1 && cnt_lo != k) {
+      const unsigned long long mid = lo + ((hi - lo) >> 1);
+      const int cnt = count_ge64(mid);
+      parity ^= 1;
+      if (cnt >= k) { lo = mid; cnt_lo = cnt; } else { hi = mid; }
+    }
+    tau = lo;
+    const int gt = count_ge64(tau + 1);
+    parity ^= 1;
+    need = k - gt;
+  }
+
+  // selection flags in column order
+  unsigned sel = 0;
+  int nsel = 0;
+  {
+    int neq = 0;
+    if (active && !all && !none) {
+#pragma unroll
+      for (int r = 0; r < F::EPT; ++r) neq += (key[r] == tau) ? 1 : 0;
     }
     int tot;
-    const int pos0 = block_excl_scan_i32(nsel, scan_tmp, &tot);
+    const int eq_before = block_excl_scan_i32(neq, scan_tmp, &tot);
     if (active) {
-      int pos = base + pos0;
+      int e = eq_before;
 #pragma unroll
       for (int r = 0; r < F::EPT; ++r) {
-        if (sel & (1u << r)) {
-          E[2 * static_cast<int64_t>(pos)] = row;
-          E[2 * static_cast<int64_t>(pos) + 1] = col0 + r;
-          c[pos] = __double2float_rn(v[r]);
-          ++pos;
-        }
+        bool take;
+        if (all) take = true;
+        else if (none) take = false;
+        else if (key[r] > tau) take = true;
+        else if (key[r] == tau) { take = e < need; ++e; }
+        else take = false;
+        if (take) { sel |= 1u << r; ++nsel; }
+      }
+    }
+  }
+  int tot;
+  const int pos0 = block_excl_scan_i32(nsel, scan_tmp, &tot);
+  if (active) {
+    int pos = base + pos0;
+#pragma unroll
+    for (int r = 0; r < F::EPT; ++r) {
+      if (sel & (1u << r)) {
+        E[2 * static_cast<int64_t>(pos)] = row;
+        E[2 * static_cast<int64_t>(pos) + 1] = col0 + r;
+        c[pos] = __double2float_rn(v[r]);
+        ++pos;
       }
     }
   }
