@@ -10,6 +10,9 @@ under profiles/.
       what the same counter reads for a plain fp32 copy of known size
       (bench.py --calib-copy-mib). Writes one `traffic:` line per kernel,
       tagged with the digest of the library's sources, which bench.py reads.
+  python bench_profile.py counters OUT_MD CSV... --ids FWD_SPMM,BWD_SPMM --title T \\
+          --intro I --command C1 --command C2 [--entries-per-wave FWD_SPMM=N,...]
+      SQ counters per profiling id from separate counter passes, with ratios
 
 The library's kernels are named by the profiling ids bench.py reports.
 """
@@ -30,6 +33,7 @@ TABLE_ONLY_IDS = {"INIT_SELECT_GLOBAL", "LAYER_SPMM"}
 # kernel symbol prefix -> profiling ids (spmm and fwht resolved by template arguments)
 KERNEL_IDS = {
     "materialize_kernel": ["MATERIALIZE"],
+    "materialize_rows_kernel": ["MATERIALIZE"],
     "dc_reduce_kernel": ["BWD_DC_REDUCE"],
     # global selection: the threshold stage
     "mag_keys_kernel": ["GLOBAL_THRESHOLD"],
@@ -66,7 +70,7 @@ def template_args(n: str):
 
 def kernel_ids(name: str):
     n = short(name)
-    if n.startswith("rows_dc_kernel<"):
+    if n.startswith("rows_dc_kernel<") or n.startswith("rows_dc16_kernel<"):
         return ["BWD_SPMM"]
     if n.startswith("rows_kernel<"):
         # the plain gather: forward (source z, fp32; bf16 output as in the
@@ -166,6 +170,67 @@ def cmd_traffic(a):
     print("wrote", a.out)
 
 
+SQ_DERIVED = [
+    ("VALU busy per SIMD (4 waves x SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)",
+     lambda m: f"{100 * 4 * m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.0f}%"),
+    ("wave lifetime spent waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)",
+     lambda m: f"{100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.0f}%"),
+    ("waiting on a dependency (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
+     lambda m: f"{100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.0f}%"),
+    ("issue slots a wave uses (all instructions / SQ_WAVE_CYCLES)",
+     lambda m: f"{100 * sum(m[c] for c in ('SQ_INSTS_VALU', 'SQ_INSTS_SALU', 'SQ_INSTS_LDS', 'SQ_INSTS_VMEM_RD', 'SQ_INSTS_SMEM')) / m['SQ_WAVE_CYCLES']:.0f}%"),
+    ("VALU instructions per wave", lambda m: f"{m['SQ_INSTS_VALU'] / m['SQ_WAVES']:.0f}"),
+    ("SALU instructions per wave", lambda m: f"{m['SQ_INSTS_SALU'] / m['SQ_WAVES']:.0f}"),
+    ("SALU per VALU instruction", lambda m: f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_VALU']:.2f}"),
+    ("LDS instructions per wave", lambda m: f"{m['SQ_INSTS_LDS'] / m['SQ_WAVES']:.0f}"),
+    ("global load instructions per wave", lambda m: f"{m['SQ_INSTS_VMEM_RD'] / m['SQ_WAVES']:.0f}"),
+    ("LDS bank-conflict cycles / LDS active cycles",
+     lambda m: f"{100 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_ACTIVE_INST_LDS']:.1f}%"),
+    ("waiting on LDS (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES)",
+     lambda m: f"{100 * m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:.1f}%"),
+]
+
+
+def cmd_counters(a):
+    """SQ counters of the profiling ids in --ids, from one or more counter runs
+    (each its own pass): the mean per dispatch, the launch shape and ratios."""
+    ids = a.ids.split(",")
+    vals = {k: collections.defaultdict(list) for k in ids}
+    shape = {}
+    for path in a.csvs:
+        for r in csv.DictReader(open(path)):
+            for kid in kernel_ids(r["Kernel_Name"]):
+                if kid in vals:
+                    vals[kid][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                    shape[kid] = (r["Grid_Size"], r["Workgroup_Size"], r["LDS_Block_Size"])
+    m = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    n = {k: len(vals[k]["SQ_WAVES"]) for k in ids}
+    with open(a.out, "w") as f:
+        f.write(f"# {a.title}\n\n{a.intro} Each counter pass is its own run (from /tmp with "
+                "TMPDIR=/tmp, one MI355X; $REPO is the repository root):\n\n```\n"
+                + "\n".join(a.command) + "\n```\n\n")
+        f.write("Per dispatch, mean over " + ", ".join(f"{n[k]} ({k})" for k in ids)
+                + " dispatches (counter values summed over the chip; cycle counters in the SQ's "
+                "own units, used only in ratios):\n\n")
+        f.write("| counter | " + " | ".join(ids) + " |\n|---" + "|---" * len(ids) + "|\n")
+        for c in sorted(set().union(*(m[k] for k in ids))):
+            f.write(f"| {c} | " + " | ".join(f"{m[k].get(c, 0):.4g}" for k in ids) + " |\n")
+        f.write("\n| launch | " + " | ".join(ids) + " |\n|---" + "|---" * len(ids) + "|\n")
+        for i, lab in enumerate(("grid (threads)", "workgroup", "LDS bytes per workgroup")):
+            f.write(f"| {lab} | " + " | ".join(shape[k][i] for k in ids) + " |\n")
+        f.write(f"\nDerived ({a.derived_note}):\n\n| quantity | " + " | ".join(ids)
+                + " |\n|---" + "|---" * len(ids) + "|\n")
+        for lab, fn in SQ_DERIVED:
+            f.write(f"| {lab} | " + " | ".join(fn(m[k]) for k in ids) + " |\n")
+        if a.entries_per_wave:
+            per = dict(kv.split("=") for kv in a.entries_per_wave.split(","))
+            f.write("| VALU instructions per entry (entries a wave covers in its tile: "
+                    + ", ".join(f"{k} {v}" for k, v in per.items()) + ") | "
+                    + " | ".join(f"{m[k]['SQ_INSTS_VALU'] / m[k]['SQ_WAVES'] / float(per[k]):.1f}"
+                                 if k in per else "" for k in ids) + " |\n")
+    print("wrote", a.out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -182,8 +247,19 @@ def main():
     t.add_argument("--calib-mib", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("csvs", nargs="+")
+    c.add_argument("--ids", required=True, help="profiling ids, comma-separated")
+    c.add_argument("--title", required=True)
+    c.add_argument("--intro", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--derived-note", default="a SIMD holds 4 of a workgroup's 16 waves; one "
+                   "workgroup per CU")
+    c.add_argument("--entries-per-wave", default="",
+                   help="ID=entries pairs: the nonzeros one wave covers in its token tile")
     a = ap.parse_args()
-    (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
