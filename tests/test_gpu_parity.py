@@ -293,8 +293,9 @@ def test_init_global_configs(q, strategy, cfg):
                                           # more nonzeros per row than the row kernel holds
                                           # in registers (128 at 1024 columns)
                                           (8, 1024, 4000),
-                                          # more rows than workgroups (1024 at 4096 columns)
-                                          (1500, 4096, 60000)])
+                                          # more rows than workgroups (1024 at 4096
+                                          # columns, 512 at 8192)
+                                          (1500, 4096, 60000), (600, 8192, 30000)])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_materialize(q, d_out, d_in, p, out_dt):
     say("materialize", d_out, d_in, p, out_dt)
