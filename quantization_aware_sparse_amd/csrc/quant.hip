@@ -357,12 +357,16 @@ __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t 
 // bf16x8 of 128 + q for the 8 codes of a word (bf16(128 + q) = 0x4300 | q):
 // dword i takes byte i of w (low nibble q_2i) and byte i of w >> 4 (low
 // nibble q_2i+1) into its bytes 0 and 2, then keeps those nibbles
-__device__ __forceinline__ bf16x8 unpack_off128(uint32_t w) {
+__device__ __forceinline__ bf16x8 unpack_off128(uint32_t w, uint32_t mask) {
   const uint32_t u = w >> 4;
   uint32_t d[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    d[i] = (__builtin_amdgcn_perm(u, w, 0x0C040C00u + 0x00010001u * i) & 0x000F000Fu) | 0x43004300u;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = __builtin_amdgcn_perm(u, w, 0x0C040C00u + 0x00010001u * i);
+    // (x & mask) | 0x43004300 in one instruction (mask 0x000F000F in a VGPR:
+    // one scalar operand per VALU instruction on this target)
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d[i]) : "v"(x), "v"(mask), "s"(0x43004300u));
+  }
   bf16x8 r;
   __builtin_memcpy(&r, d, 16);
   return r;
@@ -458,6 +462,8 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
     __builtin_memcpy(&ones, o, 16);
   }
   const int gmask = (1 << qw.lg_group) - 1;
+  uint32_t nib_mask = 0x000F000Fu;
+  asm volatile("" : "+v"(nib_mask));   // kept in a VGPR
   const int lr = lane & 15, lq = lane >> 4;
   const int aswz = qswz(lr);
   const int nsteps = K / kQK;
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void qgemm4_ring_kernel(const uint16_t* __r
                                                           0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 bf = unpack_off128(cw[kh][j]);
+        const bf16x8 bf = unpack_off128(cw[kh][j], nib_mask);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kh][i], bf,
