@@ -109,11 +109,11 @@ class HipEvents:
 CALL_KERNELS = {
     "init": ["INIT_SELECT"],
     "materialize": ["MATERIALIZE"],
-    "fwd_save": ["FWD_FWHT", "FWD_SPMM"],
     "fwd_z": ["FWD_SPMM"],
     "bwd_saved": ["BWD_SPMM", "BWD_FWHT_DX", "BWD_DC_REDUCE"],
     "bwd_dz": ["BWD_SPMM", "BWD_DC_REDUCE"],
     "fwht_dx": ["FWHT"],
+    "fwht_z": ["FWD_FWHT@FWHT"],   # z = FWHT(x)/n by qwha_fwht, reported as FWD_FWHT
 }
 KID = dict(K, FWHT=9)
 
@@ -130,7 +130,9 @@ class Block:
     the group, kept, then each adapter's gather-SpMM) and the backward (each
     adapter's dz and dc against the kept z; one transform of the summed dz for
     a shared group); then every adapter's c += 1e-3 sign(dc) and
-    re-materialisation."""
+    re-materialisation. The transforms of x and the first materialisations
+    run on a second stream beside the inits and the forward, ordered by
+    events."""
 
     def __init__(self, cfg, nsets, dev, hip):
         import numpy as np
@@ -205,22 +207,42 @@ class Block:
             a["times"] = {k: [] for k in KID}
             self.ads.append(a)
         self.nsets = nsets
-        self.stream = torch.cuda.current_stream().cuda_stream
+        self.main = torch.cuda.current_stream()
+        self.stream = self.main.cuda_stream
+        # a second stream (default priority) for the work that does not wait
+        # for the init: z = FWHT(x)/n, and the first materialisation of dW
+        self.side = torch.cuda.Stream(device=dev)
+        self.ev_z, self.ev_init, self.ev_mat = (torch.cuda.Event() for _ in range(3))
 
     def _arm(self, a, call, record):
         from quantization_aware_sparse_amd import check, lib
         if not record:
             return
         for k in CALL_KERNELS[call]:
-            check(lib.qwha_profile_next(KID[k], a["ev"][k][0], a["ev"][k][1]), "profile")
-            a["armed"].append(k)
+            label, _, kid = k.partition("@")
+            check(lib.qwha_profile_next(KID[kid or label], a["ev"][label][0], a["ev"][label][1]),
+                  "profile")
+            a["armed"].append(label)
 
     def step(self, s, record=False):
         from quantization_aware_sparse_amd import check, lib
         st, A = self.stream, self.act_code
+        side = self.side.cuda_stream
         T = self.T
         for a in self.ads:
             a["armed"] = []
+        # side stream, once the previous step is done with z and dW: every
+        # group's z = FWHT(x)/n (it needs no init, so it runs beside it)
+        self.side.wait_stream(self.main)
+        for g in self.groups:
+            x = g["x"][s % self.nsets]
+            self._arm(self.ads[g["members"][0]], "fwht_z", record)
+            d_in = g["d_in"]
+            b = d_in & -d_in
+            check(lib.qwha_fwht(x.data_ptr(), A, g["z"].data_ptr(), 0, T * (d_in // b), b,
+                                1.0 / b, side), "fwht z")
+        self.ev_z.record(self.side)
+        # main stream: each init; its dW materialised on the side stream
         for a in self.ads:
             sp = a["spec"]
             self._arm(a, "init", record)
@@ -229,27 +251,22 @@ class Block:
                                        a["c"].data_ptr(), a["col_ptr"].data_ptr(),
                                        a["perm"].data_ptr(), a["ws_i"].data_ptr(),
                                        a["ws_i"].numel(), st), "init")
+            self.ev_init.record(self.main)
+            self.side.wait_event(self.ev_init)
             self._arm(a, "materialize", record)
             check(lib.qwha_materialize(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
                                        a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
-                                       a["dW"].data_ptr(), 0, st), "materialize")
+                                       a["dW"].data_ptr(), 0, side), "materialize")
+        self.ev_mat.record(self.side)
+        self.main.wait_event(self.ev_z)
         for g in self.groups:
-            x = g["x"][s % self.nsets]
-            for n, i in enumerate(g["members"]):
+            for i in g["members"]:
                 a, sp = self.ads[i], self.ads[i]["spec"]
-                if n == 0:
-                    self._arm(a, "fwd_save", record)
-                    check(lib.qwha_fwd_save(x.data_ptr(), A, T, sp.d_in, sp.d_out, sp.p,
-                                            a["row_ptr"].data_ptr(), a["E"].data_ptr(),
-                                            a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
-                                            g["z"].data_ptr(), a["ws_f"].data_ptr(),
-                                            a["ws_f"].numel(), st), "fwd")
-                else:
-                    self._arm(a, "fwd_z", record)
-                    check(lib.qwha_fwd_z(g["z"].data_ptr(), A, T, sp.d_in, sp.d_out, sp.p,
-                                         a["row_ptr"].data_ptr(), a["E"].data_ptr(),
-                                         a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
-                                         a["ws_f"].data_ptr(), a["ws_f"].numel(), st), "fwd_z")
+                self._arm(a, "fwd_z", record)
+                check(lib.qwha_fwd_z(g["z"].data_ptr(), A, T, sp.d_in, sp.d_out, sp.p,
+                                     a["row_ptr"].data_ptr(), a["E"].data_ptr(),
+                                     a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
+                                     a["ws_f"].data_ptr(), a["ws_f"].numel(), st), "fwd_z")
         for g in self.groups:
             if len(g["members"]) == 1:
                 a = self.ads[g["members"][0]]
@@ -277,6 +294,9 @@ class Block:
             b = d_in & -d_in
             check(lib.qwha_fwht(g["dz"].data_ptr(), 0, g["dx"].data_ptr(), A, T * (d_in // b), b,
                                 1.0 / b, st), "fwht dx")
+        # the update changes c and the re-materialisation overwrites dW: both
+        # after the side stream's first materialisation
+        self.main.wait_event(self.ev_mat)
         for a in self.ads:
             sp = a["spec"]
             check(lib.qwha_sign_update(a["c"].data_ptr(), a["dc"].data_ptr(), sp.p, 1e-3, st),
