@@ -110,9 +110,8 @@ CALL_KERNELS = {
     "init": ["INIT_SELECT"],
     "materialize": ["MATERIALIZE"],
     "fwd_z": ["FWD_SPMM"],
-    "bwd_saved": ["BWD_SPMM", "BWD_FWHT_DX", "BWD_DC_REDUCE"],
     "bwd_dz": ["BWD_SPMM", "BWD_DC_REDUCE"],
-    "fwht_dx": ["FWHT"],
+    "fwht_dx": ["BWD_FWHT_DX@FWHT"],   # dx = FWHT(dz)/n by qwha_fwht
     "fwht_z": ["FWD_FWHT@FWHT"],   # z = FWHT(x)/n by qwha_fwht, reported as FWD_FWHT
 }
 KID = dict(K, FWHT=9)
@@ -130,9 +129,9 @@ class Block:
     the group, kept, then each adapter's gather-SpMM) and the backward (each
     adapter's dz and dc against the kept z; one transform of the summed dz for
     a shared group); then every adapter's c += 1e-3 sign(dc) and
-    re-materialisation. The transforms of x and the first materialisations
-    run on a second stream beside the inits and the forward, ordered by
-    events."""
+    re-materialisation. The transforms (x -> z, dz -> dx) and the first
+    materialisations run on a second stream beside the inits, the forward
+    and the updates, ordered by events."""
 
     def __init__(self, cfg, nsets, dev, hip):
         import numpy as np
@@ -180,8 +179,7 @@ class Block:
                        x=[xd] + [xd.clone() for _ in range(nsets - 1)],
                        z=torch.empty((self.T, d_in), dtype=torch.float32, device=dev),
                        dx=torch.empty((self.T, d_in), dtype=adt, device=dev))
-            if len(members) > 1:
-                grp["dz"] = torch.empty((self.T, d_in), dtype=torch.float32, device=dev)
+            grp["dz"] = torch.empty((self.T, d_in), dtype=torch.float32, device=dev)
             self.groups.append(grp)
         self.ads = []
         for i, (sp, L) in enumerate(zip(self.specs, self.layers)):
@@ -212,7 +210,7 @@ class Block:
         # a second stream (default priority) for the work that does not wait
         # for the init: z = FWHT(x)/n, and the first materialisation of dW
         self.side = torch.cuda.Stream(device=dev)
-        self.ev_z, self.ev_init, self.ev_mat = (torch.cuda.Event() for _ in range(3))
+        self.ev_z, self.ev_init, self.ev_mat, self.ev_dz = (torch.cuda.Event() for _ in range(4))
 
     def _arm(self, a, call, record):
         from quantization_aware_sparse_amd import check, lib
@@ -227,13 +225,24 @@ class Block:
     def step(self, s, record=False):
         from quantization_aware_sparse_amd import check, lib
         st, A = self.stream, self.act_code
-        side = self.side.cuda_stream
+        # Timed steps overlap the two streams. Profiled steps (record) issue
+        # everything on the main stream, so that each kernel's recorded time
+        # is its own and not shared with a kernel running beside it.
+        overlap = not record
+        side = self.side.cuda_stream if overlap else st
         T = self.T
         for a in self.ads:
             a["armed"] = []
+
+        def cross(ev, src, dst):   # dst waits for src's work so far
+            if overlap:
+                ev.record(src)
+                dst.wait_event(ev)
+
         # side stream, once the previous step is done with z and dW: every
         # group's z = FWHT(x)/n (it needs no init, so it runs beside it)
-        self.side.wait_stream(self.main)
+        if overlap:
+            self.side.wait_stream(self.main)
         for g in self.groups:
             x = g["x"][s % self.nsets]
             self._arm(self.ads[g["members"][0]], "fwht_z", record)
@@ -241,7 +250,8 @@ class Block:
             b = d_in & -d_in
             check(lib.qwha_fwht(x.data_ptr(), A, g["z"].data_ptr(), 0, T * (d_in // b), b,
                                 1.0 / b, side), "fwht z")
-        self.ev_z.record(self.side)
+        if overlap:
+            self.ev_z.record(self.side)
         # main stream: each init; its dW materialised on the side stream
         for a in self.ads:
             sp = a["spec"]
@@ -251,14 +261,14 @@ class Block:
                                        a["c"].data_ptr(), a["col_ptr"].data_ptr(),
                                        a["perm"].data_ptr(), a["ws_i"].data_ptr(),
                                        a["ws_i"].numel(), st), "init")
-            self.ev_init.record(self.main)
-            self.side.wait_event(self.ev_init)
+            cross(self.ev_init, self.main, self.side)
             self._arm(a, "materialize", record)
             check(lib.qwha_materialize(a["row_ptr"].data_ptr(), a["E"].data_ptr(),
                                        a["c"].data_ptr(), sp.d_out, sp.d_in, sp.p, 1.0, 0,
                                        a["dW"].data_ptr(), 0, side), "materialize")
-        self.ev_mat.record(self.side)
-        self.main.wait_event(self.ev_z)
+        if overlap:
+            self.ev_mat.record(self.side)
+            self.main.wait_event(self.ev_z)
         for g in self.groups:
             for i in g["members"]:
                 a, sp = self.ads[i], self.ads[i]["spec"]
@@ -267,18 +277,10 @@ class Block:
                                      a["row_ptr"].data_ptr(), a["E"].data_ptr(),
                                      a["c"].data_ptr(), 1.0, a["y"].data_ptr(), 0,
                                      a["ws_f"].data_ptr(), a["ws_f"].numel(), st), "fwd_z")
+        # backward: dz (summed over a shared group) and dc on the main stream;
+        # dx = FWHT(dz)/n on the side stream, beside the updates, which need
+        # only dc
         for g in self.groups:
-            if len(g["members"]) == 1:
-                a = self.ads[g["members"][0]]
-                sp = a["spec"]
-                self._arm(a, "bwd_saved", record)
-                check(lib.qwha_bwd_saved(g["z"].data_ptr(), a["dy"][s % self.nsets].data_ptr(),
-                                         A, T, sp.d_in, sp.d_out, sp.p, a["row_ptr"].data_ptr(),
-                                         a["E"].data_ptr(), a["c"].data_ptr(),
-                                         a["col_ptr"].data_ptr(), a["perm"].data_ptr(), 1.0,
-                                         g["dx"].data_ptr(), 0, a["dc"].data_ptr(),
-                                         a["ws_b"].data_ptr(), a["ws_b"].numel(), st), "bwd")
-                continue
             for n, i in enumerate(g["members"]):
                 a, sp = self.ads[i], self.ads[i]["spec"]
                 self._arm(a, "bwd_dz", record)
@@ -288,15 +290,17 @@ class Block:
                                       a["perm"].data_ptr(), 1.0, g["dz"].data_ptr(),
                                       int(n > 0), a["dc"].data_ptr(), a["ws_b"].data_ptr(),
                                       a["ws_b"].numel(), st), "bwd_dz")
+            cross(self.ev_dz, self.main, self.side)
             a0 = self.ads[g["members"][0]]
             self._arm(a0, "fwht_dx", record)
             d_in = g["d_in"]
             b = d_in & -d_in
             check(lib.qwha_fwht(g["dz"].data_ptr(), 0, g["dx"].data_ptr(), A, T * (d_in // b), b,
-                                1.0 / b, st), "fwht dx")
+                                1.0 / b, side), "fwht dx")
         # the update changes c and the re-materialisation overwrites dW: both
         # after the side stream's first materialisation
-        self.main.wait_event(self.ev_mat)
+        if overlap:
+            self.main.wait_event(self.ev_mat)
         for a in self.ads:
             sp = a["spec"]
             check(lib.qwha_sign_update(a["c"].data_ptr(), a["dc"].data_ptr(), sp.p, 1e-3, st),
